@@ -1,0 +1,94 @@
+"""fp8_paged_kv_pa_amd -- paged decode attention over a page-shuffled FP8
+(e4m3fn) KV cache with per-token K/V scales, for MI355X (gfx950).
+
+A thin Python face of the C ABI in ``include/fp8pa.h`` (same names).  The
+functions here only marshal torch tensors into descriptors; all work runs in
+the HIP kernels of ``libfp8pa.so``.  PyTorch supplies device memory and the
+stream.
+"""
+
+import ctypes
+
+from ._lib import (  # noqa: F401
+    EXPORTS, PaConfig, PaDecodeOpts, PaError, PaPlanInfo, PaTensor, SCALE_NONE,
+    SCALE_PER_TOKEN, SCALE_SCALAR, STATUS, check, desc, load, ref, stream_handle,
+)
+
+PAGE_SIZE = 128
+HEAD_DIM = 128
+GROUP_SIZE = 16
+BLOCK_BYTES = PAGE_SIZE * HEAD_DIM
+
+
+def pa_decode(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+              cu_seqlens_q, sparse_page_idx, scale_mode, out, stream=None):
+    """Paged decode attention into ``out`` (see ``pa_decode`` in include/fp8pa.h)."""
+    lib = load()
+    d = [desc(t) for t in (q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                           cu_seqlens_q, sparse_page_idx)]
+    do = desc(out)
+    check(lib.pa_decode(*[ref(x) for x in d], int(scale_mode), ref(do), stream_handle(stream)))
+    return out
+
+
+def pa_decode_ex(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                 cu_seqlens_q, sparse_page_idx, scale_mode, out, sm_scale=0.0, max_q_len=0,
+                 force_parts=0, main_begin_event=None, main_end_event=None, stream=None):
+    """``pa_decode`` with options; events are torch.cuda.Event objects that
+    have been recorded once (so they exist)."""
+    lib = load()
+    opts = PaDecodeOpts()
+    opts.sm_scale = float(sm_scale)
+    opts.max_q_len = int(max_q_len)
+    opts.force_parts = int(force_parts)
+    opts.main_begin_event = main_begin_event.cuda_event if main_begin_event is not None else None
+    opts.main_end_event = main_end_event.cuda_event if main_end_event is not None else None
+    d = [desc(t) for t in (q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                           cu_seqlens_q, sparse_page_idx)]
+    do = desc(out)
+    check(lib.pa_decode_ex(*[ref(x) for x in d], int(scale_mode), ref(do), ctypes.byref(opts),
+                           stream_handle(stream)))
+    return out
+
+
+def kv_quant_write(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, scale_mode,
+                   stream=None):
+    """Quantize and store new K/V tokens (see ``kv_quant_write`` in include/fp8pa.h)."""
+    lib = load()
+    d = [desc(t) for t in (k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale)]
+    check(lib.kv_quant_write(*[ref(x) for x in d], int(scale_mode), stream_handle(stream)))
+
+
+def make_config(num_kv_heads, rows, batch, max_pages, topk=0, ragged=False, max_q_len=0,
+                scale_mode=SCALE_PER_TOKEN, kv_dtype=1, force_parts=0, group_size=GROUP_SIZE,
+                head_dim=HEAD_DIM, page_size=PAGE_SIZE):
+    c = PaConfig()
+    c.num_kv_heads, c.group_size, c.head_dim, c.page_size = num_kv_heads, group_size, head_dim, page_size
+    c.kv_dtype, c.scale_mode = kv_dtype, scale_mode
+    c.rows, c.batch, c.max_pages, c.topk = rows, batch, max_pages, topk
+    c.ragged, c.max_q_len, c.force_parts = int(bool(ragged)), max_q_len, force_parts
+    return c
+
+
+def pa_query_support(cfg):
+    """0 if the configuration is served, else the pa_status it would fail with."""
+    return load().pa_query_support(ctypes.byref(cfg))
+
+
+def pa_plan_describe(cfg):
+    """The plan (as a dict) a configuration maps to; raises PaError if refused."""
+    info = PaPlanInfo()
+    check(load().pa_plan_describe(ctypes.byref(cfg), ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in PaPlanInfo._fields_ if f != "reserved"}
+
+
+def pa_reserve(cfg, stream=None):
+    check(load().pa_reserve(ctypes.byref(cfg), stream_handle(stream)))
+
+
+def pa_release():
+    check(load().pa_release())
+
+
+def pa_last_error():
+    return load().pa_last_error().decode()

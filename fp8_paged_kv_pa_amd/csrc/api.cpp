@@ -1,0 +1,398 @@
+// C-ABI entry points: descriptor checks (all before any launch), the
+// capacity-bucketed split-K scratch, and the kernel launches.
+//
+// Every condition the host can check is refused with a status code before
+// anything runs on the device (ROCm/ATOM pull request 2710 review, "Should
+// fix" 2; ROCm/ATOM pull request 2614, "Change": decline a call before the
+// low-level launcher would abort).  Scratch comes from one arena per
+// (device, stream), sized by capacity bucket and grown only outside graph
+// capture (ROCm/ATOM pull request 2710 review, "Must fix" 1: bounded plan
+// and scratch shapes, allocated where the memory accounting can see them).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/fp8pa.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace fp8pa {
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int64_t numel(const pa_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+bool contiguous(const pa_tensor* t) {
+  int64_t s = 1;
+  for (int i = t->ndim - 1; i >= 0; --i) {
+    if (t->shape[i] != 1 && t->stride[i] != s) return false;
+    s *= t->shape[i];
+  }
+  return true;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int check_tensor(const pa_tensor* t, const char* name) {
+  if (!t) return fail(PA_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (t->ndim < 1 || t->ndim > PA_MAX_DIMS)
+    return fail(PA_ERR_SHAPE, std::string(name) + ": ndim out of range");
+  for (int i = 0; i < t->ndim; ++i)
+    if (t->shape[i] < 0) return fail(PA_ERR_SHAPE, std::string(name) + ": negative extent");
+  if (numel(t) > 0 && !t->data) return fail(PA_ERR_INVALID_ARG, std::string(name) + ": data is NULL");
+  return PA_OK;
+}
+
+// K or V cache: [num_blocks, Hkv, ...] with 16384 bytes per (block, head),
+// contiguous.
+int check_cache(const pa_tensor* t, const char* name, int64_t* nb, int64_t* hkv) {
+  int rc = check_tensor(t, name);
+  if (rc) return rc;
+  if (t->dtype != PA_DTYPE_U8 && t->dtype != PA_DTYPE_F8E4M3)
+    return fail(PA_ERR_DTYPE, std::string(name) + " must be uint8 or float8_e4m3fn");
+  if (t->ndim < 3) return fail(PA_ERR_SHAPE, std::string(name) + " must be [num_blocks, Hkv, 16384]");
+  int64_t inner = 1;
+  for (int i = 2; i < t->ndim; ++i) inner *= t->shape[i];
+  if (inner != kBlockBytes)
+    return fail(PA_ERR_SHAPE, std::string(name) + ": each (page, head) block must hold 16384 bytes (128-token pages, head_dim 128)");
+  if (!contiguous(t)) return fail(PA_ERR_LAYOUT, std::string(name) + " must be contiguous");
+  if (!aligned(t->data, 16)) return fail(PA_ERR_LAYOUT, std::string(name) + " must be 16-byte aligned");
+  *nb = t->shape[0];
+  *hkv = t->shape[1];
+  return PA_OK;
+}
+
+int check_scales(const pa_tensor* ks, const pa_tensor* vs, int mode, int64_t nb, int64_t hkv) {
+  if (mode == PA_SCALE_NONE) return PA_OK;
+  const pa_tensor* ts[2] = {ks, vs};
+  const char* names[2] = {"k_scale", "v_scale"};
+  for (int i = 0; i < 2; ++i) {
+    int rc = check_tensor(ts[i], names[i]);
+    if (rc) return rc;
+    if (ts[i]->dtype != PA_DTYPE_F32) return fail(PA_ERR_DTYPE, std::string(names[i]) + " must be float32");
+    if (mode == PA_SCALE_SCALAR) {
+      if (numel(ts[i]) != 1) return fail(PA_ERR_SHAPE, std::string(names[i]) + " must hold one value in scalar mode");
+    } else {
+      if (ts[i]->ndim != 3 || ts[i]->shape[0] != nb || ts[i]->shape[1] != hkv || ts[i]->shape[2] != kPage)
+        return fail(PA_ERR_SHAPE, std::string(names[i]) + " must be [num_blocks, Hkv, 128] in per-token mode");
+      if (!contiguous(ts[i])) return fail(PA_ERR_LAYOUT, std::string(names[i]) + " must be contiguous");
+      if (!aligned(ts[i]->data, 16)) return fail(PA_ERR_LAYOUT, std::string(names[i]) + " must be 16-byte aligned");
+    }
+  }
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch arenas, one per (device, stream).
+struct Arena {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_mu;
+std::map<std::pair<int, void*>, Arena> g_arenas;
+
+int get_scratch(hipStream_t stream, size_t need, void** out) {
+  *out = nullptr;
+  if (need == 0) return PA_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_mu);
+  Arena& ar = g_arenas[{dev, reinterpret_cast<void*>(stream)}];
+  if (ar.bytes >= need) {
+    *out = ar.ptr;
+    return PA_OK;
+  }
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) != hipSuccess) return fail(PA_ERR_HIP, "hipStreamIsCapturing failed");
+  if (st != hipStreamCaptureStatusNone)
+    return fail(PA_ERR_NOT_RESERVED,
+                "split-K scratch must grow to " + std::to_string(need) +
+                    " bytes while the stream is being captured; call pa_reserve before capture");
+  size_t sz = 1;
+  while (sz < need) sz <<= 1;
+  if (ar.ptr) {
+    // kernels still queued on this stream may use the old arena
+    if (hipStreamSynchronize(stream) != hipSuccess) return fail(PA_ERR_HIP, "hipStreamSynchronize failed");
+    hipFree(ar.ptr);
+    ar.ptr = nullptr;
+    ar.bytes = 0;
+  }
+  if (hipMalloc(&ar.ptr, sz) != hipSuccess) {
+    ar.ptr = nullptr;
+    return fail(PA_ERR_HIP, "hipMalloc of " + std::to_string(sz) + " bytes of split-K scratch failed");
+  }
+  ar.bytes = sz;
+  *out = ar.ptr;
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
+int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const pa_tensor* ks,
+                const pa_tensor* vs, const pa_tensor* bt, const pa_tensor* ctx, const pa_tensor* cu,
+                const pa_tensor* sp, int mode, pa_tensor* out, const pa_decode_opts* opts,
+                void* stream_ptr) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_tensor(q, "q"))) return rc;
+  if (q->dtype != PA_DTYPE_BF16) return fail(PA_ERR_DTYPE, "q must be bfloat16");
+  if (q->ndim != 3) return fail(PA_ERR_SHAPE, "q must be [rows, 16*Hkv, 128]");
+  const int64_t rows = q->shape[0], Hq = q->shape[1];
+  if (q->shape[2] != kDim) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (Hq % kGroup != 0) return fail(PA_ERR_UNSUPPORTED, "query heads must be 16 per KV head");
+  if (q->stride[2] != 1 || q->stride[0] % 8 || q->stride[1] % 8 || !aligned(q->data, 16))
+    return fail(PA_ERR_LAYOUT, "q: last dim contiguous, row/head strides multiples of 8, 16-byte aligned");
+
+  int64_t nb = 0, hkv = 0, nb2 = 0, hkv2 = 0;
+  if ((rc = check_cache(kc, "k_cache", &nb, &hkv))) return rc;
+  if ((rc = check_cache(vc, "v_cache", &nb2, &hkv2))) return rc;
+  if (nb2 != nb || hkv2 != hkv) return fail(PA_ERR_SHAPE, "k_cache and v_cache shapes differ");
+  if (kc->dtype != vc->dtype) return fail(PA_ERR_DTYPE, "k_cache and v_cache dtypes differ");
+  if (hkv * kGroup != Hq)
+    return fail(PA_ERR_UNSUPPORTED, "q has " + std::to_string(Hq) + " heads but the cache has " +
+                                        std::to_string(hkv) + " KV heads: the group must be 16");
+  if (mode < PA_SCALE_NONE || mode > PA_SCALE_PER_TOKEN) return fail(PA_ERR_INVALID_ARG, "unknown scale_mode");
+  if ((rc = check_scales(ks, vs, mode, nb, hkv))) return rc;
+
+  if ((rc = check_tensor(bt, "block_table"))) return rc;
+  if (bt->dtype != PA_DTYPE_I32 || bt->ndim != 2) return fail(PA_ERR_DTYPE, "block_table must be int32 [batch, W]");
+  if (bt->stride[1] != 1) return fail(PA_ERR_LAYOUT, "block_table rows must be contiguous");
+  const int64_t B = bt->shape[0], W = bt->shape[1];
+  if ((rc = check_tensor(ctx, "context_lens"))) return rc;
+  if (ctx->dtype != PA_DTYPE_I32 || ctx->ndim != 1 || ctx->shape[0] != B || (B > 1 && ctx->stride[0] != 1))
+    return fail(PA_ERR_SHAPE, "context_lens must be contiguous int32 [batch]");
+  const bool ragged = cu != nullptr && cu->data != nullptr;
+  if (ragged) {
+    if ((rc = check_tensor(cu, "cu_seqlens_q"))) return rc;
+    if (cu->dtype != PA_DTYPE_I32 || cu->ndim != 1 || cu->shape[0] != B + 1 || cu->stride[0] != 1)
+      return fail(PA_ERR_SHAPE, "cu_seqlens_q must be contiguous int32 [batch + 1]");
+  }
+  int64_t topk = 0;
+  const bool sparse = sp != nullptr && sp->data != nullptr;
+  if (sparse) {
+    if ((rc = check_tensor(sp, "sparse_page_idx"))) return rc;
+    if (sp->dtype != PA_DTYPE_I32 || sp->ndim != 2 || sp->shape[0] != rows || sp->stride[1] != 1)
+      return fail(PA_ERR_SHAPE, "sparse_page_idx must be int32 [rows, topk] with contiguous rows");
+    topk = sp->shape[1];
+    if (topk < 1) return fail(PA_ERR_SHAPE, "sparse_page_idx needs topk >= 1");
+  }
+  if ((rc = check_tensor(out, "out"))) return rc;
+  if (out->dtype != PA_DTYPE_BF16 || out->ndim != 3 || out->shape[0] != rows || out->shape[1] != Hq ||
+      out->shape[2] != kDim)
+    return fail(PA_ERR_SHAPE, "out must be bfloat16 with the shape of q");
+  if (out->stride[2] != 1 || out->stride[0] % 8 || out->stride[1] % 8 || !aligned(out->data, 16))
+    return fail(PA_ERR_LAYOUT, "out: last dim contiguous, row/head strides multiples of 8, 16-byte aligned");
+
+  pa_config cfg{};
+  cfg.num_kv_heads = int32_t(hkv);
+  cfg.group_size = kGroup;
+  cfg.head_dim = kDim;
+  cfg.page_size = kPage;
+  cfg.kv_dtype = kc->dtype;
+  cfg.scale_mode = mode;
+  cfg.rows = rows;
+  cfg.batch = B;
+  cfg.max_pages = W;
+  cfg.topk = topk;
+  cfg.ragged = ragged ? 1 : 0;
+  cfg.max_q_len = opts ? opts->max_q_len : 0;
+  cfg.force_parts = opts ? opts->force_parts : 0;
+  Plan plan;
+  std::string perr;
+  if ((rc = make_plan(cfg, &plan, &perr))) return fail(rc, perr);
+  if (rows == 0) return PA_OK;
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  void* scratch = nullptr;
+  if ((rc = get_scratch(stream, size_t(plan.scratch_bytes), &scratch))) return rc;
+
+  DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.q_row_stride = q->stride[0];
+  a.q_head_stride = q->stride[1];
+  a.k_cache = static_cast<const uint8_t*>(kc->data);
+  a.v_cache = static_cast<const uint8_t*>(vc->data);
+  a.k_scale = mode == PA_SCALE_NONE ? nullptr : static_cast<const float*>(ks->data);
+  a.v_scale = mode == PA_SCALE_NONE ? nullptr : static_cast<const float*>(vs->data);
+  a.block_table = static_cast<const int32_t*>(bt->data);
+  a.bt_stride = bt->stride[0];
+  a.context_lens = static_cast<const int32_t*>(ctx->data);
+  a.cu_seqlens_q = ragged ? static_cast<const int32_t*>(cu->data) : nullptr;
+  a.sparse_idx = sparse ? static_cast<const int32_t*>(sp->data) : nullptr;
+  a.sp_stride = sparse ? sp->stride[0] : 0;
+  a.out = static_cast<uint16_t*>(out->data);
+  a.out_row_stride = out->stride[0];
+  a.out_head_stride = out->stride[1];
+  if (plan.merge) {
+    const int64_t pairs = int64_t(plan.parts_launched) * rows * Hq;
+    a.part_ml = static_cast<float*>(scratch);
+    a.part_acc = static_cast<float*>(scratch) + 2 * pairs;
+  }
+  a.num_blocks = nb;
+  a.hkv = int32_t(hkv);
+  a.rows = int32_t(rows);
+  a.batch = int32_t(B);
+  a.width = int32_t(W);
+  a.topk = int32_t(topk);
+  a.uniform_q_len = ragged ? 0 : int32_t(rows / B);
+  a.rt = plan.rt;
+  a.groups = plan.groups;
+  a.parts = plan.parts_launched;
+  a.ppp = plan.ppp;
+  a.scale_mode = mode;
+  float sm = (opts && opts->sm_scale != 0.0f) ? opts->sm_scale : 1.0f / std::sqrt(float(kDim));
+  a.sm_log2 = sm * 1.4426950408889634f;
+
+  hipEvent_t e0 = opts ? reinterpret_cast<hipEvent_t>(opts->main_begin_event) : nullptr;
+  hipEvent_t e1 = opts ? reinterpret_cast<hipEvent_t>(opts->main_end_event) : nullptr;
+  hipError_t he = launch_decode(a, plan.grid, plan.merge, plan.sparse, e0, e1, stream);
+  if (he != hipSuccess) return fail(PA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(he));
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace fp8pa
+
+using namespace fp8pa;
+
+extern "C" {
+
+int pa_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+              const pa_tensor* k_scale, const pa_tensor* v_scale, const pa_tensor* block_table,
+              const pa_tensor* context_lens, const pa_tensor* cu_seqlens_q,
+              const pa_tensor* sparse_page_idx, int scale_mode, pa_tensor* out, void* stream) {
+  return decode_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, cu_seqlens_q,
+                     sparse_page_idx, scale_mode, out, nullptr, stream);
+}
+
+int pa_decode_ex(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                 const pa_tensor* k_scale, const pa_tensor* v_scale, const pa_tensor* block_table,
+                 const pa_tensor* context_lens, const pa_tensor* cu_seqlens_q,
+                 const pa_tensor* sparse_page_idx, int scale_mode, pa_tensor* out,
+                 const pa_decode_opts* opts, void* stream) {
+  return decode_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, cu_seqlens_q,
+                     sparse_page_idx, scale_mode, out, opts, stream);
+}
+
+int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,
+                   pa_tensor* k_cache, pa_tensor* v_cache, pa_tensor* k_scale, pa_tensor* v_scale,
+                   int scale_mode, void* stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_tensor(k_new, "k_new"))) return rc;
+  if ((rc = check_tensor(v_new, "v_new"))) return rc;
+  if (k_new->dtype != PA_DTYPE_F32 && k_new->dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_DTYPE, "k_new must be float32 or bfloat16");
+  if (v_new->dtype != k_new->dtype) return fail(PA_ERR_DTYPE, "k_new and v_new dtypes differ");
+  if (k_new->ndim != 3 || v_new->ndim != 3) return fail(PA_ERR_SHAPE, "k_new, v_new must be [T, Hkv, 128]");
+  for (int i = 0; i < 3; ++i)
+    if (k_new->shape[i] != v_new->shape[i]) return fail(PA_ERR_SHAPE, "k_new and v_new shapes differ");
+  const int64_t T = k_new->shape[0], hkv_in = k_new->shape[1];
+  if (k_new->shape[2] != kDim) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 128");
+  const int64_t esz = k_new->dtype == PA_DTYPE_F32 ? 4 : 2;
+  for (const pa_tensor* t : {k_new, v_new})
+    if (t->stride[2] != 1 || t->stride[0] % 2 || t->stride[1] % 2 || !aligned(t->data, uintptr_t(2 * esz)))
+      return fail(PA_ERR_LAYOUT, "k_new/v_new: last dim contiguous, even strides, aligned pairs");
+  if ((rc = check_tensor(slot_mapping, "slot_mapping"))) return rc;
+  if (slot_mapping->dtype != PA_DTYPE_I64 || slot_mapping->ndim != 1 || slot_mapping->shape[0] != T ||
+      (T > 1 && slot_mapping->stride[0] != 1))
+    return fail(PA_ERR_SHAPE, "slot_mapping must be contiguous int64 [T]");
+  int64_t nb = 0, hkv = 0, nb2 = 0, hkv2 = 0;
+  if ((rc = check_cache(k_cache, "k_cache", &nb, &hkv))) return rc;
+  if ((rc = check_cache(v_cache, "v_cache", &nb2, &hkv2))) return rc;
+  if (nb2 != nb || hkv2 != hkv) return fail(PA_ERR_SHAPE, "k_cache and v_cache shapes differ");
+  if (hkv != hkv_in) return fail(PA_ERR_SHAPE, "k_new has a different number of KV heads than the cache");
+  if (scale_mode < PA_SCALE_NONE || scale_mode > PA_SCALE_PER_TOKEN)
+    return fail(PA_ERR_INVALID_ARG, "unknown scale_mode");
+  if ((rc = check_scales(k_scale, v_scale, scale_mode, nb, hkv))) return rc;
+  if (T == 0) return PA_OK;
+
+  WriteArgs a{};
+  a.k_new = k_new->data;
+  a.v_new = v_new->data;
+  a.k_tok_stride = k_new->stride[0];
+  a.k_head_stride = k_new->stride[1];
+  a.v_tok_stride = v_new->stride[0];
+  a.v_head_stride = v_new->stride[1];
+  a.in_bf16 = k_new->dtype == PA_DTYPE_BF16;
+  a.slots = static_cast<const int64_t*>(slot_mapping->data);
+  a.k_cache = static_cast<uint8_t*>(k_cache->data);
+  a.v_cache = static_cast<uint8_t*>(v_cache->data);
+  a.k_scale = scale_mode == PA_SCALE_NONE ? nullptr : static_cast<float*>(k_scale->data);
+  a.v_scale = scale_mode == PA_SCALE_NONE ? nullptr : static_cast<float*>(v_scale->data);
+  a.num_blocks = nb;
+  a.tokens = T;
+  a.hkv = int32_t(hkv);
+  a.scale_mode = scale_mode;
+  hipError_t he = launch_write(a, reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return fail(PA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(he));
+  return PA_OK;
+}
+
+int pa_query_support(const pa_config* cfg) {
+  g_err.clear();
+  if (!cfg) return fail(PA_ERR_INVALID_ARG, "cfg is NULL");
+  Plan p;
+  std::string err;
+  int rc = make_plan(*cfg, &p, &err);
+  if (rc) return fail(rc, err);
+  return PA_OK;
+}
+
+int pa_plan_describe(const pa_config* cfg, pa_plan_info* info) {
+  g_err.clear();
+  if (!cfg || !info) return fail(PA_ERR_INVALID_ARG, "cfg or info is NULL");
+  Plan p;
+  std::string err;
+  int rc = make_plan(*cfg, &p, &err);
+  if (rc) return fail(rc, err);
+  describe(p, info);
+  return PA_OK;
+}
+
+int pa_reserve(const pa_config* cfg, void* stream) {
+  g_err.clear();
+  if (!cfg) return fail(PA_ERR_INVALID_ARG, "cfg is NULL");
+  Plan p;
+  std::string err;
+  int rc = make_plan(*cfg, &p, &err);
+  if (rc) return fail(rc, err);
+  void* s = nullptr;
+  return get_scratch(reinterpret_cast<hipStream_t>(stream), size_t(p.scratch_bytes), &s);
+}
+
+int pa_release(void) {
+  g_err.clear();
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_arenas.empty()) return PA_OK;
+  int cur = 0;
+  hipGetDevice(&cur);
+  int rc = PA_OK;
+  for (auto& kv : g_arenas) {
+    if (!kv.second.ptr) continue;
+    hipSetDevice(kv.first.first);
+    if (hipDeviceSynchronize() != hipSuccess) rc = fail(PA_ERR_HIP, "hipDeviceSynchronize failed");
+    hipFree(kv.second.ptr);
+  }
+  g_arenas.clear();
+  hipSetDevice(cur);
+  return rc;
+}
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

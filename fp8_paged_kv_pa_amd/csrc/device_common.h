@@ -1,0 +1,72 @@
+// Device-side helpers for gfx950: vector types, FP8 <-> bf16/f32
+// conversion, wave reductions.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace fp8pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Eight OCP e4m3fn bytes (two dwords, byte 0 first) to eight bf16.  Every
+// e4m3fn value, subnormals included, is a bf16 value, so this is exact.
+// v_cvt_scalef32_pk_bf16_fp8 converts the two bytes of the selected 16-bit
+// half; a scale of 1.0 leaves the values unchanged.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// fp32 -> e4m3fn byte: round to nearest, ties to even, saturate to +-448
+// (infinities included); NaN -> 0x7F with the sign.  Pure integer work on
+// the fp32 bit pattern, so its result does not depend on any conversion
+// instruction's overflow mode.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t bits = __float_as_uint(y);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t a = bits & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;   // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;  // |y| >= 448
+  if (a < 0x3C800000u) {                       // |y| < 2^-6: spacing 2^-9
+    const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);  // exact scale, RNE
+    return sign | uint32_t(m);                 // 8 -> 0x08 = 2^-6, the smallest normal
+  }
+  // normal: biased e4m3 exponent = fp32 exponent - 120, three mantissa bits
+  uint32_t code = (((a >> 23) - 120u) << 3) | ((a >> 20) & 7u);
+  const uint32_t rem = a & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) code += 1;  // carry may bump exponent
+  if (code > 0x7Eu) code = 0x7Eu;
+  return sign | code;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+}  // namespace fp8pa

@@ -1,0 +1,71 @@
+// Kernel argument blocks and launcher entry points shared by the host API
+// (api.cpp) and the kernel translation units.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/fp8pa.h"
+
+namespace fp8pa {
+
+// Arguments of the main decode kernel and of the merge kernel.
+struct DecodeArgs {
+  const uint16_t* q;          // bf16 [rows, Hq, 128]
+  int64_t q_row_stride;       // elements
+  int64_t q_head_stride;
+  const uint8_t* k_cache;     // [num_blocks, Hkv, 16384]
+  const uint8_t* v_cache;
+  const float* k_scale;       // per-token [num_blocks, Hkv, 128] or scalar [1] or null
+  const float* v_scale;
+  const int32_t* block_table; // [batch, W]
+  int64_t bt_stride;
+  const int32_t* context_lens;  // [batch]
+  const int32_t* cu_seqlens_q;  // [batch+1] or null (uniform)
+  const int32_t* sparse_idx;    // [rows, topk] or null
+  int64_t sp_stride;
+  uint16_t* out;              // bf16 [rows, Hq, 128]
+  int64_t out_row_stride;
+  int64_t out_head_stride;
+  float* part_ml;             // scratch: (m, l) float2 [parts][rows][Hq]
+  float* part_acc;            // scratch: float [parts][rows][Hq][128]
+  int64_t num_blocks;
+  int32_t hkv;
+  int32_t rows;
+  int32_t batch;
+  int32_t width;              // block-table width W
+  int32_t topk;
+  int32_t uniform_q_len;      // rows/batch when cu_seqlens_q is null
+  int32_t rt;                 // rows per workgroup (template value, repeated)
+  int32_t groups;
+  int32_t parts;              // partitions launched per unit
+  int32_t ppp;                // pages / list entries per partition
+  int32_t scale_mode;
+  float sm_log2;              // sm_scale * log2(e)
+};
+
+struct WriteArgs {
+  const void* k_new;          // f32 or bf16 [T, Hkv, 128]
+  const void* v_new;
+  int64_t k_tok_stride, k_head_stride;  // elements
+  int64_t v_tok_stride, v_head_stride;
+  int32_t in_bf16;            // 1: inputs are bf16, 0: f32
+  const int64_t* slots;       // [T]
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  float* k_scale;             // per-token output, scalar input, or null
+  float* v_scale;
+  int64_t num_blocks;
+  int64_t tokens;
+  int32_t hkv;
+  int32_t scale_mode;
+};
+
+// Launchers (defined with their kernels).  Return hipSuccess or the launch
+// error.
+hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool sparse,
+                         hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
+hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
+
+}  // namespace fp8pa

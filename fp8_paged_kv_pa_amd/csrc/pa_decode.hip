@@ -1,0 +1,500 @@
+// Paged decode attention over the page-shuffled e4m3fn cache (gfx950).
+//
+// What is computed (ROCm/ATOM pull request 2614, "Change": dense and sparse
+// decode through one shuffled paged-decode contract with per-token FP8
+// scales; ROCm/ATOM pull request 2122, section 2: row i of a q_len-L request
+// sees context_len - L + i + 1 tokens; vllm-project/vllm pull request 52060,
+// "Suggested Fix": scalar scales fold into the score scale and the
+// normalized output):
+//   out[row, 16h+j] = sum_t softmax_t(sm * <q, ks_t k_t>) * vs_t v_t
+// over the row's tokens, exact softmax, split into partitions whose
+// (max, sum, accumulator) partials a log-sum-exp merge combines (ROCm/ATOM
+// pull request 2710 review, "Must fix" 1, names that partial scratch).
+//
+// Kernel shape.  A workgroup of 4 wavefronts owns (request or row, KV head,
+// row group, partition).  Wave w handles token chunk w (32 tokens) of every
+// page of the partition, so the 4 waves stream one page together.  Each
+// lane's 16-byte loads are, byte for byte, its matrix-core operands (the
+// cache layout is defined that way), so nothing goes through LDS in the
+// loop:
+//   S^T[token, head] = K[token, d] * Q^T[d, head]     (bf16 MFMA 16x16x32)
+//   O^T[d, head]    += V^T[d, token] * P^T[token, head]
+// Computing S transposed leaves each lane with one head and 8 tokens, which
+// is exactly the B-operand of the P*V product: no transpose of P.  The
+// e4m3 -> bf16 conversion is exact; the per-token K scale multiplies each
+// score column once and the per-token V scale multiplies P before the
+// bf16 rounding, so no scale touches a 128-wide vector.
+// Online softmax in the exp2 domain; the running max is only raised when a
+// chunk exceeds it by more than 2^8, so P stays <= 256 and the rescale of
+// the accumulators is rare.  The four waves' partials merge through LDS at
+// the end; with one partition the workgroup writes bf16 output directly.
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8pa {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr float kLazyMax = 8.0f;  // log2 headroom before the running max moves
+constexpr int kAccPad = 132;      // LDS row pitch (floats) for the wave merge
+
+struct Chunk {
+  u32x4 k[4];
+  u32x4 v[4];
+  f32x4 ks[2];
+  f32x4 vs[2];
+};
+
+// Request of a query row: largest b with cu[b] <= row.
+__device__ __forceinline__ int find_request(const int32_t* cu, int batch, int row) {
+  int lo = 0, hi = batch;  // answer in [0, batch)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= row) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Rows [start, start + L) of request b from cu_seqlens_q, clamped into
+// [0, rows) so that a malformed cu can only give wrong values, never an
+// access outside q or out.
+__device__ __forceinline__ void request_rows(const DecodeArgs& a, int b, int* start, int* L) {
+  const int s = min(max(a.cu_seqlens_q[b], 0), a.rows);
+  const int e = min(max(a.cu_seqlens_q[b + 1], s), a.rows);
+  *start = s;
+  *L = e - s;
+}
+
+template <bool PER_TOKEN>
+__device__ __forceinline__ void load_chunk(Chunk& c, const DecodeArgs& a, int64_t blk, int wave,
+                                           int lane) {
+  const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + blk * 16384 + wave * 4096) + lane;
+  const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_cache + blk * 16384 + wave * 4096) + lane;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c.k[i] = kp[64 * i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c.v[i] = vp[64 * i];
+  if constexpr (PER_TOKEN) {
+    const int g = lane >> 4;
+    const f32x4* ksp = reinterpret_cast<const f32x4*>(a.k_scale + blk * 128 + wave * 32);
+    const f32x4* vsp = reinterpret_cast<const f32x4*>(a.v_scale + blk * 128 + wave * 32);
+    c.ks[0] = ksp[g];
+    c.ks[1] = ksp[4 + g];
+    c.vs[0] = vsp[g];
+    c.vs[1] = vsp[4 + g];
+  }
+}
+
+template <int RT, bool PER_TOKEN, bool SPARSE>
+__global__ __launch_bounds__(kWave * kWaves, (RT <= 2 ? 2 : 1)) void pa_decode_main(DecodeArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;   // lane group: tokens 4g..4g+3 of each 16-token tile
+  const int hr = lane & 15;  // query head within the GQA group
+  const int Hq = 16 * a.hkv;
+
+  const int part = int(blockIdx.x % uint32_t(a.parts));
+  const int64_t unit = blockIdx.x / uint32_t(a.parts);
+
+  // ---- which rows, which request, which tokens -------------------------
+  int h, b, row0, nrows, lim0;  // row row0+i sees tokens t < lim0 + i
+  if constexpr (SPARSE) {
+    h = int(unit % a.hkv);
+    row0 = int(unit / a.hkv);
+    int start, L;
+    if (a.cu_seqlens_q) {
+      b = find_request(a.cu_seqlens_q, a.batch, row0);
+      request_rows(a, b, &start, &L);
+    } else {
+      L = a.uniform_q_len;
+      b = row0 / L;
+      start = b * L;
+    }
+    nrows = 1;
+    lim0 = a.context_lens[b] - L + (row0 - start) + 1;
+  } else {
+    const int gi = int(unit % a.groups);
+    const int64_t bh = unit / a.groups;
+    h = int(bh % a.hkv);
+    b = int(bh / a.hkv);
+    int start, L;
+    if (a.cu_seqlens_q) {
+      request_rows(a, b, &start, &L);
+    } else {
+      L = a.uniform_q_len;
+      start = b * L;
+    }
+    const int i0 = gi * RT;
+    if (i0 >= L) return;  // this request has no rows in this group
+    nrows = min(RT, L - i0);
+    row0 = start + i0;
+    lim0 = a.context_lens[b] - L + i0 + 1;
+  }
+  const int cap = a.width * 128;
+  const int lim_min = max(0, min(lim0, cap));
+  const int lim_max = max(0, min(lim0 + nrows - 1, cap));
+
+  int n0 = part * a.ppp, n1;
+  if constexpr (SPARSE) {
+    n1 = min(n0 + a.ppp, a.topk);
+  } else {
+    const int npages = (lim_max + 127) >> 7;
+    n1 = min(n0 + a.ppp, npages);
+  }
+  if (n0 >= n1 && a.parts > 1) return;  // nothing here; the merge skips this partition
+
+  // ---- query operands: B of S^T = K Q^T, lane = (head hr, dims 8g..8g+7 of each 32) ----
+  bf16x8 qop[RT][4];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (r < nrows) {
+        const uint16_t* qp = a.q + int64_t(row0 + r) * a.q_row_stride +
+                             int64_t(16 * h + hr) * a.q_head_stride + 32 * j + 8 * g;
+        qop[r][j] = *reinterpret_cast<const bf16x8*>(qp);
+      } else {
+        qop[r][j] = bf16x8{};
+      }
+    }
+  }
+
+  float k_fold = a.sm_log2;  // scalar / none: the K scale folds into the score scale
+  float v_fold = 1.0f;       // ... and the V scale into the normalized output
+  if constexpr (!PER_TOKEN) {
+    if (a.k_scale) k_fold *= *a.k_scale;
+    if (a.v_scale) v_fold = *a.v_scale;
+  }
+
+  f32x4 acc[RT][8];
+  float m_run[RT], l_run[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[r][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // physical page and first token of list position n; -1 if nothing to read
+  auto page_at = [&](int n, int* tbase) -> int64_t {
+    int ln = n;
+    if constexpr (SPARSE) {
+      ln = a.sparse_idx[int64_t(row0) * a.sp_stride + n];
+      if (ln < 0 || ln >= a.width || ln * 128 >= lim_max) return -1;
+    }
+    const int P = a.block_table[int64_t(b) * a.bt_stride + ln];
+    if (P < 0 || P >= a.num_blocks) return -1;
+    *tbase = ln * 128;
+    return int64_t(P) * a.hkv + h;
+  };
+
+  auto process = [&](Chunk& c, int tbase) {
+    const int t0 = tbase + 32 * wave;
+    if (t0 >= lim_max) return;  // chunk past the context for every row (uniform)
+    const bool full = t0 + 32 <= lim_min;
+
+    // token of this lane's score slot e: t0 + 16*(e/4) + 4g + e%4
+    if (!full) {
+      // zero V bytes of tokens past the context: their bytes were never written
+      uint32_t m0 = 0, m1 = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (t0 + 4 * g + e < lim_max) m0 |= 0xFFu << (8 * e);
+        if (t0 + 16 + 4 * g + e < lim_max) m1 |= 0xFFu << (8 * e);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c.v[i][0] &= m0; c.v[i][1] &= m1; c.v[i][2] &= m0; c.v[i][3] &= m1;
+      }
+    }
+
+    bf16x8 kop[2][4];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        kop[tau][j] = fp8x8_to_bf16x8(c.k[2 * tau + (j >> 1)][2 * (j & 1)],
+                                      c.k[2 * tau + (j >> 1)][2 * (j & 1) + 1]);
+
+    float kc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (PER_TOKEN) kc[e] = c.ks[e >> 2][e & 3] * k_fold;
+      else kc[e] = k_fold;
+    }
+
+    bf16x8 vop[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+      vop[d] = fp8x8_to_bf16x8(c.v[d >> 1][2 * (d & 1)], c.v[d >> 1][2 * (d & 1) + 1]);
+
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      if (r >= nrows) break;
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][j], qop[r][j], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][j], qop[r][j], s1, 0, 0, 0);
+      }
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = s0[e] * kc[e];
+        x[4 + e] = s1[e] * kc[4 + e];
+      }
+      const int lim_r = min(lim0 + r, cap);
+      if (!full) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = t0 + 16 * (e >> 2) + 4 * g + (e & 3);
+          x[e] = t < lim_r ? x[e] : -INFINITY;
+        }
+      }
+      float lm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      const bool need = lm > m_run[r] + kLazyMax;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        float gm = fmaxf(lm, __shfl_xor(lm, 16, kWave));
+        gm = fmaxf(gm, __shfl_xor(gm, 32, kWave));
+        const float mn = fmaxf(m_run[r], gm);
+        const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[r] - mn);
+        l_run[r] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[r][d] *= alpha;
+        m_run[r] = mn;
+      }
+      const float mu = (m_run[r] == -INFINITY) ? 0.0f : m_run[r];
+      float p[8];
+      float ps = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(x[e] - mu);
+        ps += p[e];
+      }
+      l_run[r] += ps;
+      bf16x8 pop;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float pv = p[e];
+        if constexpr (PER_TOKEN) pv *= c.vs[e >> 2][e & 3];
+        if (!full) {
+          const int t = t0 + 16 * (e >> 2) + 4 * g + (e & 3);
+          pv = t < lim_r ? pv : 0.0f;
+        }
+        pop[e] = (__bf16)pv;
+      }
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[d], pop, acc[r][d], 0, 0, 0);
+    }
+  };
+
+  // ---- stream the partition's pages, next page's loads in flight --------
+  if (n0 < n1) {
+    Chunk ca, cb;
+    int ta = 0, tb = 0;
+    int64_t pa = page_at(n0, &ta);
+    if (pa >= 0) load_chunk<PER_TOKEN>(ca, a, pa, wave, lane);
+    for (int n = n0; n < n1; n += 2) {
+      int64_t pb = -1;
+      if (n + 1 < n1) {
+        pb = page_at(n + 1, &tb);
+        if (pb >= 0) load_chunk<PER_TOKEN>(cb, a, pb, wave, lane);
+      }
+      if (pa >= 0) process(ca, ta);
+      if (n + 1 >= n1) break;
+      pa = -1;
+      if (n + 2 < n1) {
+        pa = page_at(n + 2, &ta);
+        if (pa >= 0) load_chunk<PER_TOKEN>(ca, a, pa, wave, lane);
+      }
+      if (pb >= 0) process(cb, tb);
+    }
+  }
+
+  // ---- merge the four waves, then write output or the partition partial --
+  __shared__ float sm_ml[kWaves][RT][16][2];
+  __shared__ float sm_acc[kWaves][16][kAccPad];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    float lh = l_run[r];
+    lh += __shfl_xor(lh, 16, kWave);
+    lh += __shfl_xor(lh, 32, kWave);
+    if (g == 0) {
+      sm_ml[wave][r][hr][0] = m_run[r];
+      sm_ml[wave][r][hr][1] = lh;
+    }
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int oh = t >> 4;        // output head handled by this thread
+  const int od = (t & 15) * 8;  // first of its 8 dims
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    if (r >= nrows) break;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[w][r][hr][0]);
+    const float f = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[r] - M);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      f32x4 v = acc[r][d] * f;
+      *reinterpret_cast<f32x4*>(&sm_acc[wave][hr][16 * d + 4 * g]) = v;
+    }
+    __syncthreads();
+    float Mo = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) Mo = fmaxf(Mo, sm_ml[w][r][oh][0]);
+    float Ls = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm_ml[w][r][oh][0];
+      const float fw = (Mo == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - Mo);
+      Ls += fw * sm_ml[w][r][oh][1];
+    }
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      s0 += *reinterpret_cast<const f32x4*>(&sm_acc[w][oh][od]);
+      s1 += *reinterpret_cast<const f32x4*>(&sm_acc[w][oh][od + 4]);
+    }
+    const int row = row0 + r;
+    const int qh = 16 * h + oh;
+    if (a.parts == 1) {
+      const float inv = Ls > 0.0f ? v_fold / Ls : 0.0f;
+      uint32_t packed[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        packed[e] = uint32_t(f32_to_bf16_rne(s0[2 * e] * inv)) |
+                    (uint32_t(f32_to_bf16_rne(s0[2 * e + 1] * inv)) << 16);
+        packed[2 + e] = uint32_t(f32_to_bf16_rne(s1[2 * e] * inv)) |
+                        (uint32_t(f32_to_bf16_rne(s1[2 * e + 1] * inv)) << 16);
+      }
+      uint16_t* op = a.out + int64_t(row) * a.out_row_stride + int64_t(qh) * a.out_head_stride + od;
+      *reinterpret_cast<u32x4*>(op) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    } else {
+      const int64_t pi = (int64_t(part) * a.rows + row) * Hq + qh;
+      f32x4* ap = reinterpret_cast<f32x4*>(a.part_acc + pi * 128 + od);
+      ap[0] = s0;
+      ap[1] = s1;
+      if ((t & 15) == 0) {
+        a.part_ml[2 * pi] = Mo;
+        a.part_ml[2 * pi + 1] = Ls;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// One wavefront per (row, query head): combine the partitions' (m, l, acc)
+// with log-sum-exp weights and write bf16.  Lane owns dims 2*lane, 2*lane+1.
+__global__ __launch_bounds__(256) void pa_merge(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int Hq = 16 * a.hkv;
+  const int64_t pair = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (pair >= int64_t(a.rows) * Hq) return;
+  const int row = int(pair / Hq);
+  const int qh = int(pair - int64_t(row) * Hq);
+
+  int P = a.parts;
+  if (a.sparse_idx == nullptr) {
+    int b, start, L;
+    if (a.cu_seqlens_q) {
+      b = find_request(a.cu_seqlens_q, a.batch, row);
+      request_rows(a, b, &start, &L);
+    } else {
+      L = a.uniform_q_len;
+      b = row / L;
+      start = b * L;
+    }
+    const int i = row - start;
+    const int gi = i / a.rt;
+    const int i_last = min(L, (gi + 1) * a.rt) - 1;
+    const int lim = max(0, min(a.context_lens[b] - L + i_last + 1, a.width * 128));
+    const int npages = (lim + 127) >> 7;
+    P = min((npages + a.ppp - 1) / a.ppp, a.parts);
+  }
+
+  float M = -INFINITY;
+  for (int p0 = 0; p0 < P; p0 += 64) {
+    const int p = p0 + lane;
+    const float m = p < P ? a.part_ml[2 * ((int64_t(p) * a.rows + row) * Hq + qh)] : -INFINITY;
+    M = fmaxf(M, wave_max(m));
+  }
+  float ox = 0.0f, oy = 0.0f, Ls = 0.0f;
+  if (M != -INFINITY) {
+    for (int p0 = 0; p0 < P; p0 += 64) {
+      const int p = p0 + lane;
+      float w = 0.0f, lw = 0.0f;
+      if (p < P) {
+        const int64_t pi = (int64_t(p) * a.rows + row) * Hq + qh;
+        w = __builtin_amdgcn_exp2f(a.part_ml[2 * pi] - M);
+        lw = w * a.part_ml[2 * pi + 1];
+      }
+      Ls += wave_sum(lw);
+      const int cnt = min(64, P - p0);
+      for (int k = 0; k < cnt; ++k) {
+        const float wk = __shfl(w, k, kWave);
+        const int64_t pi = (int64_t(p0 + k) * a.rows + row) * Hq + qh;
+        const float2 v = *reinterpret_cast<const float2*>(a.part_acc + pi * 128 + 2 * lane);
+        ox += wk * v.x;
+        oy += wk * v.y;
+      }
+    }
+  }
+  float v_fold = 1.0f;
+  if (a.scale_mode != PA_SCALE_PER_TOKEN && a.v_scale) v_fold = *a.v_scale;
+  const float inv = Ls > 0.0f ? v_fold / Ls : 0.0f;
+  const uint32_t packed = uint32_t(f32_to_bf16_rne(ox * inv)) | (uint32_t(f32_to_bf16_rne(oy * inv)) << 16);
+  *reinterpret_cast<uint32_t*>(a.out + int64_t(row) * a.out_row_stride + int64_t(qh) * a.out_head_stride +
+                               2 * lane) = packed;
+}
+
+template <int RT, bool PT, bool SP>
+void launch_main_t(const DecodeArgs& a, int64_t grid, hipStream_t s) {
+  hipLaunchKernelGGL((pa_decode_main<RT, PT, SP>), dim3(uint32_t(grid)), dim3(kWave * kWaves), 0, s, a);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool sparse,
+                         hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  const bool pt = a.scale_mode == PA_SCALE_PER_TOKEN;
+  hipError_t e;
+  if (ev_begin) {
+    e = hipEventRecord(ev_begin, stream);
+    if (e != hipSuccess) return e;
+  }
+  // the one variant-selection table: (rows per group, per-token scales, sparse)
+  if (sparse) {
+    if (pt) launch_main_t<1, true, true>(a, grid, stream);
+    else launch_main_t<1, false, true>(a, grid, stream);
+  } else if (a.rt == 1) {
+    if (pt) launch_main_t<1, true, false>(a, grid, stream);
+    else launch_main_t<1, false, false>(a, grid, stream);
+  } else if (a.rt == 2) {
+    if (pt) launch_main_t<2, true, false>(a, grid, stream);
+    else launch_main_t<2, false, false>(a, grid, stream);
+  } else {
+    if (pt) launch_main_t<4, true, false>(a, grid, stream);
+    else launch_main_t<4, false, false>(a, grid, stream);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev_end) {
+    e = hipEventRecord(ev_end, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (merge) {
+    const int64_t pairs = int64_t(a.rows) * 16 * a.hkv;
+    hipLaunchKernelGGL(pa_merge, dim3(uint32_t((pairs + 3) / 4)), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace fp8pa

@@ -1,0 +1,127 @@
+// Configuration checks and the bucketed split-K plan (see plan.h).
+#include "plan.h"
+
+#include <algorithm>
+
+namespace fp8pa {
+
+namespace {
+
+int fail(std::string* err, int code, const std::string& msg) {
+  if (err) *err = msg;
+  return code;
+}
+
+}  // namespace
+
+int make_plan(const pa_config& c, Plan* out, std::string* err) {
+  if (!out) return fail(err, PA_ERR_INVALID_ARG, "plan output is NULL");
+  if (c.group_size != kGroup)
+    return fail(err, PA_ERR_UNSUPPORTED, "group_size must be 16 query heads per KV head, got " +
+                                             std::to_string(c.group_size));
+  if (c.head_dim != kDim)
+    return fail(err, PA_ERR_UNSUPPORTED, "head_dim must be 128, got " + std::to_string(c.head_dim));
+  if (c.page_size != kPage)
+    return fail(err, PA_ERR_UNSUPPORTED, "page_size must be 128 tokens, got " +
+                                             std::to_string(c.page_size));
+  if (c.num_kv_heads < 1 || c.num_kv_heads > kMaxKvHeads)
+    return fail(err, PA_ERR_UNSUPPORTED, "num_kv_heads must be in [1, 64], got " +
+                                             std::to_string(c.num_kv_heads));
+  if (c.kv_dtype != PA_DTYPE_U8 && c.kv_dtype != PA_DTYPE_F8E4M3)
+    return fail(err, PA_ERR_DTYPE, "KV cache must be uint8 or float8_e4m3fn bytes");
+  if (c.scale_mode != PA_SCALE_NONE && c.scale_mode != PA_SCALE_SCALAR &&
+      c.scale_mode != PA_SCALE_PER_TOKEN)
+    return fail(err, PA_ERR_INVALID_ARG, "unknown scale_mode " + std::to_string(c.scale_mode));
+  if (c.rows < 0 || c.batch < 1 || c.max_pages < 1 || c.topk < 0)
+    return fail(err, PA_ERR_SHAPE, "rows >= 0, batch >= 1, block-table width >= 1, topk >= 0 required");
+  if (c.rows > kMaxRows)
+    return fail(err, PA_ERR_CAPACITY, "rows " + std::to_string(c.rows) + " above the largest bucket " +
+                                          std::to_string(kMaxRows));
+  if (c.batch > kMaxBatch)
+    return fail(err, PA_ERR_CAPACITY, "batch above " + std::to_string(kMaxBatch));
+  if (c.max_pages > kMaxPages)
+    return fail(err, PA_ERR_CAPACITY, "block-table width above " + std::to_string(kMaxPages));
+  if (c.topk > kMaxTopk)
+    return fail(err, PA_ERR_CAPACITY, "topk above " + std::to_string(kMaxTopk));
+  if (c.force_parts < 0 || c.force_parts > kMaxParts)
+    return fail(err, PA_ERR_INVALID_ARG, "force_parts must be in [0, 256]");
+  if (c.max_q_len < 0) return fail(err, PA_ERR_INVALID_ARG, "max_q_len must be >= 0");
+  // Uniformity is never inferred from divisibility: without cu_seqlens_q the
+  // call *declares* every request has rows/batch rows, so rows must divide.
+  if (!c.ragged && c.rows % c.batch != 0)
+    return fail(err, PA_ERR_SHAPE,
+                "rows " + std::to_string(c.rows) + " not divisible by batch " + std::to_string(c.batch) +
+                    " and no cu_seqlens_q: a ragged segment needs cu_seqlens_q");
+
+  Plan p;
+  p.sparse = c.topk > 0;
+  const int64_t hkv = c.num_kv_heads;
+  int64_t npages;
+  if (p.sparse) {
+    p.rt = 1;
+    p.groups = 1;
+    p.lmax = 1;
+    p.units = c.rows * hkv;
+    npages = c.topk;
+  } else {
+    int64_t lmax;
+    if (!c.ragged) {
+      lmax = c.rows / c.batch;
+    } else if (c.max_q_len > 0) {
+      lmax = std::min<int64_t>(c.max_q_len, c.rows);
+    } else {
+      lmax = c.rows;  // unknown: the most any one request can own
+    }
+    lmax = std::max<int64_t>(lmax, 1);
+    p.lmax = int(lmax);
+    p.rt = lmax <= 1 ? 1 : (lmax <= 2 ? 2 : 4);
+    p.groups = int(ceil_div(lmax, p.rt));
+    p.units = c.batch * hkv * p.groups;
+    npages = c.max_pages;
+  }
+
+  p.rows_bucket = next_pow2(std::max<int64_t>(c.rows, 1));
+  p.pages_bucket = next_pow2(npages);
+  p.units_bucket = next_pow2(std::max<int64_t>(p.units, 1));
+
+  int64_t parts;
+  if (c.force_parts > 0) {
+    parts = c.force_parts;
+  } else {
+    parts = std::max<int64_t>(1, kTargetWorkgroups / p.units_bucket);
+  }
+  parts = std::min<int64_t>({parts, int64_t(kMaxParts), p.pages_bucket});
+  p.parts = int(std::max<int64_t>(parts, 1));
+  p.ppp = int(ceil_div(std::max<int64_t>(npages, 1), p.parts));
+  p.parts_launched = int(ceil_div(std::max<int64_t>(npages, 1), p.ppp));
+  p.merge = p.parts_launched > 1;
+  p.grid = p.units * p.parts_launched;
+  if (p.merge) {
+    // (m, l) pair + 128 accumulators per (partition, row, query head), sized
+    // by the bucket so one reservation serves the whole bucket.
+    const int64_t per = 2 + kDim;
+    p.scratch_bytes = int64_t(p.parts) * p.rows_bucket * hkv * kGroup * per * int64_t(sizeof(float));
+  }
+  if (p.scratch_bytes > kMaxScratchBytes)
+    return fail(err, PA_ERR_CAPACITY, "split-K scratch for this bucket exceeds 4 GiB");
+  *out = p;
+  if (err) err->clear();
+  return PA_OK;
+}
+
+void describe(const Plan& p, pa_plan_info* info) {
+  info->rows_per_group = p.rt;
+  info->groups = p.groups;
+  info->parts = p.parts_launched;
+  info->pages_per_part = p.ppp;
+  info->units = p.units;
+  info->grid_x = p.grid;
+  info->grid_y = 1;
+  info->rows_bucket = p.rows_bucket;
+  info->pages_bucket = p.pages_bucket;
+  info->scratch_bytes = p.scratch_bytes;
+  info->merge = p.merge ? 1 : 0;
+  info->reserved = 0;
+}
+
+}  // namespace fp8pa

@@ -1,0 +1,70 @@
+// Host-side planning for paged decode: configuration checks, the one
+// variant-selection table and the capacity-bucketed split-K plan.
+//
+// Pure C++ (no HIP headers) so it is also built on its own for host-only
+// tests.
+//
+// Bucketing follows ROCm/ATOM pull request 2710's review ("Must fix" 1):
+// plans and scratch must come from a bounded set of capacity buckets, not
+// one per row count.  Here the partition count and the scratch size depend
+// only on power-of-two buckets of (units, pages, rows), so scratch sized
+// for a bucket serves every call that falls in it.
+#pragma once
+
+#include <cstdint>
+#include <string>
+
+#include "../../include/fp8pa.h"
+
+namespace fp8pa {
+
+constexpr int kPage = 128;
+constexpr int kDim = 128;
+constexpr int kGroup = 16;
+constexpr int kBlockBytes = kPage * kDim;
+
+// Capacity limits (largest buckets).  Anything above is refused up front.
+constexpr int64_t kMaxRows = 65536;
+constexpr int64_t kMaxBatch = 65536;
+constexpr int64_t kMaxPages = 1 << 20;   // block-table width (2^27 tokens)
+constexpr int64_t kMaxTopk = 4096;
+constexpr int32_t kMaxKvHeads = 64;
+constexpr int32_t kMaxParts = 256;
+constexpr int64_t kMaxScratchBytes = int64_t(4) << 30;
+
+// Workgroups the plan aims for: enough to cover 256 CUs several times.
+constexpr int64_t kTargetWorkgroups = 2048;
+
+struct Plan {
+  int rt = 1;              // query rows per workgroup (1, 2 or 4)
+  int groups = 1;          // row groups per request (dense)
+  int parts = 1;           // split-K partitions per unit (scratch is sized for this)
+  int parts_launched = 1;  // partitions that can hold work given the real width
+  int ppp = 1;             // pages (dense) or list entries (sparse) per partition
+  int lmax = 1;            // bound on q_len used by the plan
+  bool sparse = false;
+  bool merge = false;
+  int64_t units = 0;       // dense: batch*Hkv*groups; sparse: rows*Hkv
+  int64_t grid = 0;        // main-kernel workgroups (1-D)
+  int64_t rows_bucket = 1;
+  int64_t pages_bucket = 1;
+  int64_t units_bucket = 1;
+  int64_t scratch_bytes = 0;
+};
+
+inline int64_t next_pow2(int64_t x) {
+  int64_t p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Checks a configuration and builds its plan.  Returns PA_OK or a pa_status
+// and fills `err`.
+int make_plan(const pa_config& cfg, Plan* plan, std::string* err);
+
+// Fills the public description of a plan.
+void describe(const Plan& p, pa_plan_info* info);
+
+}  // namespace fp8pa

@@ -1,0 +1,257 @@
+/*
+ * fp8pa -- paged-attention decode over a page-shuffled FP8 (OCP e4m3fn) KV
+ * cache with per-token K/V scales, for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every argument is a plain pointer or size; tensors travel as
+ * `pa_tensor` descriptors (data pointer, dtype, shape, strides in elements).
+ * Device tensors live in the memory of the current HIP device.  The caller
+ * owns every tensor and the stream; the library keeps no pointer to them
+ * after a call returns.  The only memory the library owns is its split-K
+ * scratch (see pa_reserve).
+ *
+ * Sources for the operations (web pages on serving MiniMax-M3 with an FP8
+ * KV cache on AMD GPUs):
+ *   [ATOM-2614]  ROCm/ATOM pull request 2614 -- general shuffled
+ *                paged-decode contract for per-token FP8 KV: sections
+ *                "Problem" and "Change".
+ *   [ATOM-2710]  ROCm/ATOM pull request 2710 -- FlyDSL paged decode on
+ *                gfx1250, and its review ("Must fix" 1: capacity buckets and
+ *                split-K scratch; "Should fix" 2: refuse unsupported calls
+ *                at startup; "Smaller": one shared cache writer).
+ *   [ATOM-2122]  ROCm/ATOM pull request 2122, "fix(minimax-m3): unblock fp8
+ *                KV cache and EAGLE3 spec decode on the vLLM plugin",
+ *                section 2: multi-row causal cutoff, ragged segments.
+ *   [vLLM-52060] vllm-project/vllm pull request 52060, "[ROCm][Perf] Fold
+ *                scalar KV scales in MiniMax-M3 sparse attention", section
+ *                "Suggested Fix": the scalar-scale fold.
+ *
+ * ---------------------------------------------------------------------------
+ * Fixed geometry: 128-token pages, head dim 128, 16 query heads per KV head
+ * (GQA group).  Query head 16*h + j reads KV head h.
+ *
+ * Cache layout (this library's definition of "page-shuffled"; [ATOM-2614]
+ * names the shuffled page without giving its byte order):
+ *   k_cache, v_cache: uint8 (or float8_e4m3fn) [num_blocks, Hkv, 16384],
+ *     contiguous.  Block (p, h) starts at byte (p*Hkv + h)*16384.  Inside a
+ *     block, token slot o (0..127) and dim d (0..127) are at
+ *       K: c=o/32, tau=(o%32)/16, r=o%16, j=d/32, g=(d%32)/8, u=d%8,
+ *          4096*c + 1024*(2*tau + j/2) + 16*(16*g + r) + 8*(j%2) + u
+ *       V: c=o/32, tau=(o%32)/16, w=o%16, g=w/4, e=4*tau + w%4,
+ *          delta=d/16, r=d%16,
+ *          4096*c + 1024*(delta/2) + 16*(16*g + r) + 8*(delta%2) + e
+ *     so each 32-token chunk is one contiguous 4 KiB run and every aligned
+ *     16-byte piece is one lane's matrix-core operand.
+ *   k_scale, v_scale:
+ *     PA_SCALE_PER_TOKEN: float32 [num_blocks, Hkv, 128] contiguous, the
+ *       scale of (page, KV head, token slot) ([ATOM-2614] "Problem": one
+ *       scale per token for K and for V; "Change": cache and scale views are
+ *       collapsed per KV head the same way).
+ *     PA_SCALE_SCALAR: float32 with one element each ([vLLM-52060]).
+ *     PA_SCALE_NONE: ignored (may be NULL).
+ *   Dequantized value = e4m3fn(code) * scale.
+ *
+ * Which tokens a query row sees ([ATOM-2122] section 2): the rows of a
+ * request are consecutive; a request with q_len L owns L rows and its
+ * context length counts them, so row i (0-based) attends tokens
+ * t < context_len - L + i + 1, capped at block_table width * 128.  q_len is
+ * cu_seqlens_q[b+1] - cu_seqlens_q[b] when cu_seqlens_q is given (ragged),
+ * else rows / batch for every request (uniform; rows % batch != 0 is an
+ * error, never a guess).  A row that sees no token outputs 0.
+ */
+#ifndef FP8PA_H
+#define FP8PA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_MAX_DIMS 6
+
+/* Element types of a pa_tensor. */
+typedef enum pa_dtype {
+  PA_DTYPE_U8 = 1,       /* raw FP8 bytes (caches labelled uint8)           */
+  PA_DTYPE_F8E4M3 = 2,   /* OCP float8_e4m3fn                               */
+  PA_DTYPE_BF16 = 3,
+  PA_DTYPE_F32 = 4,
+  PA_DTYPE_I32 = 5,
+  PA_DTYPE_I64 = 6
+} pa_dtype;
+
+/* Scale modes ([vLLM-52060] "Suggested Fix": no-scale, scalar (its
+ * KV_SCALE_MODE 1) and per-token/head). */
+typedef enum pa_scale_mode {
+  PA_SCALE_NONE = 0,
+  PA_SCALE_SCALAR = 1,
+  PA_SCALE_PER_TOKEN = 2
+} pa_scale_mode;
+
+/* Return codes.  Every host-checkable problem is reported before anything is
+ * launched ([ATOM-2710] review "Should fix" 2; [ATOM-2614] "Change": decline
+ * before the low-level launcher aborts).  pa_last_error() has the text. */
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,   /* NULL where a tensor is required, bad enum    */
+  PA_ERR_DTYPE = -2,         /* wrong element type                           */
+  PA_ERR_SHAPE = -3,         /* shapes disagree, or rows % batch with no cu  */
+  PA_ERR_LAYOUT = -4,        /* strides / alignment the kernels cannot read  */
+  PA_ERR_UNSUPPORTED = -5,   /* geometry other than 128/128/16               */
+  PA_ERR_CAPACITY = -6,      /* beyond the largest capacity bucket           */
+  PA_ERR_NOT_RESERVED = -7,  /* scratch would have to grow during capture    */
+  PA_ERR_HIP = -8            /* a HIP runtime call failed                    */
+} pa_status;
+
+/* Tensor descriptor.  Strides are in elements.  `data` is a device pointer
+ * for every tensor the kernels read or write. */
+typedef struct pa_tensor {
+  void* data;
+  int32_t dtype;                 /* pa_dtype */
+  int32_t ndim;
+  int64_t shape[PA_MAX_DIMS];
+  int64_t stride[PA_MAX_DIMS];
+} pa_tensor;
+
+/* Optional knobs of pa_decode_ex.  Zero-initialise, then set what you need. */
+typedef struct pa_decode_opts {
+  float sm_scale;          /* 0 => 1/sqrt(128)                                */
+  int32_t max_q_len;       /* ragged only: caller-measured max rows per       */
+                           /* request (0 => unknown, bounded by rows)         */
+  int32_t force_parts;     /* 0 => plan chooses; else split-K partitions      */
+  void* main_begin_event;  /* hipEvent_t recorded on `stream` right before    */
+  void* main_end_event;    /* and right after the main kernel (may be NULL)   */
+} pa_decode_opts;
+
+/* Host-side description of a decode call, for capability queries, planning
+ * and scratch reservation without any device data. */
+typedef struct pa_config {
+  int32_t num_kv_heads;    /* Hkv                                            */
+  int32_t group_size;      /* query heads per KV head: must be 16            */
+  int32_t head_dim;        /* must be 128                                    */
+  int32_t page_size;       /* must be 128                                    */
+  int32_t kv_dtype;        /* PA_DTYPE_U8 or PA_DTYPE_F8E4M3                 */
+  int32_t scale_mode;      /* pa_scale_mode                                  */
+  int64_t rows;            /* query rows (sum of q_len)                      */
+  int64_t batch;           /* requests                                       */
+  int64_t max_pages;       /* block_table width                              */
+  int64_t topk;            /* sparse list length; 0 => dense                 */
+  int32_t ragged;          /* 1 if cu_seqlens_q is given                     */
+  int32_t max_q_len;       /* as pa_decode_opts.max_q_len                    */
+  int32_t force_parts;     /* as pa_decode_opts.force_parts                  */
+  int32_t reserved;
+} pa_config;
+
+/* The launch plan a config maps to (pa_plan_describe). */
+typedef struct pa_plan_info {
+  int32_t rows_per_group;  /* query rows one workgroup carries (1, 2 or 4)   */
+  int32_t groups;          /* row groups per request (dense) or 1 (sparse)   */
+  int32_t parts;           /* split-K partitions per unit                    */
+  int32_t pages_per_part;  /* pages (dense) or list entries (sparse) per part*/
+  int64_t units;           /* (request|row) x KV head x group                */
+  int64_t grid_x, grid_y;  /* main-kernel grid                               */
+  int64_t rows_bucket;     /* capacity bucket of rows (power of two)         */
+  int64_t pages_bucket;    /* capacity bucket of pages / topk                */
+  int64_t scratch_bytes;   /* split-K scratch this bucket needs (0 if none)  */
+  int32_t merge;           /* 1 if the LSE merge kernel runs                 */
+  int32_t reserved;
+} pa_plan_info;
+
+/*
+ * pa_decode -- paged decode attention ([ATOM-2614] "Change": dense max-q-len-1
+ * per-token FP8 decode through the general shuffled contract, the same
+ * contract for sparse decode; [ATOM-2122] section 2: uniform and ragged
+ * multi-row decode; [vLLM-52060] "Suggested Fix": scale modes).
+ *
+ *   q             bf16 [rows, 16*Hkv, 128], last dim contiguous, 16-byte
+ *                 aligned rows.
+ *   k_cache,
+ *   v_cache       u8/f8e4m3 [num_blocks, Hkv, 16384] contiguous (layout above).
+ *   k_scale,
+ *   v_scale       see "scale" above, per scale_mode.
+ *   block_table   int32 [batch, W]: physical page of each logical page.  Only
+ *                 entries below ceil(limit/128) (dense) or named by the
+ *                 sparse list are read.  Entries outside [0, num_blocks)
+ *                 contribute no tokens.
+ *   context_lens  int32 [batch]: tokens in each request's context, counting
+ *                 the request's own query rows.
+ *   cu_seqlens_q  int32 [batch+1] (ragged: row starts, cu[0] = 0,
+ *                 cu[batch] = rows, non-decreasing) or NULL (uniform).
+ *   sparse_page_idx  int32 [rows, topk] logical page numbers each row attends
+ *                 (block-sparse; -1 = padding; no duplicates) or NULL (dense).
+ *   scale_mode    pa_scale_mode.
+ *   out           bf16 [rows, 16*Hkv, 128], last dim contiguous.
+ *   stream        hipStream_t (NULL = default stream).
+ *
+ * Asynchronous on `stream`; no host synchronisation; graph-capturable once
+ * the scratch is reserved (pa_reserve).  Returns PA_OK or a pa_status.
+ * Device-side preconditions (not checked on the host): cu_seqlens_q
+ * monotone with the stated ends, context_len >= q_len, sparse lists free of
+ * duplicates, finite scales.  Violations give unspecified output values but
+ * no out-of-bounds access.
+ */
+int pa_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+              const pa_tensor* k_scale, const pa_tensor* v_scale,
+              const pa_tensor* block_table, const pa_tensor* context_lens,
+              const pa_tensor* cu_seqlens_q, const pa_tensor* sparse_page_idx,
+              int scale_mode, pa_tensor* out, void* stream);
+
+/* pa_decode with options (softmax scale, ragged max q_len hint, forced
+ * split-K partitions, timing events).  Same kernels as pa_decode. */
+int pa_decode_ex(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                 const pa_tensor* k_scale, const pa_tensor* v_scale,
+                 const pa_tensor* block_table, const pa_tensor* context_lens,
+                 const pa_tensor* cu_seqlens_q, const pa_tensor* sparse_page_idx,
+                 int scale_mode, pa_tensor* out, const pa_decode_opts* opts, void* stream);
+
+/*
+ * kv_quant_write -- the single cache writer ([ATOM-2710] review "Smaller":
+ * one shared writer; [ATOM-2614] "Problem": page-shuffled FP8 plus
+ * per-token K/V scales).
+ *
+ *   k_new, v_new  f32 or bf16 [T, Hkv, 128], last dim contiguous.
+ *   slot_mapping  int64 [T]: page*128 + token slot; negative => skip the
+ *                 token; a slot past the cache is skipped too.
+ *   k_cache, v_cache  as in pa_decode (written at the named slots only).
+ *   k_scale, v_scale  PER_TOKEN: outputs, f32 [num_blocks, Hkv, 128], scale =
+ *                 fl32(amax/448) of the token's 128 values (an all-zero row
+ *                 stores 0).  SCALAR: inputs, one f32 each, > 0.  NONE: unused.
+ *   Codes: y = fl32(x / scale) (IEEE division; x itself when the scale is 0
+ *   or in NONE mode), then e4m3fn round-to-nearest-even with saturation to
+ *   +-448; NaN gives 0x7F with the input's sign.
+ * Slots must be distinct within one call.  Asynchronous on `stream`.
+ */
+int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new,
+                   const pa_tensor* slot_mapping, pa_tensor* k_cache, pa_tensor* v_cache,
+                   pa_tensor* k_scale, pa_tensor* v_scale, int scale_mode, void* stream);
+
+/* pa_query_support -- can this configuration be served?  Call at startup
+ * to refuse a configuration before serving it ([ATOM-2710] review "Should
+ * fix" 2).  PA_OK or the error pa_decode would return. */
+int pa_query_support(const pa_config* cfg);
+
+/* pa_plan_describe -- host-only dry run: the plan and scratch bucket a
+ * configuration maps to.  Plans depend only on the capacity buckets, so the
+ * set of distinct plans and scratch sizes is bounded ([ATOM-2710] review
+ * "Must fix" 1). */
+int pa_plan_describe(const pa_config* cfg, pa_plan_info* info);
+
+/* pa_reserve -- allocate, now, the split-K scratch that `cfg` (and every
+ * smaller bucket) needs on the current device for calls on `stream`, so
+ * later calls (including ones under graph capture) never allocate.  Scratch
+ * is per (device, stream): calls on one stream are serialised by the
+ * stream; calls on different streams use different scratch.  A captured
+ * graph keeps the scratch it was captured with; do not replay two copies of
+ * one graph concurrently. */
+int pa_reserve(const pa_config* cfg, void* stream);
+
+/* pa_release -- free all scratch (synchronises the device first). */
+int pa_release(void);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8PA_H */

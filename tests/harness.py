@@ -1,0 +1,163 @@
+"""Test-side plumbing: put a workload on the GPU through the library's own
+writer, build the oracle's side of the same workload, and compare.
+
+The GPU side and the oracle side start from the same seeded inputs
+(``workloads``); nothing the oracle uses comes from the GPU.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+import fp8_paged_kv_pa_amd as pa
+import workloads as wl
+from oracle import attention as oatt
+from oracle import layout as olay
+from oracle import writer as owr
+
+POISON_SCALE = 1e3
+
+
+def poison_arrays(w, nb=None):
+    """Initial cache contents: random finite e4m3 codes and scales of 1e3,
+    so a read of anything the call should not touch shows in the output."""
+    nb = w.num_blocks if nb is None else nb
+    rng = np.random.default_rng(w.seed + 99)
+    kc = rng.integers(0, 0x7F, size=nb * w.Hkv * 16384, dtype=np.uint8)
+    vc = rng.integers(0, 0x7F, size=nb * w.Hkv * 16384, dtype=np.uint8)
+    ks = np.full(nb * w.Hkv * 128, POISON_SCALE, dtype=np.float32)
+    return kc, vc, ks, ks.copy()
+
+
+class GpuCase:
+    """A workload resident on the GPU, its cache written by kv_quant_write."""
+
+    def __init__(self, w, device="cuda:0", kv_dtype=torch.uint8, in_dtype=torch.float32,
+                 poison=True):
+        self.w = w
+        self.dev = torch.device(device)
+        nb, Hkv = w.num_blocks, w.Hkv
+        if poison:
+            kc, vc, ks, vs = poison_arrays(w)
+            self.kc = torch.from_numpy(kc).to(self.dev).view(nb, Hkv, 16384)
+            self.vc = torch.from_numpy(vc).to(self.dev).view(nb, Hkv, 16384)
+            self.ks = torch.from_numpy(ks).to(self.dev).view(nb, Hkv, 128)
+            self.vs = torch.from_numpy(vs).to(self.dev).view(nb, Hkv, 128)
+        else:
+            self.kc = torch.zeros(nb, Hkv, 16384, dtype=torch.uint8, device=self.dev)
+            self.vc = torch.zeros_like(self.kc)
+            self.ks = torch.full((nb, Hkv, 128), POISON_SCALE, device=self.dev)
+            self.vs = torch.full((nb, Hkv, 128), POISON_SCALE, device=self.dev)
+        if kv_dtype == torch.float8_e4m3fn:
+            self.kc = self.kc.view(torch.float8_e4m3fn)
+            self.vc = self.vc.view(torch.float8_e4m3fn)
+        self.mode = w.mode
+        if w.mode == wl.SCALAR:
+            self.ks_arg = torch.tensor([w.k_scalar], dtype=torch.float32, device=self.dev)
+            self.vs_arg = torch.tensor([w.v_scalar], dtype=torch.float32, device=self.dev)
+        elif w.mode == wl.NONE:
+            self.ks_arg = self.vs_arg = None
+        else:
+            self.ks_arg, self.vs_arg = self.ks, self.vs
+        self.in_dtype = in_dtype
+        for b in range(w.B):
+            self.write_request(b)
+        self.q = torch.from_numpy(w.q).to(self.dev).to(torch.bfloat16)
+        self.bt = torch.from_numpy(w.block_table).to(self.dev)
+        self.ctx = torch.from_numpy(w.ctx).to(self.dev)
+        self.cu = None if w.cu is None else torch.from_numpy(w.cu).to(self.dev)
+        self.sp = None if w.sparse is None else torch.from_numpy(w.sparse).to(self.dev)
+        self.out = torch.empty(w.rows, w.Hq, 128, dtype=torch.bfloat16, device=self.dev)
+
+    def write_request(self, b, chunk_pages=256):
+        pages = self.w.written[b]
+        for i in range(0, len(pages), chunk_pages):
+            k, v, s = self.w.request_kv(b, pages[i:i + chunk_pages])
+            kt = torch.from_numpy(k).to(self.dev).to(self.in_dtype)
+            vt = torch.from_numpy(v).to(self.dev).to(self.in_dtype)
+            st = torch.from_numpy(s).to(self.dev)
+            pa.kv_quant_write(kt, vt, st, self.kc, self.vc, self.ks_arg, self.vs_arg, self.mode)
+
+    def decode(self, out=None, **kw):
+        out = self.out if out is None else out
+        if kw:
+            pa.pa_decode_ex(self.q, self.kc, self.vc, self.ks_arg, self.vs_arg, self.bt, self.ctx,
+                            self.cu, self.sp, self.mode, out, **kw)
+        else:
+            pa.pa_decode(self.q, self.kc, self.vc, self.ks_arg, self.vs_arg, self.bt, self.ctx,
+                         self.cu, self.sp, self.mode, out)
+        return out
+
+
+def oracle_cache(w):
+    """The oracle's cache for a (small) workload: poison, then every written
+    page through the reference writer."""
+    kc, vc, ks, vs = poison_arrays(w)
+    ks_in = np.array([w.k_scalar], np.float32)
+    vs_in = np.array([w.v_scalar], np.float32)
+    for b in range(w.B):
+        k, v, s = w.request_kv(b)
+        if w.mode == wl.SCALAR:
+            owr.quant_write_ref(k, v, s, kc, vc, ks_in, vs_in, w.mode, w.Hkv)
+        else:
+            owr.quant_write_ref(k, v, s, kc, vc, ks, vs, w.mode, w.Hkv)
+    if w.mode == wl.SCALAR:
+        return kc, vc, ks, vs, ks_in, vs_in
+    if w.mode == wl.NONE:
+        return kc, vc, ks, vs, None, None
+    return kc, vc, ks, vs, ks, vs
+
+
+def oracle_out(w, cache=None, rows_subset=None, sm_scale=None):
+    cache = oracle_cache(w) if cache is None else cache
+    kc, vc, _, _, ksa, vsa = cache
+    return oatt.attention_ref(w.q, kc, vc, ksa, vsa, w.block_table, w.ctx, w.cu, w.sparse, w.mode,
+                              w.Hkv, sm_scale=sm_scale, rows_subset=rows_subset)
+
+
+def compact_request_oracle(w, b, rows):
+    """Oracle output for some rows of request b of a large workload, built on
+    a compact cache that holds only request b's written pages."""
+    pages = [int(n) for n in w.written[b]]
+    nb = len(pages)
+    Hkv = w.Hkv
+    kc = np.zeros(nb * Hkv * 16384, np.uint8)
+    vc = np.zeros_like(kc)
+    ks = np.zeros(nb * Hkv * 128, np.float32)
+    vs = np.zeros_like(ks)
+    ks_in = np.array([w.k_scalar], np.float32)
+    vs_in = np.array([w.v_scalar], np.float32)
+    bt = np.full((1, w.W), -1, np.int64)
+    for ci, n in enumerate(pages):
+        bt[0, n] = ci
+        k, v = w.page_kv(b, n)
+        slots = ci * 128 + np.arange(k.shape[0], dtype=np.int64)
+        if w.mode == wl.SCALAR:
+            owr.quant_write_ref(k, v, slots, kc, vc, ks_in, vs_in, w.mode, Hkv)
+        else:
+            owr.quant_write_ref(k, v, slots, kc, vc, ks, vs, w.mode, Hkv)
+    start = int(w.row_start[b])
+    L = int(w.q_lens[b])
+    q = w.q[start:start + L]
+    cu = None if w.cu is None else np.array([0, L])
+    sp = None if w.sparse is None else w.sparse[start:start + L]
+    ksa, vsa = (ks_in, vs_in) if w.mode == wl.SCALAR else ((None, None) if w.mode == wl.NONE else (ks, vs))
+    sel = [r - start for r in rows]
+    return oatt.attention_ref(q, kc, vc, ksa, vsa, bt, w.ctx[b:b + 1], cu, sp, w.mode, Hkv,
+                              rows_subset=sel)
+
+
+def compare(gpu_bf16, ref64, atol=1e-2, cos_min=0.9999, what=""):
+    g = gpu_bf16.float().cpu().numpy().astype(np.float64) if torch.is_tensor(gpu_bf16) else gpu_bf16
+    r = np.asarray(ref64, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
+    err = np.abs(g - r)
+    maxerr = float(err.max()) if err.size else 0.0
+    num = float(np.sum(g * r))
+    den = math.sqrt(float(np.sum(g * g)) * float(np.sum(r * r)))
+    cos = num / den if den > 0 else (1.0 if float(np.abs(g).max(initial=0)) == 0 else 0.0)
+    assert maxerr <= atol, f"{what}: max|err| {maxerr:.3e} > {atol} (max|ref| {np.abs(r).max():.3e})"
+    assert cos >= cos_min, f"{what}: cosine {cos:.7f} < {cos_min}"
+    return maxerr, cos

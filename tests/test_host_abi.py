@@ -1,0 +1,168 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads and
+exports every entry point include/fp8pa.h declares; configuration checks,
+capacity buckets and refusals happen on the host before any launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import fp8_paged_kv_pa_amd as pa
+from fp8_paged_kv_pa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8pa.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pa.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_struct_sizes_match_header_layout():
+    # pa_tensor: ptr + 2 x int32 + 12 x int64
+    assert ctypes.sizeof(_lib.PaTensor) == 8 + 8 + 6 * 8 * 2
+    assert ctypes.sizeof(_lib.PaConfig) == 6 * 4 + 4 * 8 + 4 * 4
+    assert ctypes.sizeof(_lib.PaDecodeOpts) == 4 + 4 + 4 + 4 + 8 + 8
+
+
+def cfg(**kw):
+    base = dict(num_kv_heads=1, rows=4, batch=4, max_pages=72)
+    base.update(kw)
+    return pa.make_config(**base)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("group_size", 8, -5), ("head_dim", 64, -5), ("page_size", 16, -5),
+    ("num_kv_heads", 0, -5), ("kv_dtype", 3, -2), ("scale_mode", 7, -1),
+])
+def test_geometry_refused_up_front(field, value, status):
+    c = cfg()
+    setattr(c, field, value)
+    assert pa.pa_query_support(c) == status
+    assert pa.pa_last_error()
+
+
+def test_non_divisible_rows_without_cu_is_refused():
+    # 121 rows over 31 requests: only a ragged (cu_seqlens_q) call may take it
+    assert pa.pa_query_support(cfg(rows=121, batch=31)) == -3
+    assert "cu_seqlens_q" in pa.pa_last_error()
+    assert pa.pa_query_support(cfg(rows=121, batch=31, ragged=True)) == 0
+    # [4,4,6,2]: divisible by 4, but with cu it is planned as ragged (max q_len unknown -> rows)
+    p = pa.pa_plan_describe(cfg(rows=16, batch=4, ragged=True))
+    assert p["rows_per_group"] == 4 and p["groups"] == 4
+    p = pa.pa_plan_describe(cfg(rows=16, batch=4, ragged=True, max_q_len=6))
+    assert p["rows_per_group"] == 4 and p["groups"] == 2
+
+
+def test_capacity_refusals():
+    assert pa.pa_query_support(cfg(rows=65537, batch=1)) == -6
+    assert pa.pa_query_support(cfg(rows=65536, batch=65536, max_pages=1)) == 0
+    assert pa.pa_query_support(cfg(topk=5000, rows=4)) == -6
+    assert pa.pa_query_support(cfg(max_pages=(1 << 20) + 1)) == -6
+
+
+def test_plans_and_scratch_depend_only_on_buckets():
+    """Every row count inside one power-of-two bucket maps to the same
+    partition count and scratch size; the set of scratch sizes is bounded by
+    the number of buckets (not by the number of distinct row counts)."""
+    sizes = set()
+    for rows in range(1, 4097):
+        p = pa.pa_plan_describe(cfg(rows=rows, batch=rows, max_pages=1024))
+        bucket = 1 << (rows - 1).bit_length()
+        assert p["rows_bucket"] == bucket
+        sizes.add(p["scratch_bytes"])
+    assert len(sizes) <= 13
+    a = pa.pa_plan_describe(cfg(rows=33, batch=33, max_pages=1024))
+    b = pa.pa_plan_describe(cfg(rows=64, batch=64, max_pages=1024))
+    assert a["scratch_bytes"] == b["scratch_bytes"] and a["parts"] == b["parts"]
+
+
+def test_plan_shapes_for_the_workloads():
+    c2 = pa.pa_plan_describe(cfg(rows=4, batch=4, max_pages=72))
+    assert c2["merge"] == 1 and c2["pages_per_part"] >= 1 and c2["units"] == 4
+    c3 = pa.pa_plan_describe(cfg(rows=32, batch=32, max_pages=1024))
+    assert c3["parts"] * c3["pages_per_part"] >= 1024 and c3["grid_x"] == 32 * c3["parts"]
+    c5 = pa.pa_plan_describe(cfg(rows=16, batch=16, max_pages=1024, topk=32))
+    assert c5["units"] == 16 and c5["parts"] * c5["pages_per_part"] >= 32
+    one = pa.pa_plan_describe(cfg(rows=4, batch=4, max_pages=72, force_parts=1))
+    assert one["merge"] == 0 and one["scratch_bytes"] == 0
+
+
+def _host_tensor(shape, dtype):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _decode_args(**over):
+    t = dict(
+        q=_host_tensor((4, 16, 128), torch.bfloat16),
+        k=_host_tensor((8, 1, 16384), torch.uint8),
+        v=_host_tensor((8, 1, 16384), torch.uint8),
+        ks=_host_tensor((8, 1, 128), torch.float32),
+        vs=_host_tensor((8, 1, 128), torch.float32),
+        bt=_host_tensor((4, 2), torch.int32),
+        ctx=_host_tensor((4,), torch.int32),
+        cu=None, sp=None,
+        out=_host_tensor((4, 16, 128), torch.bfloat16),
+        mode=2,
+    )
+    t.update(over)
+    return t
+
+
+def _call_decode(t):
+    lib = pa.load()
+    d = [_lib.desc(t[k]) for k in ("q", "k", "v", "ks", "vs", "bt", "ctx", "cu", "sp")]
+    do = _lib.desc(t["out"])
+    return lib.pa_decode(*[_lib.ref(x) for x in d], t["mode"], _lib.ref(do), None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=_host_tensor((4, 16, 128), torch.float32)), -2),
+    (dict(q=_host_tensor((4, 16, 64), torch.bfloat16)), -5),
+    (dict(q=_host_tensor((4, 32, 128), torch.bfloat16)), -5),
+    (dict(k=_host_tensor((8, 1, 8192), torch.uint8)), -3),
+    (dict(v=_host_tensor((8, 1, 16384), torch.float32)), -2),
+    (dict(ks=_host_tensor((8, 1, 64), torch.float32)), -3),
+    (dict(ks=_host_tensor((8, 1, 128), torch.float32), mode=1), -3),
+    (dict(bt=_host_tensor((4, 2), torch.int64)), -2),
+    (dict(ctx=_host_tensor((3,), torch.int32)), -3),
+    (dict(cu=_host_tensor((4,), torch.int32)), -3),
+    (dict(sp=_host_tensor((3, 4), torch.int32)), -3),
+    (dict(out=_host_tensor((4, 16, 128), torch.float32)), -3),
+    (dict(q=_host_tensor((6, 16, 128), torch.bfloat16), out=_host_tensor((6, 16, 128), torch.bfloat16)), -3),
+    (dict(q=_host_tensor((4, 16, 130), torch.bfloat16)[:, :, :128]), -4),
+    (dict(mode=5), -1),
+])
+def test_decode_refuses_bad_descriptors_before_launch(over, status):
+    assert _call_decode(_decode_args(**over)) == status
+    assert pa.pa_last_error()
+
+
+def test_write_refuses_bad_descriptors_before_launch():
+    lib = pa.load()
+    k = _host_tensor((3, 1, 128), torch.float32)
+    slots = _host_tensor((3,), torch.int32)  # wrong dtype: must be int64
+    kc = _host_tensor((2, 1, 16384), torch.uint8)
+    ks = _host_tensor((2, 1, 128), torch.float32)
+    d = [_lib.desc(x) for x in (k, k, slots, kc, kc, ks, ks)]
+    assert lib.kv_quant_write(*[_lib.ref(x) for x in d], 2, None) == -3
+    k2 = _host_tensor((3, 2, 128), torch.float32)
+    d = [_lib.desc(x) for x in (k2, k2, _host_tensor((3,), torch.int64), kc, kc, ks, ks)]
+    assert lib.kv_quant_write(*[_lib.ref(x) for x in d], 2, None) == -3
+    assert "KV heads" in pa.pa_last_error()

@@ -22,8 +22,9 @@
 // Computing S transposed leaves each lane with one head and 8 tokens, which
 // is exactly the B-operand of the P*V product: no transpose of P.  The
 // e4m3 -> bf16 conversion is exact; the per-token K scale multiplies each
-// score column once and the per-token V scale multiplies P before the
-// bf16 rounding, so no scale touches a 128-wide vector.
+// score column once and the per-token V scale multiplies P, so no scale
+// touches a 128-wide vector.  P' enters the P*V product as a bf16 hi + lo
+// pair (two MFMAs), so its rounding stays near 2^-16 instead of bf16's 2^-9.
 // Online softmax in the exp2 domain; the running max is only raised when a
 // chunk exceeds it by more than 2^8, so P stays <= 256 and the rescale of
 // the accumulators is rare.  The four waves' partials merge through LDS at
@@ -275,7 +276,12 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 ? 2 : 1)) void pa_decode_m
         ps += p[e];
       }
       l_run[r] += ps;
-      bf16x8 pop;
+      // P' = p * v_scale as an unevaluated bf16 pair hi + lo: hi keeps the
+      // top 8 significant bits (truncation), lo = P' - hi is exact in fp32
+      // and rounds to bf16, so the pair carries ~16 bits -- the PV product
+      // then adds no rounding beyond fp32 accumulation order.
+      uint32_t hb[8];
+      float lo[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float pv = p[e];
@@ -284,11 +290,21 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 ? 2 : 1)) void pa_decode_m
           const int t = t0 + 16 * (e >> 2) + 4 * g + (e & 3);
           pv = t < lim_r ? pv : 0.0f;
         }
-        pop[e] = (__bf16)pv;
+        hb[e] = __float_as_uint(pv) & 0xFFFF0000u;
+        lo[e] = pv - __uint_as_float(hb[e]);
       }
+      u32x4 hw;
 #pragma unroll
-      for (int d = 0; d < 8; ++d)
-        acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[d], pop, acc[r][d], 0, 0, 0);
+      for (int e = 0; e < 4; ++e) hw[e] = __builtin_amdgcn_perm(hb[2 * e + 1], hb[2 * e], 0x07060302u);
+      const bf16x8 phi = __builtin_bit_cast(bf16x8, hw);
+      bf16x8 plo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) plo[e] = (__bf16)lo[e];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[d], phi, acc[r][d], 0, 0, 0);
+        acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[d], plo, acc[r][d], 0, 0, 0);
+      }
     }
   };
 

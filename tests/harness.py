@@ -155,9 +155,14 @@ def compare(gpu_bf16, ref64, atol=1e-2, cos_min=0.9999, what=""):
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
     err = np.abs(g - r)
     maxerr = float(err.max()) if err.size else 0.0
+    # bf16 output: for |out| >= 4 half an ulp alone exceeds 1e-2, so there
+    # the bound is relative (2^-7 |ref|); below |out| = 1.28 it is 1e-2.
+    tol = np.maximum(atol, 2.0 ** -7 * np.abs(r))
+    worst = float((err / tol).max()) if err.size else 0.0
     num = float(np.sum(g * r))
     den = math.sqrt(float(np.sum(g * g)) * float(np.sum(r * r)))
     cos = num / den if den > 0 else (1.0 if float(np.abs(g).max(initial=0)) == 0 else 0.0)
-    assert maxerr <= atol, f"{what}: max|err| {maxerr:.3e} > {atol} (max|ref| {np.abs(r).max():.3e})"
+    assert worst <= 1.0, (f"{what}: max|err| {maxerr:.3e} exceeds max({atol}, 2^-7|ref|) "
+                          f"(max|ref| {np.abs(r).max():.3e}, worst err/tol {worst:.3f})")
     assert cos >= cos_min, f"{what}: cosine {cos:.7f} < {cos_min}"
     return maxerr, cos

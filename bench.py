@@ -1,0 +1,397 @@
+"""Decode-attention benchmark on one MI355X.
+
+A step is one pass of the hot path over one batch: kv_quant_write of the
+step's new tokens (the last q_len tokens of every request), then pa_decode
+(main kernel, plus the log-sum-exp merge when the plan splits the context).
+The default workload is the 8K serving shape: batch 4, q_len 1, one KV head x
+16 query heads, head_dim 128, 128-token pages, contexts uniform in
+[8192, 9216], per-token e4m3 scales, random block table over a 4096-page
+pool.  Its cache is replicated over 64 layers (64 distinct pools) and steps
+rotate through them, as consecutive attention layers of one model would, so
+every step reads its KV from HBM rather than from the 256 MB Infinity Cache.
+
+Timing: W untimed warmup steps, then exactly K steps replayed from captured
+HIP graphs, bracketed by torch.cuda.synchronize().  The main decode kernel's
+own duration is measured with HIP events recorded around it on the launch
+stream.  Prints one JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fp8_paged_kv_pa_amd as pa  # noqa: E402
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+
+CONFIGS = {
+    "c1": lambda: wl.c1_tiny(),
+    "c2": lambda: wl.c2_dense_8k(),
+    "c3": lambda: wl.c3_dense_128k(wl.PER_TOKEN),
+    "c3s": lambda: wl.c3_dense_128k(wl.SCALAR),
+    "c4": lambda: wl.c4_spec("uniform"),
+    "c4r": lambda: wl.c4_spec("ragged"),
+    "c4m": lambda: wl.c4_spec("mixed"),
+    "c5": lambda: wl.c5_sparse(False),
+    "c5t": lambda: wl.c5_sparse(True),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Layers:
+    """The workload's cache replicated over `n` layers in one allocation;
+    layer l's block table points at pool pages [l*NB, (l+1)*NB)."""
+
+    def __init__(self, w, n, dev):
+        self.w, self.n, self.dev = w, n, dev
+        NB, Hkv = w.num_blocks, w.Hkv
+        tot = NB * n
+        self.kc = torch.empty(tot, Hkv, 16384, dtype=torch.uint8, device=dev)
+        self.vc = torch.empty_like(self.kc)
+        self.ks = torch.empty(tot, Hkv, 128, dtype=torch.float32, device=dev)
+        self.vs = torch.empty_like(self.ks)
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed)
+        # unwritten slots hold random finite codes and large scales
+        self.kc[:NB].random_(0, 0x7F, generator=g)
+        self.vc[:NB].random_(0, 0x7F, generator=g)
+        self.ks[:NB].fill_(1e3)
+        self.vs[:NB].fill_(1e3)
+        self.mode = w.mode
+        if w.mode == wl.SCALAR:
+            self.ks_arg = torch.tensor([w.k_scalar], dtype=torch.float32, device=dev)
+            self.vs_arg = torch.tensor([w.v_scalar], dtype=torch.float32, device=dev)
+        elif w.mode == wl.NONE:
+            self.ks_arg = self.vs_arg = None
+        else:
+            self.ks_arg, self.vs_arg = self.ks, self.vs
+        t0 = time.time()
+        for b in range(w.B):
+            pages = w.written[b]
+            for i in range(0, len(pages), 256):
+                k, v, s = w.request_kv(b, pages[i:i + 256])
+                pa.kv_quant_write(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
+                                  torch.from_numpy(s).to(dev), self.kc, self.vc, self.ks_arg,
+                                  self.vs_arg, self.mode)
+        torch.cuda.synchronize()
+        for l in range(1, n):
+            self.kc[l * NB:(l + 1) * NB].copy_(self.kc[:NB])
+            self.vc[l * NB:(l + 1) * NB].copy_(self.vc[:NB])
+            self.ks[l * NB:(l + 1) * NB].copy_(self.ks[:NB])
+            self.vs[l * NB:(l + 1) * NB].copy_(self.vs[:NB])
+        torch.cuda.synchronize()
+        log(f"cache for {w.name} x {n} layers written in {time.time() - t0:.1f}s")
+        bt = torch.from_numpy(w.block_table).to(dev)
+        self.bt = [torch.where(bt >= 0, bt + l * NB, bt).contiguous() for l in range(n)]
+        self.ctx = torch.from_numpy(w.ctx).to(dev)
+        self.cu = None if w.cu is None else torch.from_numpy(w.cu).to(dev)
+        self.sp = None if w.sparse is None else torch.from_numpy(w.sparse).to(dev)
+        q = torch.from_numpy(w.q).to(dev).to(torch.bfloat16)
+        self.q = [q.clone() for _ in range(n)]
+        self.out = [torch.empty(w.rows, w.Hq, 128, dtype=torch.bfloat16, device=dev) for _ in range(n)]
+        k, v, s = w.step_tokens()
+        self.step_k = torch.from_numpy(k).to(dev)
+        self.step_v = torch.from_numpy(v).to(dev)
+        self.step_slots = [torch.from_numpy(s + np.int64(l * NB * 128)).to(dev) for l in range(n)]
+        self.max_q_len = int(w.q_lens.max())
+
+    force_parts = 0
+
+    def step(self, l, ev=None):
+        pa.kv_quant_write(self.step_k, self.step_v, self.step_slots[l], self.kc, self.vc,
+                          self.ks_arg, self.vs_arg, self.mode)
+        pa.pa_decode_ex(self.q[l], self.kc, self.vc, self.ks_arg, self.vs_arg, self.bt[l], self.ctx,
+                        self.cu, self.sp, self.mode, self.out[l],
+                        max_q_len=self.max_q_len if self.cu is not None else 0,
+                        force_parts=self.force_parts,
+                        main_begin_event=None if ev is None else ev[0],
+                        main_end_event=None if ev is None else ev[1])
+
+
+def algorithmic_bytes(w):
+    """Bytes one decode call must move: attended KV (codes + per-token
+    scales), q, out, the block-table entries and per-request metadata."""
+    kv = w.kv_bytes_attended()
+    qo = 2 * w.rows * w.Hq * 128 * 2
+    pages = sum(int(math.ceil(min(int(c), w.W * 128) / 128)) for c in w.ctx) if w.sparse is None \
+        else w.sparse.size
+    meta = 4 * pages + 4 * w.B + (0 if w.cu is None else 4 * (w.B + 1)) + \
+        (0 if w.sparse is None else 4 * w.sparse.size)
+    return kv, kv + qo + meta
+
+
+def hbm_probe(dev, gib=4):
+    """Best streaming-read rate (GB/s) of a plain 16-byte-per-lane read
+    kernel over a 4 GiB buffer, for a few grid sizes."""
+    import ctypes
+    path = os.path.join(ROOT, "fp8_paged_kv_pa_amd", "libhbmprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_void_p]
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    best = 0.0
+    stream = torch.cuda.current_stream()
+    for blocks in (256, 512, 1024, 2048, 4096):
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+        for rep in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = lib.hbm_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream.cuda_stream)
+            e1.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                return None
+            if rep:
+                best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return round(best, 1)
+
+
+def cpu_baseline(w, layers, budget_s=12.0):
+    """The oracle, as it stands, on one core: the same step -- write the
+    step's new tokens of a request, then attend that request's rows over its
+    cache -- for requests of the workload, repeated until about `budget_s`
+    seconds of CPU work.  The oracle's cache for a request is prepared
+    untimed (it is state, as the GPU cache is).  The GPU's layer-0 output for
+    the same rows is checked against the oracle's."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from harness import compare
+    from oracle import attention as oatt
+    from oracle import writer as owr
+
+    lim = threadpool_limits(1) if threadpool_limits else None
+    try:
+        out0 = layers.out[0].float().cpu().numpy()
+        sk, sv, _ = w.step_tokens()
+        done_bytes, t_used, n, check = 0, 0.0, 0, None
+        while (t_used < budget_s and n < 64) or n < min(w.B, 2):
+            b = n % w.B
+            start, L = int(w.row_start[b]), int(w.q_lens[b])
+            rows = list(range(start, start + L))
+            # untimed: the oracle's compact cache of request b
+            pages = [int(x) for x in w.written[b]]
+            nb = len(pages) + 1
+            kc = np.zeros(nb * w.Hkv * 16384, np.uint8)
+            vc = np.zeros_like(kc)
+            ks = np.zeros(nb * w.Hkv * 128, np.float32)
+            vs = np.zeros_like(ks)
+            sc_k = np.array([w.k_scalar], np.float32)
+            sc_v = np.array([w.v_scalar], np.float32)
+            ka, va = (sc_k, sc_v) if w.mode == wl.SCALAR else ((ks, vs) if w.mode == wl.PER_TOKEN else (None, None))
+            bt = np.full((1, w.W), -1, np.int64)
+            for ci, pg in enumerate(pages):
+                bt[0, pg] = ci
+                k, v = w.page_kv(b, pg)
+                owr.quant_write_ref(k, v, ci * 128 + np.arange(k.shape[0], dtype=np.int64), kc, vc,
+                                    ka, va, w.mode, w.Hkv)
+            new_slots = np.array([bt[0, (int(w.ctx[b]) - L + i) // 128] * 128 + (int(w.ctx[b]) - L + i) % 128
+                                  for i in range(L)], dtype=np.int64)
+            sp = None if w.sparse is None else w.sparse[start:start + L]
+            cu = None if w.cu is None else np.array([0, L])
+            # timed: the step on the CPU
+            t0 = time.time()
+            owr.quant_write_ref(sk[start:start + L], sv[start:start + L], new_slots, kc, vc, ka, va,
+                                w.mode, w.Hkv)
+            ref = oatt.attention_ref(w.q[start:start + L], kc, vc, ka, va, bt, w.ctx[b:b + 1], cu, sp,
+                                     w.mode, w.Hkv)
+            t_used += time.time() - t0
+            if n < w.B:
+                err, cos = compare(out0[rows], ref, what=f"bench check request {b}")
+                check = (err, cos) if check is None else (max(err, check[0]), min(cos, check[1]))
+            if w.sparse is None:
+                toks = min(int(w.ctx[b]), w.W * 128)
+            else:
+                sel = {int(x) for r in rows for x in w.sparse[r] if 0 <= x < w.W}
+                toks = sum(min(128, int(w.ctx[b]) - 128 * x) for x in sel)
+            done_bytes += toks * w.Hkv * (256 + (8 if w.mode == wl.PER_TOKEN else 0))
+            n += 1
+    finally:
+        if lim is not None:
+            lim.__exit__(None, None, None)
+    return {
+        "value": round(done_bytes / t_used / 1e9, 5),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{n} request-steps of {w.name} (write the request's new tokens, dequantize its "
+                  f"attended pages, fp64 softmax attention for its rows), one host thread, "
+                  f"{t_used:.1f} s timed",
+        "check_max_abs_err": None if check is None else round(check[0], 6),
+        "check_min_cos": None if check is None else round(check[1], 8),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3200)
+    ap.add_argument("--warmup", type=int, default=128)
+    ap.add_argument("--config", default="c2", choices=sorted(CONFIGS))
+    ap.add_argument("--layers", type=int, default=0, help="distinct cache copies to rotate (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--force-parts", type=int, default=0, help="split-K partitions (0: the plan's choice)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB copy kernel (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
+              f"multi-GPU path; the decode kernel's per-GPU share is what one GPU shows).", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = CONFIGS[args.config]()
+    kv_bytes, alg_bytes = algorithmic_bytes(w)
+    n_layers = args.layers or max(1, min(64, int(math.ceil(1.0e9 / max(kv_bytes, 1)))))
+    layers = Layers(w, n_layers, dev)
+
+    stream = torch.cuda.Stream()
+    cfg = pa.make_config(w.Hkv, w.rows, w.B, w.W, topk=0 if w.sparse is None else w.sparse.shape[1],
+                         ragged=w.cu is not None, max_q_len=int(w.q_lens.max()) if w.cu is not None else 0,
+                         scale_mode=w.mode, force_parts=args.force_parts)
+    layers.force_parts = args.force_parts
+    plan = pa.pa_plan_describe(cfg)
+    pa.pa_reserve(cfg, stream)
+
+    K, W = args.steps, args.warmup
+    G = min(n_layers, max(1, K))
+    with torch.cuda.stream(stream):
+        for i in range(max(W, n_layers)):   # warm up eagerly (also first-touch)
+            layers.step(i % n_layers)
+    torch.cuda.synchronize()
+
+    # one graph per G consecutive steps (layers 0..G-1)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for l in range(G):
+            layers.step(l)
+    tail = K % G
+    tail_graph = None
+    if tail:
+        tail_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(tail_graph, stream=stream):
+            for l in range(tail):
+                layers.step(l)
+    torch.cuda.synchronize()
+    for _ in range(max(1, W // G)):
+        graph.replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps --------------------------------
+    reps = K // G
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    if tail_graph is not None:
+        tail_graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    # ---- live duration of the main decode kernel --------------------------
+    # Eager steps queued behind a spin kernel, so the stream runs them back to
+    # back; the library records a HIP event pair around every main-kernel
+    # launch on the launch stream.
+    n_ev = min(max(K, 1), max(4 * n_layers, 32), 512)
+    evs2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n_ev)]
+    with torch.cuda.stream(stream):
+        for a, b in evs2:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2e8))
+        for i, ev in enumerate(evs2):
+            layers.step(i % n_layers, ev)
+    torch.cuda.synchronize()
+    main_ms = [a.elapsed_time(b) for a, b in evs2]
+    timing = (f"HIP events recorded around each main-kernel launch on the launch stream, {n_ev} "
+              f"steps queued behind a spin kernel")
+    main_avg_ms = float(np.mean(main_ms))
+    achieved = alg_bytes / (main_avg_ms * 1e-3) / 1e9
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    tokens_per_s = w.attended_tokens() * w.Hkv / (ms_per_step * 1e-3)
+
+    if args.calib_copy:
+        x = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            torch.mul(x, 1.0, out=y)
+        torch.cuda.synchronize()
+
+    probe = hbm_probe(dev)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, layers)
+
+    res = {
+        "metric": "decode attention KV GB/s & % HBM roofline (attended tokens/s), 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-kv/bf16-mfma/f32-acc",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.B, "q_len": int(w.q_lens.max()), "rows": w.rows, "kv_heads": w.Hkv,
+            "q_heads_per_kv": 16, "head_dim": 128, "page": 128,
+            "context": [int(w.ctx.min()), int(w.ctx.max())],
+            "scale_mode": ["none", "scalar", "per_token"][w.mode],
+            "sparse_topk": 0 if w.sparse is None else int(w.sparse.shape[1]),
+            "layers_rotated": n_layers,
+            "kv_bytes_per_step": int(kv_bytes),
+            "plan": {k: int(v) for k, v in plan.items() if k in ("parts", "pages_per_part", "grid_x",
+                                                                  "rows_per_group", "merge")},
+        },
+        "attended_tokens_per_s": round(tokens_per_s, 1),
+        "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_decode_main",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(main_avg_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(alg_bytes),
+            "timing": timing,
+            "hbm_read_probe_gbs": probe,
+            "frac_of_probe": None if not probe else round(achieved / probe, 4),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp8pa.so")
+PROBE_LIB = os.path.join(HERE, "libhbmprobe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["pa_decode.hip", "kv_write.hip", "api.cpp", "plan.cpp"]
@@ -47,8 +48,15 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # the bench's HBM read probe: a separate library, not part of the C ABI
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC] + COMMON + ["-shared", os.path.join(CSRC, "probe", "hbm_probe.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building the HBM probe failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

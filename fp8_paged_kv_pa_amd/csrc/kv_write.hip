@@ -62,14 +62,14 @@ __global__ __launch_bounds__(kWave * kWriteWaves) void kv_write_kernel(WriteArgs
   if (pair >= a.tokens * a.hkv) return;  // whole wave exits together
   const int64_t t = pair / a.hkv;
   const int h = int(pair - t * a.hkv);
+  // inputs and slot in one round trip: the value loads do not depend on the slot
+  float k0, k1, v0, v1;
+  load_pair(a.k_new, t * a.k_tok_stride + h * a.k_head_stride + 2 * lane, a.in_bf16, &k0, &k1);
+  load_pair(a.v_new, t * a.v_tok_stride + h * a.v_head_stride + 2 * lane, a.in_bf16, &v0, &v1);
   const int64_t slot = a.slots[t];
   if (slot < 0 || slot >= a.num_blocks * 128) return;
   const int64_t page = slot >> 7;
   const int o = int(slot & 127);
-
-  float k0, k1, v0, v1;
-  load_pair(a.k_new, t * a.k_tok_stride + h * a.k_head_stride + 2 * lane, a.in_bf16, &k0, &k1);
-  load_pair(a.v_new, t * a.v_tok_stride + h * a.v_head_stride + 2 * lane, a.in_bf16, &v0, &v1);
 
   float ks, vs;
   const uint32_t kc = quantize_pair(k0, k1, a.scale_mode, a.k_scale, &ks);

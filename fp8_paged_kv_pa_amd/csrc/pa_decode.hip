@@ -29,6 +29,8 @@
 // chunk exceeds it by more than 2^8, so P stays <= 256 and the rescale of
 // the accumulators is rare.  The four waves' partials merge through LDS at
 // the end; with one partition the workgroup writes bf16 output directly.
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -99,10 +101,16 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 ? 2 : 1)) void pa_decode_m
   const int64_t unit = blockIdx.x / uint32_t(a.parts);
 
   // ---- which rows, which request, which tokens -------------------------
+  // The loads that decide the partition's work (context length, row range,
+  // the partition's first block-table entry) are issued together, before
+  // any branch, so they cost one memory round trip.
+  const int n0 = part * a.ppp;  // < width (dense) or < topk (sparse) by construction of the grid
   int h, b, row0, nrows, lim0;  // row row0+i sees tokens t < lim0 + i
+  int first_entry;              // dense: block_table[b][n0]; sparse: sparse_idx[row0][n0]
   if constexpr (SPARSE) {
     h = int(unit % a.hkv);
     row0 = int(unit / a.hkv);
+    first_entry = a.sparse_idx[int64_t(row0) * a.sp_stride + n0];
     int start, L;
     if (a.cu_seqlens_q) {
       b = find_request(a.cu_seqlens_q, a.batch, row0);
@@ -119,6 +127,8 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 ? 2 : 1)) void pa_decode_m
     const int64_t bh = unit / a.groups;
     h = int(bh % a.hkv);
     b = int(bh / a.hkv);
+    first_entry = a.block_table[int64_t(b) * a.bt_stride + n0];
+    const int ctx = a.context_lens[b];
     int start, L;
     if (a.cu_seqlens_q) {
       request_rows(a, b, &start, &L);
@@ -130,20 +140,29 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 ? 2 : 1)) void pa_decode_m
     if (i0 >= L) return;  // this request has no rows in this group
     nrows = min(RT, L - i0);
     row0 = start + i0;
-    lim0 = a.context_lens[b] - L + i0 + 1;
+    lim0 = ctx - L + i0 + 1;
   }
   const int cap = a.width * 128;
   const int lim_min = max(0, min(lim0, cap));
   const int lim_max = max(0, min(lim0 + nrows - 1, cap));
 
-  int n0 = part * a.ppp, n1;
+  int n1;
   if constexpr (SPARSE) {
     n1 = min(n0 + a.ppp, a.topk);
   } else {
     const int npages = (lim_max + 127) >> 7;
     n1 = min(n0 + a.ppp, npages);
   }
-  if (n0 >= n1 && a.parts > 1) return;  // nothing here; the merge skips this partition
+  if (n0 >= n1 && a.parts > 1) {
+    // nothing to attend in this partition: leave an empty partial (weight 0)
+    // so the merge can read every partition without knowing the context
+    if (threadIdx.x < 16 * nrows) {
+      const int r = threadIdx.x >> 4;
+      const int64_t pi = (int64_t(part) * a.rows + row0 + r) * Hq + 16 * h + (threadIdx.x & 15);
+      *reinterpret_cast<float2*>(a.part_ml + 2 * pi) = float2{-INFINITY, 0.0f};
+    }
+    return;
+  }
 
   // ---- query operands: B of S^T = K Q^T, lane = (head hr, dims 8g..8g+7 of each 32) ----
   bf16x8 qop[RT][4];
@@ -182,10 +201,10 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 ? 2 : 1)) void pa_decode_m
   auto page_at = [&](int n, int* tbase) -> int64_t {
     int ln = n;
     if constexpr (SPARSE) {
-      ln = a.sparse_idx[int64_t(row0) * a.sp_stride + n];
+      ln = n == n0 ? first_entry : a.sparse_idx[int64_t(row0) * a.sp_stride + n];
       if (ln < 0 || ln >= a.width || ln * 128 >= lim_max) return -1;
     }
-    const int P = a.block_table[int64_t(b) * a.bt_stride + ln];
+    const int P = (!SPARSE && n == n0) ? first_entry : a.block_table[int64_t(b) * a.bt_stride + ln];
     if (P < 0 || P >= a.num_blocks) return -1;
     *tbase = ln * 128;
     return int64_t(P) * a.hkv + h;
@@ -405,73 +424,106 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 ? 2 : 1)) void pa_decode_m
   }
 }
 
-// One wavefront per (row, query head): combine the partitions' (m, l, acc)
-// with log-sum-exp weights and write bf16.  Lane owns dims 2*lane, 2*lane+1.
+// One workgroup per (row, query head): combine the partitions' (m, l, acc)
+// with log-sum-exp weights and write bf16.  Wave w takes partitions
+// w, w+4, ...; lane owns dims 2*lane, 2*lane+1.  Every load of a batch of
+// partitions is issued before any weight is needed, so the kernel costs
+// about one memory round trip per 64 partitions.
+constexpr int kMergeBatch = 16;  // partitions per wave per batch (64 per workgroup)
+
 __global__ __launch_bounds__(256) void pa_merge(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int Hq = 16 * a.hkv;
-  const int64_t pair = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (pair >= int64_t(a.rows) * Hq) return;
+  const int64_t pair = blockIdx.x;
   const int row = int(pair / Hq);
   const int qh = int(pair - int64_t(row) * Hq);
 
-  int P = a.parts;
-  if (a.sparse_idx == nullptr) {
-    int b, start, L;
-    if (a.cu_seqlens_q) {
-      b = find_request(a.cu_seqlens_q, a.batch, row);
-      request_rows(a, b, &start, &L);
-    } else {
-      L = a.uniform_q_len;
-      b = row / L;
-      start = b * L;
-    }
-    const int i = row - start;
-    const int gi = i / a.rt;
-    const int i_last = min(L, (gi + 1) * a.rt) - 1;
-    const int lim = max(0, min(a.context_lens[b] - L + i_last + 1, a.width * 128));
-    const int npages = (lim + 127) >> 7;
-    P = min((npages + a.ppp - 1) / a.ppp, a.parts);
-  }
+  // Every launched partition left a partial; empty ones have m = -inf and
+  // weight 0 (their accumulators are never read into the sum).
+  const int P = a.parts;
 
-  float M = -INFINITY;
-  for (int p0 = 0; p0 < P; p0 += 64) {
-    const int p = p0 + lane;
-    const float m = p < P ? a.part_ml[2 * ((int64_t(p) * a.rows + row) * Hq + qh)] : -INFINITY;
-    M = fmaxf(M, wave_max(m));
-  }
+  __shared__ float sm_w[256];
+  __shared__ float sm_red[2][4];
+  __shared__ float2 sm_acc[4][64];
+  const int64_t stride_p = int64_t(a.rows) * Hq;  // between partitions
+  const int64_t base = int64_t(row) * Hq + qh;
+
   float ox = 0.0f, oy = 0.0f, Ls = 0.0f;
-  if (M != -INFINITY) {
-    for (int p0 = 0; p0 < P; p0 += 64) {
-      const int p = p0 + lane;
-      float w = 0.0f, lw = 0.0f;
-      if (p < P) {
-        const int64_t pi = (int64_t(p) * a.rows + row) * Hq + qh;
-        w = __builtin_amdgcn_exp2f(a.part_ml[2 * pi] - M);
-        lw = w * a.part_ml[2 * pi + 1];
-      }
-      Ls += wave_sum(lw);
-      const int cnt = min(64, P - p0);
-      for (int k = 0; k < cnt; ++k) {
-        const float wk = __shfl(w, k, kWave);
-        const int64_t pi = (int64_t(p0 + k) * a.rows + row) * Hq + qh;
-        const float2 v = *reinterpret_cast<const float2*>(a.part_acc + pi * 128 + 2 * lane);
-        ox += wk * v.x;
-        oy += wk * v.y;
-      }
+  for (int p0 = 0; p0 < P; p0 += 4 * kMergeBatch) {
+    const int cnt = min(4 * kMergeBatch, P - p0);
+    // accumulators of this wave's partitions in the batch (independent loads)
+    float2 v[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int pj = 4 * j + wave;
+      v[j] = pj < cnt ? *reinterpret_cast<const float2*>(a.part_acc + ((p0 + pj) * stride_p + base) * 128 +
+                                                          2 * lane)
+                      : float2{0.f, 0.f};
     }
+    // (m, l) of the batch: thread t < cnt holds partition p0 + t
+    const int t = threadIdx.x;
+    float m = -INFINITY, l = 0.0f;
+    if (t < cnt) {
+      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * ((p0 + t) * stride_p + base));
+      m = ml.x;
+      l = ml.y;
+    }
+    float wm = wave_max(m);
+    if (lane == 0) sm_red[0][wave] = wm;
+    __syncthreads();
+    const float Mb = fmaxf(fmaxf(sm_red[0][0], sm_red[0][1]), fmaxf(sm_red[0][2], sm_red[0][3]));
+    // running combination across batches (only one batch unless P > 64)
+    float M = Mb;
+    float scale_old = 1.0f;
+    if (p0 > 0) {
+      M = fmaxf(Mb, sm_red[1][0]);
+      scale_old = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sm_red[1][0] - M);
+    }
+    const float wgt = (M == -INFINITY || t >= cnt) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    sm_w[t] = wgt;
+    const float lw = wave_sum(wgt * l);
+    __syncthreads();
+    if (lane == 0) sm_red[0][wave] = lw;
+    __syncthreads();
+    Ls = Ls * scale_old + (sm_red[0][0] + sm_red[0][1] + sm_red[0][2] + sm_red[0][3]);
+    ox *= scale_old;
+    oy *= scale_old;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const float wj = sm_w[4 * j + wave];
+      ox += wj != 0.0f ? wj * v[j].x : 0.0f;
+      oy += wj != 0.0f ? wj * v[j].y : 0.0f;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) sm_red[1][0] = M;
+    __syncthreads();
   }
-  float v_fold = 1.0f;
-  if (a.scale_mode != PA_SCALE_PER_TOKEN && a.v_scale) v_fold = *a.v_scale;
-  const float inv = Ls > 0.0f ? v_fold / Ls : 0.0f;
-  const uint32_t packed = uint32_t(f32_to_bf16_rne(ox * inv)) | (uint32_t(f32_to_bf16_rne(oy * inv)) << 16);
-  *reinterpret_cast<uint32_t*>(a.out + int64_t(row) * a.out_row_stride + int64_t(qh) * a.out_head_stride +
-                               2 * lane) = packed;
+  sm_acc[wave][lane] = float2{ox, oy};
+  __syncthreads();
+  if (wave == 0) {
+    float2 s0 = sm_acc[0][lane], s1 = sm_acc[1][lane], s2 = sm_acc[2][lane], s3 = sm_acc[3][lane];
+    const float sx = (s0.x + s1.x) + (s2.x + s3.x);
+    const float sy = (s0.y + s1.y) + (s2.y + s3.y);
+    float v_fold = 1.0f;
+    if (a.scale_mode != PA_SCALE_PER_TOKEN && a.v_scale) v_fold = *a.v_scale;
+    const float inv = Ls > 0.0f ? v_fold / Ls : 0.0f;
+    const uint32_t packed =
+        uint32_t(f32_to_bf16_rne(sx * inv)) | (uint32_t(f32_to_bf16_rne(sy * inv)) << 16);
+    *reinterpret_cast<uint32_t*>(a.out + int64_t(row) * a.out_row_stride +
+                                 int64_t(qh) * a.out_head_stride + 2 * lane) = packed;
+  }
 }
 
+// With events, the dispatch itself records them (start and end of this
+// kernel), so the measured time is the kernel's own, without marker packets.
 template <int RT, bool PT, bool SP>
-void launch_main_t(const DecodeArgs& a, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((pa_decode_main<RT, PT, SP>), dim3(uint32_t(grid)), dim3(kWave * kWaves), 0, s, a);
+void launch_main_t(const DecodeArgs& a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (e0 || e1)
+    hipExtLaunchKernelGGL((pa_decode_main<RT, PT, SP>), dim3(uint32_t(grid)), dim3(kWave * kWaves), 0, s,
+                          e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL((pa_decode_main<RT, PT, SP>), dim3(uint32_t(grid)), dim3(kWave * kWaves), 0, s, a);
 }
 
 }  // namespace
@@ -480,34 +532,26 @@ hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool spa
                          hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   const bool pt = a.scale_mode == PA_SCALE_PER_TOKEN;
-  hipError_t e;
-  if (ev_begin) {
-    e = hipEventRecord(ev_begin, stream);
-    if (e != hipSuccess) return e;
-  }
+  hipEvent_t e0 = ev_begin, e1 = ev_end;
   // the one variant-selection table: (rows per group, per-token scales, sparse)
   if (sparse) {
-    if (pt) launch_main_t<1, true, true>(a, grid, stream);
-    else launch_main_t<1, false, true>(a, grid, stream);
+    if (pt) launch_main_t<1, true, true>(a, grid, stream, e0, e1);
+    else launch_main_t<1, false, true>(a, grid, stream, e0, e1);
   } else if (a.rt == 1) {
-    if (pt) launch_main_t<1, true, false>(a, grid, stream);
-    else launch_main_t<1, false, false>(a, grid, stream);
+    if (pt) launch_main_t<1, true, false>(a, grid, stream, e0, e1);
+    else launch_main_t<1, false, false>(a, grid, stream, e0, e1);
   } else if (a.rt == 2) {
-    if (pt) launch_main_t<2, true, false>(a, grid, stream);
-    else launch_main_t<2, false, false>(a, grid, stream);
+    if (pt) launch_main_t<2, true, false>(a, grid, stream, e0, e1);
+    else launch_main_t<2, false, false>(a, grid, stream, e0, e1);
   } else {
-    if (pt) launch_main_t<4, true, false>(a, grid, stream);
-    else launch_main_t<4, false, false>(a, grid, stream);
+    if (pt) launch_main_t<4, true, false>(a, grid, stream, e0, e1);
+    else launch_main_t<4, false, false>(a, grid, stream, e0, e1);
   }
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ev_end) {
-    e = hipEventRecord(ev_end, stream);
-    if (e != hipSuccess) return e;
-  }
   if (merge) {
     const int64_t pairs = int64_t(a.rows) * 16 * a.hkv;
-    hipLaunchKernelGGL(pa_merge, dim3(uint32_t((pairs + 3) / 4)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(pa_merge, dim3(uint32_t(pairs)), dim3(256), 0, stream, a);
     e = hipGetLastError();
   }
   return e;

@@ -32,8 +32,11 @@ constexpr int32_t kMaxKvHeads = 64;
 constexpr int32_t kMaxParts = 256;
 constexpr int64_t kMaxScratchBytes = int64_t(4) << 30;
 
-// Workgroups the plan aims for: enough to cover 256 CUs several times.
-constexpr int64_t kTargetWorkgroups = 2048;
+// Workgroups the plan aims for: about one per CU (256 CUs).  Measured on
+// the 128K and 8K decode shapes, one long-running 4-wave workgroup per CU
+// streams better than several short ones, and fewer partitions mean less
+// split-K scratch and a cheaper merge.
+constexpr int64_t kTargetWorkgroups = 256;
 
 struct Plan {
   int rt = 1;              // query rows per workgroup (1, 2 or 4)

@@ -109,6 +109,7 @@ class Layers:
         self.max_q_len = int(w.q_lens.max())
 
     force_parts = 0
+    prefetch_depth = 0
 
     def step(self, l, ev=None):
         pa.kv_quant_write(self.step_k, self.step_v, self.step_slots[l], self.kc, self.vc,
@@ -116,7 +117,7 @@ class Layers:
         pa.pa_decode_ex(self.q[l], self.kc, self.vc, self.ks_arg, self.vs_arg, self.bt[l], self.ctx,
                         self.cu, self.sp, self.mode, self.out[l],
                         max_q_len=self.max_q_len if self.cu is not None else 0,
-                        force_parts=self.force_parts,
+                        force_parts=self.force_parts, prefetch_depth=self.prefetch_depth,
                         main_begin_event=None if ev is None else ev[0],
                         main_end_event=None if ev is None else ev[1])
 
@@ -252,6 +253,7 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="distinct cache copies to rotate (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--force-parts", type=int, default=0, help="split-K partitions (0: the plan's choice)")
+    ap.add_argument("--prefetch-depth", type=int, default=0, help="pages in flight per wave (0: the plan's)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -274,6 +276,7 @@ def main():
                          ragged=w.cu is not None, max_q_len=int(w.q_lens.max()) if w.cu is not None else 0,
                          scale_mode=w.mode, force_parts=args.force_parts)
     layers.force_parts = args.force_parts
+    layers.prefetch_depth = args.prefetch_depth
     plan = pa.pa_plan_describe(cfg)
     pa.pa_reserve(cfg, stream)
 

@@ -11,7 +11,7 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libfp8pa.so")
+LIB_PATH = os.environ.get("FP8PA_LIB") or os.path.join(HERE, "libfp8pa.so")
 
 MAX_DIMS = 6
 
@@ -51,6 +51,8 @@ class PaDecodeOpts(ctypes.Structure):
         ("force_parts", ctypes.c_int32),
         ("main_begin_event", ctypes.c_void_p),
         ("main_end_event", ctypes.c_void_p),
+        ("prefetch_depth", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

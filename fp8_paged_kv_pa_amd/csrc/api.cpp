@@ -162,6 +162,7 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   if ((rc = check_cache(vc, "v_cache", &nb2, &hkv2))) return rc;
   if (nb2 != nb || hkv2 != hkv) return fail(PA_ERR_SHAPE, "k_cache and v_cache shapes differ");
   if (kc->dtype != vc->dtype) return fail(PA_ERR_DTYPE, "k_cache and v_cache dtypes differ");
+  if (nb < 1) return fail(PA_ERR_SHAPE, "the KV cache must hold at least one page");
   if (hkv * kGroup != Hq)
     return fail(PA_ERR_UNSUPPORTED, "q has " + std::to_string(Hq) + " heads but the cache has " +
                                         std::to_string(hkv) + " KV heads: the group must be 16");
@@ -211,6 +212,8 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   cfg.ragged = ragged ? 1 : 0;
   cfg.max_q_len = opts ? opts->max_q_len : 0;
   cfg.force_parts = opts ? opts->force_parts : 0;
+  if (opts && (opts->prefetch_depth < 0 || opts->prefetch_depth > 4))
+    return fail(PA_ERR_INVALID_ARG, "prefetch_depth must be in [0, 4]");
   Plan plan;
   std::string perr;
   if ((rc = make_plan(cfg, &plan, &perr))) return fail(rc, perr);
@@ -259,7 +262,8 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
 
   hipEvent_t e0 = opts ? reinterpret_cast<hipEvent_t>(opts->main_begin_event) : nullptr;
   hipEvent_t e1 = opts ? reinterpret_cast<hipEvent_t>(opts->main_end_event) : nullptr;
-  hipError_t he = launch_decode(a, plan.grid, plan.merge, plan.sparse, e0, e1, stream);
+  const int depth = (opts && opts->prefetch_depth > 0) ? opts->prefetch_depth : plan.depth;
+  hipError_t he = launch_decode(a, plan.grid, plan.merge, plan.sparse, depth, e0, e1, stream);
   if (he != hipSuccess) return fail(PA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(he));
   return PA_OK;
 }

@@ -41,6 +41,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr float kLazyMax = 8.0f;  // log2 headroom before the running max moves
 constexpr int kAccPad = 132;      // LDS row pitch (floats) for the wave merge
+constexpr int kNoTokens = 1 << 30;  // token base of a position with nothing to read
 
 struct Chunk {
   u32x4 k[4];
@@ -69,28 +70,51 @@ __device__ __forceinline__ void request_rows(const DecodeArgs& a, int b, int* st
   *L = e - s;
 }
 
+// An empty asm that reads every register of a chunk: forces the compiler to
+// complete the chunk's loads here (used on paths that skip the chunk).
 template <bool PER_TOKEN>
-__device__ __forceinline__ void load_chunk(Chunk& c, const DecodeArgs& a, int64_t blk, int wave,
-                                           int lane) {
-  const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + blk * 16384 + wave * 4096) + lane;
-  const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_cache + blk * 16384 + wave * 4096) + lane;
+__device__ __forceinline__ void consume_chunk(const Chunk& c) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) c.k[i] = kp[64 * i];
+  for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(c.k[i]), "v"(c.v[i]));
+  if constexpr (PER_TOKEN) asm volatile("" ::"v"(c.ks[0]), "v"(c.ks[1]), "v"(c.vs[0]), "v"(c.vs[1]));
+}
+
+// Loads one wave's 32-token chunk of (page, KV head) block `blk`.  When
+// `valid` is false every lane reads the same 16 bytes of block 0 instead:
+// the same number of load instructions is issued on every path (so the
+// compiler's wait counts stay exact across the prefetch ring) at almost no
+// memory traffic.
+template <bool PER_TOKEN>
+__device__ __forceinline__ void load_chunk(Chunk& c, const DecodeArgs& a, int64_t blk, bool valid,
+                                           int wave, int lane) {
+  const int64_t base = valid ? blk * 16384 + wave * 4096 + lane * 16 : 0;
+  const int istep = valid ? 64 : 0;
+  const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + base);
+  const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_cache + base);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) c.v[i] = vp[64 * i];
+  for (int i = 0; i < 4; ++i) c.k[i] = kp[istep * i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c.v[i] = vp[istep * i];
   if constexpr (PER_TOKEN) {
     const int g = lane >> 4;
-    const f32x4* ksp = reinterpret_cast<const f32x4*>(a.k_scale + blk * 128 + wave * 32);
-    const f32x4* vsp = reinterpret_cast<const f32x4*>(a.v_scale + blk * 128 + wave * 32);
-    c.ks[0] = ksp[g];
-    c.ks[1] = ksp[4 + g];
-    c.vs[0] = vsp[g];
-    c.vs[1] = vsp[4 + g];
+    const int64_t sbase = valid ? blk * 128 + wave * 32 + 4 * g : 0;
+    const int s4 = valid ? 16 : 0;
+    c.ks[0] = *reinterpret_cast<const f32x4*>(a.k_scale + sbase);
+    c.ks[1] = *reinterpret_cast<const f32x4*>(a.k_scale + sbase + s4);
+    c.vs[0] = *reinterpret_cast<const f32x4*>(a.v_scale + sbase);
+    c.vs[1] = *reinterpret_cast<const f32x4*>(a.v_scale + sbase + s4);
   }
 }
 
-template <int RT, bool PER_TOKEN, bool SPARSE>
-__global__ __launch_bounds__(kWave * kWaves, (RT <= 2 ? 2 : 1)) void pa_decode_main(DecodeArgs a) {
+// Read-only tables (block table, sparse lists) read through the constant
+// address space: uniform reads become scalar loads, counted apart from the
+// vector loads of the KV stream, so waiting for a table entry never waits
+// for KV bytes in flight.
+typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
+__device__ __forceinline__ const_i32_ptr as_const(const int32_t* p) { return (const_i32_ptr)(p); }
+
+template <int RT, bool PER_TOKEN, bool SPARSE, int NBUF>
+__global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) void pa_decode_main(DecodeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;   // lane group: tokens 4g..4g+3 of each 16-token tile
@@ -110,7 +134,7 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 ? 2 : 1)) void pa_decode_m
   if constexpr (SPARSE) {
     h = int(unit % a.hkv);
     row0 = int(unit / a.hkv);
-    first_entry = a.sparse_idx[int64_t(row0) * a.sp_stride + n0];
+    first_entry = as_const(a.sparse_idx + int64_t(row0) * a.sp_stride)[n0];
     int start, L;
     if (a.cu_seqlens_q) {
       b = find_request(a.cu_seqlens_q, a.batch, row0);
@@ -127,7 +151,7 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 ? 2 : 1)) void pa_decode_m
     const int64_t bh = unit / a.groups;
     h = int(bh % a.hkv);
     b = int(bh / a.hkv);
-    first_entry = a.block_table[int64_t(b) * a.bt_stride + n0];
+    first_entry = as_const(a.block_table + int64_t(b) * a.bt_stride)[n0];
     const int ctx = a.context_lens[b];
     int start, L;
     if (a.cu_seqlens_q) {
@@ -197,22 +221,34 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 ? 2 : 1)) void pa_decode_m
     for (int d = 0; d < 8; ++d) acc[r][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // physical page and first token of list position n; -1 if nothing to read
-  auto page_at = [&](int n, int* tbase) -> int64_t {
-    int ln = n;
-    if constexpr (SPARSE) {
-      ln = n == n0 ? first_entry : a.sparse_idx[int64_t(row0) * a.sp_stride + n];
-      if (ln < 0 || ln >= a.width || ln * 128 >= lim_max) return -1;
-    }
-    const int P = (!SPARSE && n == n0) ? first_entry : a.block_table[int64_t(b) * a.bt_stride + ln];
-    if (P < 0 || P >= a.num_blocks) return -1;
-    *tbase = ln * 128;
-    return int64_t(P) * a.hkv + h;
+  const_i32_ptr bt_c = as_const(a.block_table + int64_t(b) * a.bt_stride);
+  const_i32_ptr sp_c = nullptr;
+  if constexpr (SPARSE) sp_c = as_const(a.sparse_idx + int64_t(row0) * a.sp_stride);
+  // Table reads are split in two so that a scalar load is never waited for
+  // in the step that issues it: raw_at() issues the read of list position n
+  // (its physical page), valid_page() checks it one step later.
+  // logical page of list position n (sparse: the list entry; -1 past the end)
+  auto logical_at = [&](int n) -> int {
+    if constexpr (SPARSE) return n < n1 ? (n == n0 ? first_entry : sp_c[n]) : -1;
+    return n;
   };
-
+  auto logical_ok = [&](int n, int ln) -> bool {
+    return n < n1 && ln >= 0 && ln < a.width && ln * 128 < lim_max;
+  };
+  // raw physical page of logical page ln (read only if the position is usable)
+  auto raw_at = [&](int n, int ln) -> int {
+    if (!logical_ok(n, ln)) return -1;
+    return (!SPARSE && n == n0) ? first_entry : bt_c[ln];
+  };
+  auto valid_page = [&](int P) -> bool { return P >= 0 && P < a.num_blocks; };
   auto process = [&](Chunk& c, int tbase) {
     const int t0 = tbase + 32 * wave;
-    if (t0 >= lim_max) return;  // chunk past the context for every row (uniform)
+    if (t0 >= lim_max) {
+      // nothing of this chunk is attended: still consume its registers so the
+      // loads are complete on this path too
+      consume_chunk<PER_TOKEN>(c);
+      return;
+    }
     const bool full = t0 + 32 <= lim_min;
 
     // token of this lane's score slot e: t0 + 16*(e/4) + 4g + e%4
@@ -327,26 +363,41 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 ? 2 : 1)) void pa_decode_m
     }
   };
 
-  // ---- stream the partition's pages, next page's loads in flight --------
+  // ---- stream the partition's pages: a ring of NBUF chunk buffers, the
+  // loads of the next NBUF-1 pages in flight while one is processed.  Table
+  // entries are read one step ahead of their use. -------------------------
   if (n0 < n1) {
-    Chunk ca, cb;
-    int ta = 0, tb = 0;
-    int64_t pa = page_at(n0, &ta);
-    if (pa >= 0) load_chunk<PER_TOKEN>(ca, a, pa, wave, lane);
-    for (int n = n0; n < n1; n += 2) {
-      int64_t pb = -1;
-      if (n + 1 < n1) {
-        pb = page_at(n + 1, &tb);
-        if (pb >= 0) load_chunk<PER_TOKEN>(cb, a, pb, wave, lane);
+    Chunk buf[NBUF];
+    int tb[NBUF];
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k) {
+      const int ln = logical_at(n0 + k);
+      const int P = raw_at(n0 + k, ln);
+      const bool ok = valid_page(P);
+      tb[k] = ok ? ln * 128 : kNoTokens;
+      load_chunk<PER_TOKEN>(buf[k], a, int64_t(P) * a.hkv + h, ok, wave, lane);
+    }
+    // raw entry of the next position to load (n0 + NBUF - 1) and the
+    // logical page of the one after it
+    int ln_next = logical_at(n0 + NBUF - 1);
+    int P_next = raw_at(n0 + NBUF - 1, ln_next);
+    int ln_after = logical_at(n0 + NBUF);
+    for (int n = n0; n < n1; n += NBUF) {
+#pragma unroll
+      for (int k = 0; k < NBUF; ++k) {
+        const int nn = n + k;
+        if (nn >= n1) break;
+        const int ls = (k + NBUF - 1) % NBUF;  // slot of position nn + NBUF - 1 (held nn - 1)
+        const int nl = nn + NBUF - 1;
+        const bool ok = valid_page(P_next);
+        tb[ls] = ok ? ln_next * 128 : kNoTokens;
+        load_chunk<PER_TOKEN>(buf[ls], a, int64_t(P_next) * a.hkv + h, ok, wave, lane);
+        // table reads for the following steps (checked one step later)
+        ln_next = ln_after;
+        P_next = raw_at(nl + 1, ln_next);
+        ln_after = logical_at(nl + 2);
+        process(buf[k], tb[k]);
       }
-      if (pa >= 0) process(ca, ta);
-      if (n + 1 >= n1) break;
-      pa = -1;
-      if (n + 2 < n1) {
-        pa = page_at(n + 2, &ta);
-        if (pa >= 0) load_chunk<PER_TOKEN>(ca, a, pa, wave, lane);
-      }
-      if (pb >= 0) process(cb, tb);
     }
   }
 
@@ -517,35 +568,48 @@ __global__ __launch_bounds__(256) void pa_merge(DecodeArgs a) {
 
 // With events, the dispatch itself records them (start and end of this
 // kernel), so the measured time is the kernel's own, without marker packets.
-template <int RT, bool PT, bool SP>
+template <int RT, bool PT, bool SP, int NB>
 void launch_main_t(const DecodeArgs& a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (e0 || e1)
-    hipExtLaunchKernelGGL((pa_decode_main<RT, PT, SP>), dim3(uint32_t(grid)), dim3(kWave * kWaves), 0, s,
-                          e0, e1, 0, a);
+    hipExtLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB>), dim3(uint32_t(grid)), dim3(kWave * kWaves), 0,
+                          s, e0, e1, 0, a);
   else
-    hipLaunchKernelGGL((pa_decode_main<RT, PT, SP>), dim3(uint32_t(grid)), dim3(kWave * kWaves), 0, s, a);
+    hipLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB>), dim3(uint32_t(grid)), dim3(kWave * kWaves), 0, s,
+                       a);
+}
+
+template <int RT, bool PT, bool SP>
+void launch_depth(const DecodeArgs& a, int depth, int64_t grid, hipStream_t s, hipEvent_t e0,
+                  hipEvent_t e1) {
+  if constexpr (RT == 1 && !SP) {
+    if (depth == 3) return launch_main_t<RT, PT, SP, 3>(a, grid, s, e0, e1);
+    if (depth >= 4) return launch_main_t<RT, PT, SP, 4>(a, grid, s, e0, e1);
+  }
+  launch_main_t<RT, PT, SP, 2>(a, grid, s, e0, e1);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool sparse,
+hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool sparse, int depth,
                          hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   const bool pt = a.scale_mode == PA_SCALE_PER_TOKEN;
   hipEvent_t e0 = ev_begin, e1 = ev_end;
-  // the one variant-selection table: (rows per group, per-token scales, sparse)
+  // the one variant-selection table: (rows per group, per-token scales,
+  // sparse, prefetch depth)
+  const int d = depth;
   if (sparse) {
-    if (pt) launch_main_t<1, true, true>(a, grid, stream, e0, e1);
-    else launch_main_t<1, false, true>(a, grid, stream, e0, e1);
+    if (pt) launch_depth<1, true, true>(a, d, grid, stream, e0, e1);
+    else launch_depth<1, false, true>(a, d, grid, stream, e0, e1);
   } else if (a.rt == 1) {
-    if (pt) launch_main_t<1, true, false>(a, grid, stream, e0, e1);
-    else launch_main_t<1, false, false>(a, grid, stream, e0, e1);
+    if (pt) launch_depth<1, true, false>(a, d, grid, stream, e0, e1);
+    else launch_depth<1, false, false>(a, d, grid, stream, e0, e1);
   } else if (a.rt == 2) {
-    if (pt) launch_main_t<2, true, false>(a, grid, stream, e0, e1);
-    else launch_main_t<2, false, false>(a, grid, stream, e0, e1);
+    if (pt) launch_depth<2, true, false>(a, d, grid, stream, e0, e1);
+    else launch_depth<2, false, false>(a, d, grid, stream, e0, e1);
   } else {
-    if (pt) launch_main_t<4, true, false>(a, grid, stream, e0, e1);
-    else launch_main_t<4, false, false>(a, grid, stream, e0, e1);
+    if (pt) launch_depth<4, true, false>(a, d, grid, stream, e0, e1);
+    else launch_depth<4, false, false>(a, d, grid, stream, e0, e1);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

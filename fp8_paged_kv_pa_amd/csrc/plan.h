@@ -45,6 +45,7 @@ struct Plan {
   int parts_launched = 1;  // partitions that can hold work given the real width
   int ppp = 1;             // pages (dense) or list entries (sparse) per partition
   int lmax = 1;            // bound on q_len used by the plan
+  int depth = 2;           // pages of KV in flight per wave (chunk-buffer ring)
   bool sparse = false;
   bool merge = false;
   int64_t units = 0;       // dense: batch*Hkv*groups; sparse: rows*Hkv

@@ -118,8 +118,12 @@ typedef struct pa_decode_opts {
   int32_t max_q_len;       /* ragged only: caller-measured max rows per       */
                            /* request (0 => unknown, bounded by rows)         */
   int32_t force_parts;     /* 0 => plan chooses; else split-K partitions      */
-  void* main_begin_event;  /* hipEvent_t recorded on `stream` right before    */
-  void* main_end_event;    /* and right after the main kernel (may be NULL)   */
+  void* main_begin_event;  /* hipEvent_t pair recorded by the main kernel's   */
+  void* main_end_event;    /* dispatch (its start and end); may be NULL       */
+  int32_t prefetch_depth;  /* 0 => plan chooses; else 2..4 pages of KV in     */
+                           /* flight per wave (tuning; values other than 2    */
+                           /* apply to single-row dense calls)                */
+  int32_t reserved;
 } pa_decode_opts;
 
 /* Host-side description of a decode call, for capability queries, planning
@@ -165,7 +169,8 @@ typedef struct pa_plan_info {
  *   q             bf16 [rows, 16*Hkv, 128], last dim contiguous, 16-byte
  *                 aligned rows.
  *   k_cache,
- *   v_cache       u8/f8e4m3 [num_blocks, Hkv, 16384] contiguous (layout above).
+ *   v_cache       u8/f8e4m3 [num_blocks, Hkv, 16384] contiguous (layout
+ *                 above), num_blocks >= 1.
  *   k_scale,
  *   v_scale       see "scale" above, per scale_mode.
  *   block_table   int32 [batch, W]: physical page of each logical page.  Only

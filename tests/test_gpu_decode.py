@@ -130,3 +130,14 @@ def test_repeated_calls_are_deterministic():
     o2 = case.decode(out=torch.empty_like(case.out), force_parts=4).clone()
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("depth", [3, 4])
+@pytest.mark.parametrize("kw", [CASES[0], CASES[1], CASES[6], CASES[7]], ids=["201", "202", "207", "208"])
+def test_prefetch_depths_match_oracle(kw, depth):
+    w = wl.small_case(**kw)
+    case = GpuCase(w)
+    for parts in (0, 1, 3):
+        out = case.decode(out=torch.empty_like(case.out), force_parts=parts, prefetch_depth=depth)
+        torch.cuda.synchronize()
+        compare(out, oracle_out(w), what=f"{w.name} depth={depth} parts={parts}")

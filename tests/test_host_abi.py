@@ -38,7 +38,7 @@ def test_struct_sizes_match_header_layout():
     # pa_tensor: ptr + 2 x int32 + 12 x int64
     assert ctypes.sizeof(_lib.PaTensor) == 8 + 8 + 6 * 8 * 2
     assert ctypes.sizeof(_lib.PaConfig) == 6 * 4 + 4 * 8 + 4 * 4
-    assert ctypes.sizeof(_lib.PaDecodeOpts) == 4 + 4 + 4 + 4 + 8 + 8
+    assert ctypes.sizeof(_lib.PaDecodeOpts) == 4 + 4 + 4 + 4 + 8 + 8 + 4 + 4
 
 
 def cfg(**kw):

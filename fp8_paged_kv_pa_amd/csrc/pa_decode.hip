@@ -166,6 +166,39 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
     row0 = start + i0;
     lim0 = ctx - L + i0 + 1;
   }
+  // The partition's first chunk and the query operands do not depend on the
+  // context length: issue their loads now, so they travel together with the
+  // context-length read instead of after it (masking handles the rest).
+  Chunk buf[NBUF];
+  int tb[NBUF];
+  {
+    int ln0 = n0, P0 = first_entry;
+    if constexpr (SPARSE) {
+      ln0 = first_entry;
+      P0 = (ln0 >= 0 && ln0 < a.width) ? as_const(a.block_table + int64_t(b) * a.bt_stride)[ln0] : -1;
+    }
+    const bool ok0 = P0 >= 0 && P0 < a.num_blocks;
+    tb[0] = ok0 ? ln0 * 128 : kNoTokens;
+    load_chunk<PER_TOKEN>(buf[0], a, int64_t(P0) * a.hkv + h, ok0, wave, lane);
+  }
+  // query operands: B of S^T = K Q^T, lane = (head hr, dims 8g..8g+7 of
+  // each 32-dim k-step)
+  static_assert(RT == 1 || RT == 2, "a workgroup carries one or two query rows");
+  bf16x8 qop[RT][4];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (r < nrows) {
+        const uint16_t* qp = a.q + int64_t(row0 + r) * a.q_row_stride +
+                             int64_t(16 * h + hr) * a.q_head_stride + 32 * j + 8 * g;
+        qop[r][j] = *reinterpret_cast<const bf16x8*>(qp);
+      } else {
+        qop[r][j] = bf16x8{};
+      }
+    }
+  }
+
   const int cap = a.width * 128;
   const int lim_min = max(0, min(lim0, cap));
   const int lim_max = max(0, min(lim0 + nrows - 1, cap));
@@ -186,22 +219,6 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
       *reinterpret_cast<float2*>(a.part_ml + 2 * pi) = float2{-INFINITY, 0.0f};
     }
     return;
-  }
-
-  // ---- query operands: B of S^T = K Q^T, lane = (head hr, dims 8g..8g+7 of each 32) ----
-  bf16x8 qop[RT][4];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (r < nrows) {
-        const uint16_t* qp = a.q + int64_t(row0 + r) * a.q_row_stride +
-                             int64_t(16 * h + hr) * a.q_head_stride + 32 * j + 8 * g;
-        qop[r][j] = *reinterpret_cast<const bf16x8*>(qp);
-      } else {
-        qop[r][j] = bf16x8{};
-      }
-    }
   }
 
   float k_fold = a.sm_log2;  // scalar / none: the K scale folds into the score scale
@@ -266,40 +283,51 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
       }
     }
 
-    bf16x8 kop[2][4];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        kop[tau][j] = fp8x8_to_bf16x8(c.k[2 * tau + (j >> 1)][2 * (j & 1)],
-                                      c.k[2 * tau + (j >> 1)][2 * (j & 1) + 1]);
-
-    float kc[8];
+    // per-token factors of this lane's 8 tokens (slot e <-> token
+    // t0 + 16*(e/4) + 4g + e%4): K scale folded with sm*log2(e), V scale
+    float kc[8], vsf[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if constexpr (PER_TOKEN) kc[e] = c.ks[e >> 2][e & 3] * k_fold;
-      else kc[e] = k_fold;
+      if constexpr (PER_TOKEN) {
+        kc[e] = c.ks[e >> 2][e & 3] * k_fold;
+        vsf[e] = c.vs[e >> 2][e & 3];
+      } else {
+        kc[e] = k_fold;
+        vsf[e] = 1.0f;
+      }
     }
 
-    bf16x8 vop[8];
+    // S^T = K Q^T for every row tile, k-step outer so each converted K
+    // operand (exact e4m3 -> bf16) serves all row tiles
+    f32x4 st[RT][2];
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
-      vop[d] = fp8x8_to_bf16x8(c.v[d >> 1][2 * (d & 1)], c.v[d >> 1][2 * (d & 1) + 1]);
+    for (int r = 0; r < RT; ++r) st[r][0] = st[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 k0 = fp8x8_to_bf16x8(c.k[j >> 1][2 * (j & 1)], c.k[j >> 1][2 * (j & 1) + 1]);
+      const bf16x8 k1 = fp8x8_to_bf16x8(c.k[2 + (j >> 1)][2 * (j & 1)], c.k[2 + (j >> 1)][2 * (j & 1) + 1]);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        if (r >= nrows) break;
+        const bf16x8 qv = qop[r][j];
+        st[r][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qv, st[r][0], 0, 0, 0);
+        st[r][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qv, st[r][1], 0, 0, 0);
+      }
+    }
 
+    // online softmax per row tile; P' = p * v_scale as a bf16 hi + lo pair:
+    // hi keeps the top 8 significant bits (truncation), lo = P' - hi is exact
+    // in fp32 and rounds to bf16, so the pair carries ~16 bits -- the PV
+    // product then adds no rounding beyond fp32 accumulation order.
+    bf16x8 phi[RT], plo[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       if (r >= nrows) break;
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][j], qop[r][j], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][j], qop[r][j], s1, 0, 0, 0);
-      }
       float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[e] = s0[e] * kc[e];
-        x[4 + e] = s1[e] * kc[4 + e];
+        x[e] = st[r][0][e] * kc[e];
+        x[4 + e] = st[r][1][e] * kc[4 + e];
       }
       const int lim_r = min(lim0 + r, cap);
       if (!full) {
@@ -309,8 +337,8 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
           x[e] = t < lim_r ? x[e] : -INFINITY;
         }
       }
-      float lm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      const float lm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
       const bool need = lm > m_run[r] + kLazyMax;
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
         float gm = fmaxf(lm, __shfl_xor(lm, 16, kWave));
@@ -323,24 +351,14 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
         m_run[r] = mn;
       }
       const float mu = (m_run[r] == -INFINITY) ? 0.0f : m_run[r];
-      float p[8];
       float ps = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(x[e] - mu);
-        ps += p[e];
-      }
-      l_run[r] += ps;
-      // P' = p * v_scale as an unevaluated bf16 pair hi + lo: hi keeps the
-      // top 8 significant bits (truncation), lo = P' - hi is exact in fp32
-      // and rounds to bf16, so the pair carries ~16 bits -- the PV product
-      // then adds no rounding beyond fp32 accumulation order.
       uint32_t hb[8];
       float lo[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float pv = p[e];
-        if constexpr (PER_TOKEN) pv *= c.vs[e >> 2][e & 3];
+        const float p = __builtin_amdgcn_exp2f(x[e] - mu);
+        ps += p;
+        float pv = p * vsf[e];
         if (!full) {
           const int t = t0 + 16 * (e >> 2) + 4 * g + (e & 3);
           pv = t < lim_r ? pv : 0.0f;
@@ -348,17 +366,25 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
         hb[e] = __float_as_uint(pv) & 0xFFFF0000u;
         lo[e] = pv - __uint_as_float(hb[e]);
       }
+      l_run[r] += ps;
       u32x4 hw;
 #pragma unroll
       for (int e = 0; e < 4; ++e) hw[e] = __builtin_amdgcn_perm(hb[2 * e + 1], hb[2 * e], 0x07060302u);
-      const bf16x8 phi = __builtin_bit_cast(bf16x8, hw);
-      bf16x8 plo;
+      phi[r] = __builtin_bit_cast(bf16x8, hw);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) plo[e] = (__bf16)lo[e];
+      for (int e = 0; e < 8; ++e) plo[r][e] = (__bf16)lo[e];
+    }
+
+    // O^T += V^T P'^T, d-tile outer so each converted V operand serves all
+    // row tiles
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[d], phi, acc[r][d], 0, 0, 0);
-        acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[d], plo, acc[r][d], 0, 0, 0);
+    for (int d = 0; d < 8; ++d) {
+      const bf16x8 vop = fp8x8_to_bf16x8(c.v[d >> 1][2 * (d & 1)], c.v[d >> 1][2 * (d & 1) + 1]);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        if (r >= nrows) break;
+        acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi[r], acc[r][d], 0, 0, 0);
+        acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[r], acc[r][d], 0, 0, 0);
       }
     }
   };
@@ -367,10 +393,8 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
   // loads of the next NBUF-1 pages in flight while one is processed.  Table
   // entries are read one step ahead of their use. -------------------------
   if (n0 < n1) {
-    Chunk buf[NBUF];
-    int tb[NBUF];
 #pragma unroll
-    for (int k = 0; k < NBUF - 1; ++k) {
+    for (int k = 1; k < NBUF - 1; ++k) {
       const int ln = logical_at(n0 + k);
       const int P = raw_at(n0 + k, ln);
       const bool ok = valid_page(P);
@@ -604,12 +628,9 @@ hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool spa
   } else if (a.rt == 1) {
     if (pt) launch_depth<1, true, false>(a, d, grid, stream, e0, e1);
     else launch_depth<1, false, false>(a, d, grid, stream, e0, e1);
-  } else if (a.rt == 2) {
+  } else {
     if (pt) launch_depth<2, true, false>(a, d, grid, stream, e0, e1);
     else launch_depth<2, false, false>(a, d, grid, stream, e0, e1);
-  } else {
-    if (pt) launch_depth<4, true, false>(a, d, grid, stream, e0, e1);
-    else launch_depth<4, false, false>(a, d, grid, stream, e0, e1);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

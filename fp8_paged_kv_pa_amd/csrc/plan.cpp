@@ -74,7 +74,10 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
     }
     lmax = std::max<int64_t>(lmax, 1);
     p.lmax = int(lmax);
-    p.rt = lmax <= 1 ? 1 : (lmax <= 2 ? 2 : 4);
+    // one or two query rows per workgroup: with two, the accumulators,
+    // operands and a two-page prefetch ring fill the 256 VGPRs that let two
+    // workgroups share a CU; longer q_len runs as several row groups
+    p.rt = lmax <= 1 ? 1 : 2;
     p.groups = int(ceil_div(lmax, p.rt));
     p.units = c.batch * hkv * p.groups;
     npages = c.max_pages;

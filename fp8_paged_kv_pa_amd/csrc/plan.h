@@ -39,7 +39,7 @@ constexpr int64_t kMaxScratchBytes = int64_t(4) << 30;
 constexpr int64_t kTargetWorkgroups = 256;
 
 struct Plan {
-  int rt = 1;              // query rows per workgroup (1, 2 or 4)
+  int rt = 1;              // query rows per workgroup (1 or 2)
   int groups = 1;          // row groups per request (dense)
   int parts = 1;           // split-K partitions per unit (scratch is sized for this)
   int parts_launched = 1;  // partitions that can hold work given the real width

@@ -65,9 +65,11 @@ def test_non_divisible_rows_without_cu_is_refused():
     assert pa.pa_query_support(cfg(rows=121, batch=31, ragged=True)) == 0
     # [4,4,6,2]: divisible by 4, but with cu it is planned as ragged (max q_len unknown -> rows)
     p = pa.pa_plan_describe(cfg(rows=16, batch=4, ragged=True))
-    assert p["rows_per_group"] == 4 and p["groups"] == 4
+    assert p["rows_per_group"] == 2 and p["groups"] == 8
     p = pa.pa_plan_describe(cfg(rows=16, batch=4, ragged=True, max_q_len=6))
-    assert p["rows_per_group"] == 4 and p["groups"] == 2
+    assert p["rows_per_group"] == 2 and p["groups"] == 3
+    p = pa.pa_plan_describe(cfg(rows=16, batch=16))
+    assert p["rows_per_group"] == 1 and p["groups"] == 1
 
 
 def test_capacity_refusals():

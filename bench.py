@@ -134,6 +134,28 @@ def algorithmic_bytes(w):
     return kv, kv + qo + meta
 
 
+KERNEL_SOURCES = ("fp8_paged_kv_pa_amd/csrc/pa_decode.hip", "fp8_paged_kv_pa_amd/csrc/device_common.h",
+                  "fp8_paged_kv_pa_amd/csrc/launch.h")
+
+
+def recorded_traffic(workload):
+    """HBM bytes per main-kernel launch from the committed counter record
+    (profiles/pa_decode_main_traffic.json), or None when the record is for
+    other kernel sources or another workload."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "pa_decode_main_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec.get("source_sha256"):
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    return None if w is None else int(w["traffic_bytes_per_launch"])
+
+
 def hbm_probe(dev, gib=4):
     """Best streaming-read rate (GB/s) of a plain 16-byte-per-lane read
     kernel over a 4 GiB buffer, for a few grid sizes."""
@@ -384,7 +406,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(w.name),
             "avg_launch_us": round(main_avg_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": int(alg_bytes),
             "timing": timing,

@@ -156,9 +156,11 @@ def recorded_traffic(workload):
     return None if w is None else int(w["traffic_bytes_per_launch"])
 
 
-def hbm_probe(dev, gib=4):
+def hbm_probe(dev, gib=4, same_bytes=None):
     """Best streaming-read rate (GB/s) of a plain 16-byte-per-lane read
-    kernel over a 4 GiB buffer, for a few grid sizes."""
+    kernel over a 4 GiB buffer, for a few grid sizes; with `same_bytes`, also
+    the best rate for reads of that size (rotating through the buffer so
+    they come from HBM), the floor a kernel moving that many bytes meets."""
     import ctypes
     path = os.path.join(ROOT, "fp8_paged_kv_pa_amd", "libhbmprobe.so")
     if not os.path.exists(path):
@@ -183,9 +185,29 @@ def hbm_probe(dev, gib=4):
                 return None
             if rep:
                 best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    best_small = None
+    if same_bytes:
+        nb = (int(same_bytes) + 15) // 16 * 16
+        slots = max(1, nbytes // nb)
+        best_small = 0.0
+        for blocks in (256, 512, 1024):
+            sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(24)]
+            torch.cuda.synchronize()
+            torch.cuda._sleep(int(5e7))
+            for i, (e0, e1) in enumerate(evs):
+                e0.record()
+                lib.hbm_read_probe(buf.data_ptr() + (i % slots) * nb, nb, sink.data_ptr(), blocks,
+                                   stream.cuda_stream)
+                e1.record()
+            torch.cuda.synchronize()
+            ts = sorted(a.elapsed_time(b) for a, b in evs[4:])
+            best_small = max(best_small, nb / (ts[len(ts) // 2] * 1e-3) / 1e9)
+        best_small = round(best_small, 1)
     del buf
     torch.cuda.empty_cache()
-    return round(best, 1)
+    return round(best, 1), best_small
 
 
 def cpu_baseline(w, layers, budget_s=12.0):
@@ -208,20 +230,17 @@ def cpu_baseline(w, layers, budget_s=12.0):
     try:
         out0 = layers.out[0].float().cpu().numpy()
         sk, sv, _ = w.step_tokens()
-        done_bytes, t_used, n, check = 0, 0.0, 0, None
-        while (t_used < budget_s and n < 64) or n < min(w.B, 2):
-            b = n % w.B
-            start, L = int(w.row_start[b]), int(w.q_lens[b])
-            rows = list(range(start, start + L))
-            # untimed: the oracle's compact cache of request b
+        sc_k = np.array([w.k_scalar], np.float32)
+        sc_v = np.array([w.v_scalar], np.float32)
+
+        def request_state(b):
+            """untimed: the oracle's compact cache of request b (state, like the GPU cache)"""
             pages = [int(x) for x in w.written[b]]
             nb = len(pages) + 1
             kc = np.zeros(nb * w.Hkv * 16384, np.uint8)
             vc = np.zeros_like(kc)
             ks = np.zeros(nb * w.Hkv * 128, np.float32)
             vs = np.zeros_like(ks)
-            sc_k = np.array([w.k_scalar], np.float32)
-            sc_v = np.array([w.v_scalar], np.float32)
             ka, va = (sc_k, sc_v) if w.mode == wl.SCALAR else ((ks, vs) if w.mode == wl.PER_TOKEN else (None, None))
             bt = np.full((1, w.W), -1, np.int64)
             for ci, pg in enumerate(pages):
@@ -229,18 +248,30 @@ def cpu_baseline(w, layers, budget_s=12.0):
                 k, v = w.page_kv(b, pg)
                 owr.quant_write_ref(k, v, ci * 128 + np.arange(k.shape[0], dtype=np.int64), kc, vc,
                                     ka, va, w.mode, w.Hkv)
-            new_slots = np.array([bt[0, (int(w.ctx[b]) - L + i) // 128] * 128 + (int(w.ctx[b]) - L + i) % 128
-                                  for i in range(L)], dtype=np.int64)
+            start, L = int(w.row_start[b]), int(w.q_lens[b])
+            c = int(w.ctx[b])
+            new_slots = np.array([bt[0, (c - L + i) // 128] * 128 + (c - L + i) % 128 for i in range(L)],
+                                 dtype=np.int64)
+            return kc, vc, ka, va, bt, new_slots
+
+        reqs = list(range(min(w.B, 4)))
+        state = {b: request_state(b) for b in reqs}
+        done_bytes, t_used, n, check = 0, 0.0, 0, None
+        while (t_used < budget_s and n < 4096) or n < len(reqs):
+            b = reqs[n % len(reqs)]
+            kc, vc, ka, va, bt, new_slots = state[b]
+            start, L = int(w.row_start[b]), int(w.q_lens[b])
+            rows = list(range(start, start + L))
             sp = None if w.sparse is None else w.sparse[start:start + L]
             cu = None if w.cu is None else np.array([0, L])
-            # timed: the step on the CPU
+            # timed: the step on the CPU (write the new tokens, attend the rows)
             t0 = time.time()
             owr.quant_write_ref(sk[start:start + L], sv[start:start + L], new_slots, kc, vc, ka, va,
                                 w.mode, w.Hkv)
             ref = oatt.attention_ref(w.q[start:start + L], kc, vc, ka, va, bt, w.ctx[b:b + 1], cu, sp,
                                      w.mode, w.Hkv)
             t_used += time.time() - t0
-            if n < w.B:
+            if n < len(reqs):
                 err, cos = compare(out0[rows], ref, what=f"bench check request {b}")
                 check = (err, cos) if check is None else (max(err, check[0]), min(cos, check[1]))
             if w.sparse is None:
@@ -258,9 +289,9 @@ def cpu_baseline(w, layers, budget_s=12.0):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{n} request-steps of {w.name} (write the request's new tokens, dequantize its "
-                  f"attended pages, fp64 softmax attention for its rows), one host thread, "
-                  f"{t_used:.1f} s timed",
+        "sample": f"{n} request-steps over the first {len(reqs)} requests of {w.name} (write the "
+                  f"request's new tokens, dequantize its attended pages, fp64 softmax attention for its "
+                  f"rows), one host thread, {t_used:.1f} s timed",
         "check_max_abs_err": None if check is None else round(check[0], 6),
         "check_min_cos": None if check is None else round(check[1], 8),
     }
@@ -369,7 +400,7 @@ def main():
             torch.mul(x, 1.0, out=y)
         torch.cuda.synchronize()
 
-    probe = hbm_probe(dev)
+    probe, probe_same = hbm_probe(dev, same_bytes=alg_bytes) or (None, None)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, layers)
 
     res = {
@@ -412,6 +443,8 @@ def main():
             "timing": timing,
             "hbm_read_probe_gbs": probe,
             "frac_of_probe": None if not probe else round(achieved / probe, 4),
+            "hbm_read_probe_same_bytes_gbs": probe_same,
+            "frac_of_same_bytes_probe": None if not probe_same else round(achieved / probe_same, 4),
         },
         "cpu_baseline": cpu,
     }

@@ -605,7 +605,7 @@ void launch_main_t(const DecodeArgs& a, int64_t grid, hipStream_t s, hipEvent_t 
 template <int RT, bool PT, bool SP>
 void launch_depth(const DecodeArgs& a, int depth, int64_t grid, hipStream_t s, hipEvent_t e0,
                   hipEvent_t e1) {
-  if constexpr (RT == 1 && !SP) {
+  if constexpr (!SP) {
     if (depth == 3) return launch_main_t<RT, PT, SP, 3>(a, grid, s, e0, e1);
     if (depth >= 4) return launch_main_t<RT, PT, SP, 4>(a, grid, s, e0, e1);
   }

@@ -1,0 +1,146 @@
+// Host-only self-test of the planner (csrc/plan.cpp), built with
+// -fsanitize=address,undefined by tests/test_host_sanitized.py.  It walks
+// configuration space -- including every error path -- and checks the
+// invariants the launch code relies on: the grid covers every page exactly
+// once per unit, partitions never exceed the scratch they are sized for,
+// and scratch depends only on the capacity buckets.
+#include <cstdio>
+#include <algorithm>
+#include <cstdlib>
+#include <set>
+#include <string>
+
+#include "../../fp8_paged_kv_pa_amd/csrc/plan.h"
+
+using namespace fp8pa;
+
+static int failures = 0;
+#define CHECK(cond, ...)                                  \
+  do {                                                    \
+    if (!(cond)) {                                        \
+      ++failures;                                         \
+      std::fprintf(stderr, "FAIL %s:%d: %s | ", __FILE__, __LINE__, #cond); \
+      std::fprintf(stderr, __VA_ARGS__);                  \
+      std::fprintf(stderr, "\n");                         \
+    }                                                     \
+  } while (0)
+
+static pa_config base() {
+  pa_config c{};
+  c.num_kv_heads = 1;
+  c.group_size = 16;
+  c.head_dim = 128;
+  c.page_size = 128;
+  c.kv_dtype = PA_DTYPE_U8;
+  c.scale_mode = PA_SCALE_PER_TOKEN;
+  c.rows = 4;
+  c.batch = 4;
+  c.max_pages = 72;
+  return c;
+}
+
+int main() {
+  std::string err;
+  Plan p;
+  // error paths
+  {
+    pa_config c = base();
+    c.group_size = 8;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_UNSUPPORTED && !err.empty(), "group");
+    c = base(); c.head_dim = 64;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_UNSUPPORTED, "dim");
+    c = base(); c.page_size = 16;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_UNSUPPORTED, "page");
+    c = base(); c.kv_dtype = PA_DTYPE_BF16;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_DTYPE, "dtype");
+    c = base(); c.scale_mode = 9;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_INVALID_ARG, "mode");
+    c = base(); c.rows = 121; c.batch = 31;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_SHAPE, "121 rows uniform");
+    c.ragged = 1;
+    CHECK(make_plan(c, &p, &err) == PA_OK, "121 rows ragged");
+    c = base(); c.rows = kMaxRows + 1; c.batch = 1;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_CAPACITY, "rows cap");
+    c = base(); c.force_parts = 300;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_INVALID_ARG, "force parts");
+    c = base(); c.batch = 0;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_SHAPE, "batch 0");
+    CHECK(make_plan(base(), nullptr, &err) == PA_ERR_INVALID_ARG, "null plan");
+  }
+  // invariants over a grid of configurations
+  std::set<long long> scratch_by_bucket[32];
+  for (int hkv : {1, 2, 8}) {
+    for (long long batch : {1LL, 2LL, 3LL, 4LL, 31LL, 32LL, 33LL, 100LL, 4096LL}) {
+      for (int L : {1, 2, 3, 4, 6}) {
+        for (long long W : {1LL, 2LL, 5LL, 72LL, 256LL, 1024LL, 3000LL}) {
+          for (long long topk : {0LL, 1LL, 32LL, 100LL}) {
+            for (int fp : {0, 1, 3, 64}) {
+              pa_config c = base();
+              c.num_kv_heads = hkv;
+              c.batch = batch;
+              c.rows = batch * L;
+              c.max_pages = W;
+              c.topk = topk;
+              c.force_parts = fp;
+              if (c.rows > kMaxRows) continue;
+              int rc = make_plan(c, &p, &err);
+              if (rc == PA_ERR_CAPACITY && fp > 0) {
+                // a forced partition count may ask for more scratch than the
+                // largest bucket allows; it must be refused, never truncated
+                const long long pb = next_pow2(topk ? topk : W);
+                const long long parts = std::min<long long>(std::min<long long>(fp, kMaxParts), pb);
+                const long long want = parts * next_pow2(c.rows) * hkv * 16 * 130 * 4;
+                CHECK(want > kMaxScratchBytes, "refused although %lld bytes fit", want);
+                continue;
+              }
+              CHECK(rc == PA_OK, "plan rc %d (%s) fp=%d rows=%lld hkv=%d W=%lld topk=%lld", rc, err.c_str(),
+                    fp, (long long)c.rows, hkv, W, topk);
+              if (rc) continue;
+              const long long npages = topk ? topk : W;
+              CHECK(p.rt == (topk ? 1 : (L == 1 ? 1 : 2)), "rt %d", p.rt);
+              CHECK(p.groups * p.rt >= (topk ? 1 : L), "groups");
+              CHECK(p.parts_launched >= 1 && p.parts_launched <= p.parts, "parts %d/%d", p.parts_launched, p.parts);
+              CHECK(p.parts <= kMaxParts, "parts cap");
+              // every page position covered once: [k*ppp, (k+1)*ppp) for k < parts_launched
+              CHECK((long long)p.ppp * p.parts_launched >= npages, "coverage");
+              CHECK((long long)p.ppp * (p.parts_launched - 1) < npages, "no empty tail partition");
+              CHECK(p.merge == (p.parts_launched > 1), "merge flag");
+              const long long units = topk ? c.rows * hkv : batch * hkv * p.groups;
+              CHECK(p.units == units && p.grid == units * p.parts_launched, "grid");
+              if (p.merge) {
+                const long long need = (long long)p.parts_launched * c.rows * 16 * hkv * 130 * 4;
+                CHECK(p.scratch_bytes >= need, "scratch %lld < %lld", (long long)p.scratch_bytes, need);
+              } else {
+                CHECK(p.scratch_bytes == 0, "no scratch without merge");
+              }
+              CHECK(p.rows_bucket >= c.rows && (p.rows_bucket & (p.rows_bucket - 1)) == 0, "rows bucket");
+            }
+          }
+        }
+      }
+    }
+  }
+  // scratch depends only on buckets: all row counts in one bucket (lo, 2lo]
+  // (the rows that round up to the same power of two) agree
+  for (long long lo = 1; lo <= 2048; lo *= 2) {
+    std::set<long long> sizes;
+    for (long long r = lo + 1; r <= 2 * lo; ++r) {
+      pa_config c = base();
+      c.rows = r;
+      c.batch = r;
+      c.max_pages = 1024;
+      if (make_plan(c, &p, &err) == PA_OK) sizes.insert(p.scratch_bytes);
+    }
+    CHECK(sizes.size() == 1, "bucket (%lld, %lld] has %zu scratch sizes", lo, 2 * lo, sizes.size());
+  }
+  pa_plan_info info{};
+  make_plan(base(), &p, &err);
+  describe(p, &info);
+  CHECK(info.parts == p.parts_launched && info.grid_x == p.grid && info.merge == (p.merge ? 1 : 0), "describe");
+  if (failures) {
+    std::fprintf(stderr, "%d failures\n", failures);
+    return 1;
+  }
+  std::printf("plan self-test ok\n");
+  return 0;
+}

@@ -110,6 +110,7 @@ class Layers:
 
     force_parts = 0
     prefetch_depth = 0
+    workgroup_waves = 0
 
     def step(self, l, ev=None):
         pa.kv_quant_write(self.step_k, self.step_v, self.step_slots[l], self.kc, self.vc,
@@ -118,6 +119,7 @@ class Layers:
                         self.cu, self.sp, self.mode, self.out[l],
                         max_q_len=self.max_q_len if self.cu is not None else 0,
                         force_parts=self.force_parts, prefetch_depth=self.prefetch_depth,
+                        workgroup_waves=self.workgroup_waves,
                         main_begin_event=None if ev is None else ev[0],
                         main_end_event=None if ev is None else ev[1])
 
@@ -307,6 +309,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--force-parts", type=int, default=0, help="split-K partitions (0: the plan's choice)")
     ap.add_argument("--prefetch-depth", type=int, default=0, help="pages in flight per wave (0: the plan's)")
+    ap.add_argument("--workgroup-waves", type=int, default=0, help="4 or 8 waves per workgroup (0: the plan's)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -330,6 +333,7 @@ def main():
                          scale_mode=w.mode, force_parts=args.force_parts)
     layers.force_parts = args.force_parts
     layers.prefetch_depth = args.prefetch_depth
+    layers.workgroup_waves = args.workgroup_waves
     plan = pa.pa_plan_describe(cfg)
     pa.pa_reserve(cfg, stream)
 

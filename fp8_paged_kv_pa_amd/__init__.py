@@ -34,7 +34,7 @@ def pa_decode(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
 def pa_decode_ex(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
                  cu_seqlens_q, sparse_page_idx, scale_mode, out, sm_scale=0.0, max_q_len=0,
                  force_parts=0, main_begin_event=None, main_end_event=None, prefetch_depth=0,
-                 stream=None):
+                 workgroup_waves=0, stream=None):
     """``pa_decode`` with options; events are torch.cuda.Event objects that
     have been recorded once (so they exist)."""
     lib = load()
@@ -43,6 +43,7 @@ def pa_decode_ex(q, k_cache, v_cache, k_scale, v_scale, block_table, context_len
     opts.max_q_len = int(max_q_len)
     opts.force_parts = int(force_parts)
     opts.prefetch_depth = int(prefetch_depth)
+    opts.workgroup_waves = int(workgroup_waves)
     opts.main_begin_event = main_begin_event.cuda_event if main_begin_event is not None else None
     opts.main_end_event = main_end_event.cuda_event if main_end_event is not None else None
     d = [desc(t) for t in (q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,

@@ -52,7 +52,7 @@ class PaDecodeOpts(ctypes.Structure):
         ("main_begin_event", ctypes.c_void_p),
         ("main_end_event", ctypes.c_void_p),
         ("prefetch_depth", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("workgroup_waves", ctypes.c_int32),
     ]
 
 

@@ -214,6 +214,8 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   cfg.force_parts = opts ? opts->force_parts : 0;
   if (opts && (opts->prefetch_depth < 0 || opts->prefetch_depth > 4))
     return fail(PA_ERR_INVALID_ARG, "prefetch_depth must be in [0, 4]");
+  if (opts && opts->workgroup_waves != 0 && opts->workgroup_waves != 4 && opts->workgroup_waves != 8)
+    return fail(PA_ERR_INVALID_ARG, "workgroup_waves must be 0, 4 or 8");
   Plan plan;
   std::string perr;
   if ((rc = make_plan(cfg, &plan, &perr))) return fail(rc, perr);
@@ -263,7 +265,8 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   hipEvent_t e0 = opts ? reinterpret_cast<hipEvent_t>(opts->main_begin_event) : nullptr;
   hipEvent_t e1 = opts ? reinterpret_cast<hipEvent_t>(opts->main_end_event) : nullptr;
   const int depth = (opts && opts->prefetch_depth > 0) ? opts->prefetch_depth : plan.depth;
-  hipError_t he = launch_decode(a, plan.grid, plan.merge, plan.sparse, depth, e0, e1, stream);
+  const int waves = (opts && opts->workgroup_waves > 0) ? opts->workgroup_waves : plan.waves;
+  hipError_t he = launch_decode(a, plan.grid, plan.merge, plan.sparse, depth, waves, e0, e1, stream);
   if (he != hipSuccess) return fail(PA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(he));
   return PA_OK;
 }

@@ -64,7 +64,7 @@ struct WriteArgs {
 
 // Launchers (defined with their kernels).  Return hipSuccess or the launch
 // error.
-hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool sparse, int depth,
+hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool sparse, int depth, int waves,
                          hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 

@@ -38,7 +38,6 @@ namespace fp8pa {
 
 namespace {
 
-constexpr int kWaves = 4;
 constexpr float kLazyMax = 8.0f;  // log2 headroom before the running max moves
 constexpr int kAccPad = 132;      // LDS row pitch (floats) for the wave merge
 constexpr int kNoTokens = 1 << 30;  // token base of a position with nothing to read
@@ -86,8 +85,8 @@ __device__ __forceinline__ void consume_chunk(const Chunk& c) {
 // memory traffic.
 template <bool PER_TOKEN>
 __device__ __forceinline__ void load_chunk(Chunk& c, const DecodeArgs& a, int64_t blk, bool valid,
-                                           int wave, int lane) {
-  const int64_t base = valid ? blk * 16384 + wave * 4096 + lane * 16 : 0;
+                                           int chunk, int lane) {
+  const int64_t base = valid ? blk * 16384 + chunk * 4096 + lane * 16 : 0;
   const int istep = valid ? 64 : 0;
   const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + base);
   const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_cache + base);
@@ -97,7 +96,7 @@ __device__ __forceinline__ void load_chunk(Chunk& c, const DecodeArgs& a, int64_
   for (int i = 0; i < 4; ++i) c.v[i] = vp[istep * i];
   if constexpr (PER_TOKEN) {
     const int g = lane >> 4;
-    const int64_t sbase = valid ? blk * 128 + wave * 32 + 4 * g : 0;
+    const int64_t sbase = valid ? blk * 128 + chunk * 32 + 4 * g : 0;
     const int s4 = valid ? 16 : 0;
     c.ks[0] = *reinterpret_cast<const f32x4*>(a.k_scale + sbase);
     c.ks[1] = *reinterpret_cast<const f32x4*>(a.k_scale + sbase + s4);
@@ -113,10 +112,16 @@ __device__ __forceinline__ void load_chunk(Chunk& c, const DecodeArgs& a, int64_
 typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
 __device__ __forceinline__ const_i32_ptr as_const(const int32_t* p) { return (const_i32_ptr)(p); }
 
-template <int RT, bool PER_TOKEN, bool SPARSE, int NBUF>
-__global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) void pa_decode_main(DecodeArgs a) {
+template <int RT, bool PER_TOKEN, bool SPARSE, int NBUF, int NW>
+__global__ __launch_bounds__(kWave * NW, (NW == 4 && NBUF <= 2 ? 2 : 1)) void pa_decode_main(DecodeArgs a) {
+  static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
+  constexpr int S = NW / 4;  // pages streamed side by side (one per group of four waves)
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  // wave index as a provably uniform (scalar) value: table reads indexed by
+  // it stay scalar loads, off the vector-memory counter of the KV stream
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int cw = wave & 3;   // 32-token chunk of each page this wave handles
+  const int ps = wave >> 2;  // page stream: positions n0 + ps, n0 + ps + S, ...
   const int g = lane >> 4;   // lane group: tokens 4g..4g+3 of each 16-token tile
   const int hr = lane & 15;  // query head within the GQA group
   const int Hq = 16 * a.hkv;
@@ -129,12 +134,13 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
   // the partition's first block-table entry) are issued together, before
   // any branch, so they cost one memory round trip.
   const int n0 = part * a.ppp;  // < width (dense) or < topk (sparse) by construction of the grid
+  const int s0 = n0 + ps;       // this wave's first list position
   int h, b, row0, nrows, lim0;  // row row0+i sees tokens t < lim0 + i
-  int first_entry;              // dense: block_table[b][n0]; sparse: sparse_idx[row0][n0]
+  int first_entry;              // dense: block_table[b][s0]; sparse: sparse_idx[row0][s0] (-1 past the end)
   if constexpr (SPARSE) {
     h = int(unit % a.hkv);
     row0 = int(unit / a.hkv);
-    first_entry = as_const(a.sparse_idx + int64_t(row0) * a.sp_stride)[n0];
+    first_entry = s0 < a.topk ? as_const(a.sparse_idx + int64_t(row0) * a.sp_stride)[s0] : -1;
     int start, L;
     if (a.cu_seqlens_q) {
       b = find_request(a.cu_seqlens_q, a.batch, row0);
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
     const int64_t bh = unit / a.groups;
     h = int(bh % a.hkv);
     b = int(bh / a.hkv);
-    first_entry = as_const(a.block_table + int64_t(b) * a.bt_stride)[n0];
+    first_entry = s0 < a.width ? as_const(a.block_table + int64_t(b) * a.bt_stride)[s0] : -1;
     const int ctx = a.context_lens[b];
     int start, L;
     if (a.cu_seqlens_q) {
@@ -172,14 +178,14 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
   Chunk buf[NBUF];
   int tb[NBUF];
   {
-    int ln0 = n0, P0 = first_entry;
+    int ln0 = s0, P0 = first_entry;
     if constexpr (SPARSE) {
       ln0 = first_entry;
       P0 = (ln0 >= 0 && ln0 < a.width) ? as_const(a.block_table + int64_t(b) * a.bt_stride)[ln0] : -1;
     }
     const bool ok0 = P0 >= 0 && P0 < a.num_blocks;
     tb[0] = ok0 ? ln0 * 128 : kNoTokens;
-    load_chunk<PER_TOKEN>(buf[0], a, int64_t(P0) * a.hkv + h, ok0, wave, lane);
+    load_chunk<PER_TOKEN>(buf[0], a, int64_t(P0) * a.hkv + h, ok0, cw, lane);
   }
   // query operands: B of S^T = K Q^T, lane = (head hr, dims 8g..8g+7 of
   // each 32-dim k-step)
@@ -246,7 +252,7 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
   // (its physical page), valid_page() checks it one step later.
   // logical page of list position n (sparse: the list entry; -1 past the end)
   auto logical_at = [&](int n) -> int {
-    if constexpr (SPARSE) return n < n1 ? (n == n0 ? first_entry : sp_c[n]) : -1;
+    if constexpr (SPARSE) return n < n1 ? (n == s0 ? first_entry : sp_c[n]) : -1;
     return n;
   };
   auto logical_ok = [&](int n, int ln) -> bool {
@@ -255,11 +261,11 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
   // raw physical page of logical page ln (read only if the position is usable)
   auto raw_at = [&](int n, int ln) -> int {
     if (!logical_ok(n, ln)) return -1;
-    return (!SPARSE && n == n0) ? first_entry : bt_c[ln];
+    return (!SPARSE && n == s0) ? first_entry : bt_c[ln];
   };
   auto valid_page = [&](int P) -> bool { return P >= 0 && P < a.num_blocks; };
   auto process = [&](Chunk& c, int tbase) {
-    const int t0 = tbase + 32 * wave;
+    const int t0 = tbase + 32 * cw;
     if (t0 >= lim_max) {
       // nothing of this chunk is attended: still consume its registers so the
       // loads are complete on this path too
@@ -392,42 +398,43 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
   // ---- stream the partition's pages: a ring of NBUF chunk buffers, the
   // loads of the next NBUF-1 pages in flight while one is processed.  Table
   // entries are read one step ahead of their use. -------------------------
-  if (n0 < n1) {
+  if (s0 < n1) {
 #pragma unroll
     for (int k = 1; k < NBUF - 1; ++k) {
-      const int ln = logical_at(n0 + k);
-      const int P = raw_at(n0 + k, ln);
+      const int pos = s0 + k * S;
+      const int ln = logical_at(pos);
+      const int P = raw_at(pos, ln);
       const bool ok = valid_page(P);
       tb[k] = ok ? ln * 128 : kNoTokens;
-      load_chunk<PER_TOKEN>(buf[k], a, int64_t(P) * a.hkv + h, ok, wave, lane);
+      load_chunk<PER_TOKEN>(buf[k], a, int64_t(P) * a.hkv + h, ok, cw, lane);
     }
-    // raw entry of the next position to load (n0 + NBUF - 1) and the
+    // raw entry of the next position to load (s0 + (NBUF-1)*S) and the
     // logical page of the one after it
-    int ln_next = logical_at(n0 + NBUF - 1);
-    int P_next = raw_at(n0 + NBUF - 1, ln_next);
-    int ln_after = logical_at(n0 + NBUF);
-    for (int n = n0; n < n1; n += NBUF) {
+    int ln_next = logical_at(s0 + (NBUF - 1) * S);
+    int P_next = raw_at(s0 + (NBUF - 1) * S, ln_next);
+    int ln_after = logical_at(s0 + NBUF * S);
+    for (int n = s0; n < n1; n += NBUF * S) {
 #pragma unroll
       for (int k = 0; k < NBUF; ++k) {
-        const int nn = n + k;
+        const int nn = n + k * S;
         if (nn >= n1) break;
-        const int ls = (k + NBUF - 1) % NBUF;  // slot of position nn + NBUF - 1 (held nn - 1)
-        const int nl = nn + NBUF - 1;
+        const int ls = (k + NBUF - 1) % NBUF;  // slot of position nn + (NBUF-1)*S (held nn - S)
+        const int nl = nn + (NBUF - 1) * S;
         const bool ok = valid_page(P_next);
         tb[ls] = ok ? ln_next * 128 : kNoTokens;
-        load_chunk<PER_TOKEN>(buf[ls], a, int64_t(P_next) * a.hkv + h, ok, wave, lane);
+        load_chunk<PER_TOKEN>(buf[ls], a, int64_t(P_next) * a.hkv + h, ok, cw, lane);
         // table reads for the following steps (checked one step later)
         ln_next = ln_after;
-        P_next = raw_at(nl + 1, ln_next);
-        ln_after = logical_at(nl + 2);
+        P_next = raw_at(nl + S, ln_next);
+        ln_after = logical_at(nl + 2 * S);
         process(buf[k], tb[k]);
       }
     }
   }
 
-  // ---- merge the four waves, then write output or the partition partial --
-  __shared__ float sm_ml[kWaves][RT][16][2];
-  __shared__ float sm_acc[kWaves][16][kAccPad];
+  // ---- merge the waves, then write output or the partition partial --------
+  __shared__ float sm_ml[NW][RT][16][2];
+  __shared__ float sm_acc[NW][16][kAccPad];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     float lh = l_run[r];
@@ -440,14 +447,14 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
   }
   __syncthreads();
   const int t = threadIdx.x;
-  const int oh = t >> 4;        // output head handled by this thread
-  const int od = (t & 15) * 8;  // first of its 8 dims
+  const int oh = (t >> 4) & 15;  // output head handled by this thread (threads < 256)
+  const int od = (t & 15) * 8;   // first of its 8 dims
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     if (r >= nrows) break;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[w][r][hr][0]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[w][r][hr][0]);
     const float f = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[r] - M);
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
@@ -455,44 +462,46 @@ __global__ __launch_bounds__(kWave * kWaves, (RT <= 2 && NBUF <= 2 ? 2 : 1)) voi
       *reinterpret_cast<f32x4*>(&sm_acc[wave][hr][16 * d + 4 * g]) = v;
     }
     __syncthreads();
-    float Mo = -INFINITY;
+    if (t < 256) {
+      float Mo = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) Mo = fmaxf(Mo, sm_ml[w][r][oh][0]);
-    float Ls = 0.0f;
+      for (int w = 0; w < NW; ++w) Mo = fmaxf(Mo, sm_ml[w][r][oh][0]);
+      float Ls = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm_ml[w][r][oh][0];
-      const float fw = (Mo == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - Mo);
-      Ls += fw * sm_ml[w][r][oh][1];
-    }
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      s0 += *reinterpret_cast<const f32x4*>(&sm_acc[w][oh][od]);
-      s1 += *reinterpret_cast<const f32x4*>(&sm_acc[w][oh][od + 4]);
-    }
-    const int row = row0 + r;
-    const int qh = 16 * h + oh;
-    if (a.parts == 1) {
-      const float inv = Ls > 0.0f ? v_fold / Ls : 0.0f;
-      uint32_t packed[4];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        packed[e] = uint32_t(f32_to_bf16_rne(s0[2 * e] * inv)) |
-                    (uint32_t(f32_to_bf16_rne(s0[2 * e + 1] * inv)) << 16);
-        packed[2 + e] = uint32_t(f32_to_bf16_rne(s1[2 * e] * inv)) |
-                        (uint32_t(f32_to_bf16_rne(s1[2 * e + 1] * inv)) << 16);
+      for (int w = 0; w < NW; ++w) {
+        const float mw = sm_ml[w][r][oh][0];
+        const float fw = (Mo == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - Mo);
+        Ls += fw * sm_ml[w][r][oh][1];
       }
-      uint16_t* op = a.out + int64_t(row) * a.out_row_stride + int64_t(qh) * a.out_head_stride + od;
-      *reinterpret_cast<u32x4*>(op) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-    } else {
-      const int64_t pi = (int64_t(part) * a.rows + row) * Hq + qh;
-      f32x4* ap = reinterpret_cast<f32x4*>(a.part_acc + pi * 128 + od);
-      ap[0] = s0;
-      ap[1] = s1;
-      if ((t & 15) == 0) {
-        a.part_ml[2 * pi] = Mo;
-        a.part_ml[2 * pi + 1] = Ls;
+      f32x4 s0v = {0.f, 0.f, 0.f, 0.f}, s1v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        s0v += *reinterpret_cast<const f32x4*>(&sm_acc[w][oh][od]);
+        s1v += *reinterpret_cast<const f32x4*>(&sm_acc[w][oh][od + 4]);
+      }
+      const int row = row0 + r;
+      const int qh = 16 * h + oh;
+      if (a.parts == 1) {
+        const float inv = Ls > 0.0f ? v_fold / Ls : 0.0f;
+        uint32_t packed[4];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          packed[e] = uint32_t(f32_to_bf16_rne(s0v[2 * e] * inv)) |
+                      (uint32_t(f32_to_bf16_rne(s0v[2 * e + 1] * inv)) << 16);
+          packed[2 + e] = uint32_t(f32_to_bf16_rne(s1v[2 * e] * inv)) |
+                          (uint32_t(f32_to_bf16_rne(s1v[2 * e + 1] * inv)) << 16);
+        }
+        uint16_t* op = a.out + int64_t(row) * a.out_row_stride + int64_t(qh) * a.out_head_stride + od;
+        *reinterpret_cast<u32x4*>(op) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+      } else {
+        const int64_t pi = (int64_t(part) * a.rows + row) * Hq + qh;
+        f32x4* ap = reinterpret_cast<f32x4*>(a.part_acc + pi * 128 + od);
+        ap[0] = s0v;
+        ap[1] = s1v;
+        if ((t & 15) == 0) {
+          a.part_ml[2 * pi] = Mo;
+          a.part_ml[2 * pi + 1] = Ls;
+        }
       }
     }
     __syncthreads();
@@ -592,45 +601,48 @@ __global__ __launch_bounds__(256) void pa_merge(DecodeArgs a) {
 
 // With events, the dispatch itself records them (start and end of this
 // kernel), so the measured time is the kernel's own, without marker packets.
-template <int RT, bool PT, bool SP, int NB>
+template <int RT, bool PT, bool SP, int NB, int NW>
 void launch_main_t(const DecodeArgs& a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (e0 || e1)
-    hipExtLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB>), dim3(uint32_t(grid)), dim3(kWave * kWaves), 0,
+    hipExtLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB, NW>), dim3(uint32_t(grid)), dim3(kWave * NW), 0,
                           s, e0, e1, 0, a);
   else
-    hipLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB>), dim3(uint32_t(grid)), dim3(kWave * kWaves), 0, s,
+    hipLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB, NW>), dim3(uint32_t(grid)), dim3(kWave * NW), 0, s,
                        a);
 }
 
+// prefetch depth and workgroup width: eight waves (two pages side by side)
+// use the two-page ring; deeper rings are a four-wave tuning option.
 template <int RT, bool PT, bool SP>
-void launch_depth(const DecodeArgs& a, int depth, int64_t grid, hipStream_t s, hipEvent_t e0,
+void launch_shape(const DecodeArgs& a, int depth, int waves, int64_t grid, hipStream_t s, hipEvent_t e0,
                   hipEvent_t e1) {
+  if (waves == 8) return launch_main_t<RT, PT, SP, 2, 8>(a, grid, s, e0, e1);
   if constexpr (!SP) {
-    if (depth == 3) return launch_main_t<RT, PT, SP, 3>(a, grid, s, e0, e1);
-    if (depth >= 4) return launch_main_t<RT, PT, SP, 4>(a, grid, s, e0, e1);
+    if (depth == 3) return launch_main_t<RT, PT, SP, 3, 4>(a, grid, s, e0, e1);
+    if (depth >= 4) return launch_main_t<RT, PT, SP, 4, 4>(a, grid, s, e0, e1);
   }
-  launch_main_t<RT, PT, SP, 2>(a, grid, s, e0, e1);
+  launch_main_t<RT, PT, SP, 2, 4>(a, grid, s, e0, e1);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool sparse, int depth,
+hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool sparse, int depth, int waves,
                          hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   const bool pt = a.scale_mode == PA_SCALE_PER_TOKEN;
   hipEvent_t e0 = ev_begin, e1 = ev_end;
   // the one variant-selection table: (rows per group, per-token scales,
-  // sparse, prefetch depth)
-  const int d = depth;
+  // sparse, prefetch depth, waves per workgroup)
+  const int d = depth, w = waves;
   if (sparse) {
-    if (pt) launch_depth<1, true, true>(a, d, grid, stream, e0, e1);
-    else launch_depth<1, false, true>(a, d, grid, stream, e0, e1);
+    if (pt) launch_shape<1, true, true>(a, d, w, grid, stream, e0, e1);
+    else launch_shape<1, false, true>(a, d, w, grid, stream, e0, e1);
   } else if (a.rt == 1) {
-    if (pt) launch_depth<1, true, false>(a, d, grid, stream, e0, e1);
-    else launch_depth<1, false, false>(a, d, grid, stream, e0, e1);
+    if (pt) launch_shape<1, true, false>(a, d, w, grid, stream, e0, e1);
+    else launch_shape<1, false, false>(a, d, w, grid, stream, e0, e1);
   } else {
-    if (pt) launch_depth<2, true, false>(a, d, grid, stream, e0, e1);
-    else launch_depth<2, false, false>(a, d, grid, stream, e0, e1);
+    if (pt) launch_shape<2, true, false>(a, d, w, grid, stream, e0, e1);
+    else launch_shape<2, false, false>(a, d, w, grid, stream, e0, e1);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

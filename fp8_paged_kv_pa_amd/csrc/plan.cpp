@@ -97,6 +97,10 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
   p.parts = int(std::max<int64_t>(parts, 1));
   p.ppp = int(ceil_div(std::max<int64_t>(npages, 1), p.parts));
   p.parts_launched = int(ceil_div(std::max<int64_t>(npages, 1), p.ppp));
+  // Two-row workgroups take eight waves (two pages side by side): measured on
+  // q_len 4, it streams like twice the partitions without twice the partials.
+  // Single-row calls stream best with four.
+  p.waves = p.rt == 2 ? 8 : 4;
   p.merge = p.parts_launched > 1;
   p.grid = p.units * p.parts_launched;
   if (p.merge) {

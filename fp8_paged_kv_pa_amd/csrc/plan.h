@@ -46,6 +46,7 @@ struct Plan {
   int ppp = 1;             // pages (dense) or list entries (sparse) per partition
   int lmax = 1;            // bound on q_len used by the plan
   int depth = 2;           // pages of KV in flight per wave (chunk-buffer ring)
+  int waves = 4;           // waves per workgroup: 4 (one page at a time) or 8 (two side by side)
   bool sparse = false;
   bool merge = false;
   int64_t units = 0;       // dense: batch*Hkv*groups; sparse: rows*Hkv

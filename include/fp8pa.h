@@ -121,9 +121,10 @@ typedef struct pa_decode_opts {
   void* main_begin_event;  /* hipEvent_t pair recorded by the main kernel's   */
   void* main_end_event;    /* dispatch (its start and end); may be NULL       */
   int32_t prefetch_depth;  /* 0 => plan chooses; else 2..4 pages of KV in     */
-                           /* flight per wave (tuning; values other than 2    */
-                           /* apply to single-row dense calls)                */
-  int32_t reserved;
+                           /* flight per wave (tuning; depths above 2 apply   */
+                           /* to dense calls with 4-wave workgroups)          */
+  int32_t workgroup_waves; /* 0 => plan chooses; 4 (a workgroup streams one   */
+                           /* page at a time) or 8 (two pages side by side)   */
 } pa_decode_opts;
 
 /* Host-side description of a decode call, for capability queries, planning

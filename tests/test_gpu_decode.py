@@ -141,3 +141,15 @@ def test_prefetch_depths_match_oracle(kw, depth):
         out = case.decode(out=torch.empty_like(case.out), force_parts=parts, prefetch_depth=depth)
         torch.cuda.synchronize()
         compare(out, oracle_out(w), what=f"{w.name} depth={depth} parts={parts}")
+
+
+@pytest.mark.parametrize("kw", [CASES[0], CASES[2], CASES[4], CASES[6], CASES[8], CASES[9]],
+                         ids=["201", "203", "205", "207", "209", "210"])
+@pytest.mark.parametrize("waves", [4, 8])
+def test_workgroup_widths_match_oracle(kw, waves):
+    w = wl.small_case(**kw)
+    case = GpuCase(w)
+    for parts in (0, 1, 2, 5):
+        out = case.decode(out=torch.empty_like(case.out), force_parts=parts, workgroup_waves=waves)
+        torch.cuda.synchronize()
+        compare(out, oracle_out(w), what=f"{w.name} waves={waves} parts={parts}")

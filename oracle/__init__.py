@@ -14,6 +14,7 @@ What it computes is the plain definition, written out slowly and in fp64:
 * ``layout``    -- the page-shuffled byte order of the K and V pages and the
                    scale arrays, as index functions (page, head, token, dim)
                    -> byte offset.
+* ``bf16``      -- bfloat16 decode/encode for the unquantized (BF16) cache.
 * ``writer``    -- the cache writer: per (token, KV head) amax/448 scale,
                    fp32 division, e4m3 encode, store through the layout.
 * ``attention`` -- softmax attention over the dequantized cache in fp64,
@@ -36,4 +37,4 @@ GPUs):
   scale fold; "Test Plan" compares against a dequantized reference.
 """
 
-from . import e4m3, layout, writer, attention  # noqa: F401
+from . import bf16, e4m3, layout, writer, attention  # noqa: F401

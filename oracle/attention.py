@@ -34,7 +34,7 @@ import math
 
 import numpy as np
 
-from . import e4m3, layout
+from . import bf16, e4m3, layout
 
 NONE, SCALAR, PER_TOKEN = 0, 1, 2
 GROUP = 16
@@ -62,9 +62,14 @@ def row_limit(ctx: int, L: int, i: int) -> int:
     return int(ctx) - int(L) + int(i) + 1
 
 
-def _dequant_pages(cache_flat, scale_flat, pages, head, Hkv, kind, mode, scalar):
-    """Dequantized [len(pages)*128, 128] fp64 rows of the given physical pages."""
+def _dequant_pages(cache_flat, scale_flat, pages, head, Hkv, kind, mode, scalar, kv_dtype="fp8"):
+    """Dequantized [len(pages)*128, 128] fp64 rows of the given physical pages.
+    kv_dtype "bf16": the cache holds bf16 elements (uint16), no scales."""
     pages = np.asarray(pages, dtype=np.int64)
+    if kv_dtype == "bf16":
+        idx = (pages * Hkv + head)[:, None, None] * layout.BLOCK_BYTES + (
+            layout.K_IDX_BF16 if kind == "k" else layout.V_IDX_BF16)[None]
+        return bf16.decode(cache_flat[idx]).reshape(-1, DIM)
     idx = layout.block_base(pages, head, Hkv)[:, None, None] + (
         layout.K_IDX if kind == "k" else layout.V_IDX)[None]
     vals = e4m3.decode(cache_flat[idx]).reshape(-1, DIM)
@@ -106,7 +111,7 @@ def _row_tokens(b, i, L, ctx, block_table, num_blocks, sparse_row):
 
 def attention_ref(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
                   cu_seqlens_q=None, sparse_page_idx=None, mode=PER_TOKEN,
-                  num_kv_heads=1, sm_scale=None, rows_subset=None):
+                  num_kv_heads=1, sm_scale=None, rows_subset=None, kv_dtype="fp8"):
     """fp64 attention output [rows, 16*Hkv, 128] (or only ``rows_subset``).
 
     q: [rows, 16*Hkv, 128] values (bf16 inputs widened exactly).
@@ -125,6 +130,8 @@ def attention_ref(q, k_cache, v_cache, k_scale, v_scale, block_table, context_le
     num_blocks = k_cache.size // (Hkv * layout.BLOCK_BYTES)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(DIM)
+    if kv_dtype == "bf16":
+        mode = NONE
     ks = vs = None
     if mode == SCALAR:
         ks = float(np.asarray(k_scale).reshape(-1)[0])
@@ -143,8 +150,8 @@ def attention_ref(q, k_cache, v_cache, k_scale, v_scale, block_table, context_le
                 key = (P, h)
                 if key not in cache:
                     cache[key] = (
-                        _dequant_pages(k_cache, k_scale, [P], h, Hkv, "k", mode, ks),
-                        _dequant_pages(v_cache, v_scale, [P], h, Hkv, "v", mode, vs))
+                        _dequant_pages(k_cache, k_scale, [P], h, Hkv, "k", mode, ks, kv_dtype),
+                        _dequant_pages(v_cache, v_scale, [P], h, Hkv, "v", mode, vs, kv_dtype))
                 kp, vp = cache[key]
                 ks_parts.append(kp[:cnt])
                 vs_parts.append(vp[:cnt])
@@ -210,7 +217,7 @@ def lse_merge(partials):
 
 def attention_bruteforce(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
                          cu_seqlens_q=None, sparse_page_idx=None, mode=PER_TOKEN,
-                         num_kv_heads=1, sm_scale=None):
+                         num_kv_heads=1, sm_scale=None, kv_dtype="fp8"):
     q = np.asarray(q, dtype=np.float64)
     rows = q.shape[0]
     Hkv = num_kv_heads
@@ -248,17 +255,25 @@ def attention_bruteforce(q, k_cache, v_cache, k_scale, v_scale, block_table, con
                         continue
                     o = t % PAGE
                     base = (P * Hkv + h) * PAGE * DIM
-                    if mode == PER_TOKEN:
+                    if kv_dtype == "bf16":
+                        sk = sv = 1.0
+                    elif mode == PER_TOKEN:
                         sk = float(k_scale[(P * Hkv + h) * PAGE + o])
                         sv = float(v_scale[(P * Hkv + h) * PAGE + o])
                     elif mode == SCALAR:
                         sk, sv = float(k_scale[0]), float(v_scale[0])
                     else:
                         sk = sv = 1.0
-                    kvec = [e4m3.decode_byte(k_cache[base + int(layout.k_offset(o, d))]) * sk
-                            for d in range(DIM)]
-                    vvec = [e4m3.decode_byte(v_cache[base + int(layout.v_offset(o, d))]) * sv
-                            for d in range(DIM)]
+                    if kv_dtype == "bf16":
+                        kvec = [float(bf16.decode(k_cache[base + int(layout.k_offset_bf16(o, d))]))
+                                for d in range(DIM)]
+                        vvec = [float(bf16.decode(v_cache[base + int(layout.v_offset_bf16(o, d))]))
+                                for d in range(DIM)]
+                    else:
+                        kvec = [e4m3.decode_byte(k_cache[base + int(layout.k_offset(o, d))]) * sk
+                                for d in range(DIM)]
+                        vvec = [e4m3.decode_byte(v_cache[base + int(layout.v_offset(o, d))]) * sv
+                                for d in range(DIM)]
                     kv.append((kvec, vvec))
                 for j in range(GROUP):
                     qh = q[r, GROUP * h + j]

@@ -25,7 +25,7 @@ too.
 
 import numpy as np
 
-from . import e4m3, layout
+from . import bf16, e4m3, layout
 
 NONE, SCALAR, PER_TOKEN = 0, 1, 2
 E4M3_MAX = np.float32(448.0)
@@ -98,3 +98,29 @@ def quant_write_ref(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_sca
         sidx = layout.scale_index(pages[:, None], heads[None, :], offs[:, None], Hkv)
         k_scale[sidx] = ksc
         v_scale[sidx] = vsc
+
+
+def write_bf16_ref(k_new, v_new, slot_mapping, k_cache, v_cache, num_kv_heads: int):
+    """The same writer for the unquantized BF16 cache: each value is stored
+    as bf16 (round to nearest even from fp32; bf16 inputs, passed widened,
+    are stored unchanged) at the bf16 layout's element offset.  k_cache,
+    v_cache: flat uint16 arrays of num_blocks * Hkv * 16384 elements."""
+    k_new = np.asarray(k_new, dtype=np.float32)
+    v_new = np.asarray(v_new, dtype=np.float32)
+    T, Hkv, D = k_new.shape
+    assert Hkv == num_kv_heads and D == layout.DIM
+    num_blocks = k_cache.size // (Hkv * layout.BLOCK_BYTES)
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    keep = (slots >= 0) & (slots < num_blocks * layout.PAGE)
+    ts = np.nonzero(keep)[0]
+    if len(ts) == 0:
+        return
+    pages = slots[ts] // layout.PAGE
+    offs = slots[ts] % layout.PAGE
+    heads = np.arange(Hkv)
+    base = (pages[:, None] * Hkv + heads[None, :]) * layout.BLOCK_BYTES
+    dims = np.arange(layout.DIM)
+    kidx = base[:, :, None] + layout.k_offset_bf16(offs[:, None, None], dims[None, None, :])
+    vidx = base[:, :, None] + layout.v_offset_bf16(offs[:, None, None], dims[None, None, :])
+    k_cache[kidx] = bf16.encode(k_new[ts])
+    v_cache[vidx] = bf16.encode(v_new[ts])

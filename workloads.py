@@ -16,7 +16,7 @@ tokens plus one, batch 4 (concurrency) for 8K contexts and 32
 (--max-num-seqs) for 128K contexts.
 """
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import List, Optional
 
 import numpy as np
@@ -55,6 +55,7 @@ class Workload:
     written: List[np.ndarray] = field(default_factory=list)  # per request: logical pages holding data
     q: Optional[np.ndarray] = None       # float32 (bf16-exact) [rows, 16*Hkv, 128]
     sm_scale: Optional[float] = None
+    kv_dtype: str = "fp8"                # "fp8" (e4m3fn codes) or "bf16" (unquantized)
 
     @property
     def W(self) -> int:
@@ -117,7 +118,9 @@ class Workload:
     def kv_bytes_attended(self) -> int:
         """Algorithmic KV bytes one decode call must read: every distinct
         (request, KV head, attended token) once, 256 code bytes plus 8 scale
-        bytes in per-token mode."""
+        bytes in per-token mode (512 bytes for a bf16 cache)."""
+        if self.kv_dtype == "bf16":
+            return self.attended_tokens() * self.Hkv * 4 * DIM
         per_tok = 2 * DIM + (8 if self.mode == PER_TOKEN else 0)
         return self.attended_tokens() * self.Hkv * per_tok
 
@@ -245,3 +248,9 @@ def small_case(seed, ctx, q_lens, Hkv=1, ragged=False, mode=PER_TOKEN, sparse_to
     pool = pool or max(need + 3, 4)
     return _make(f"small_{seed}", seed, ctx, q_lens, Hkv, pool, ragged, mode, W=W,
                  sparse_topk=sparse_topk)
+
+
+def bf16_kv(w: Workload) -> Workload:
+    """The same workload over an unquantized bf16 cache (no scales): the
+    same queries, contexts, tables and K/V draws."""
+    return replace(w, name=w.name + "_bf16", kv_dtype="bf16", mode=NONE)

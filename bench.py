@@ -44,6 +44,11 @@ CONFIGS = {
     "c4m": lambda: wl.c4_spec("mixed"),
     "c5": lambda: wl.c5_sparse(False),
     "c5t": lambda: wl.c5_sparse(True),
+    # the same shapes over the unquantized bf16 cache (the FP8 cache's control)
+    "c2b": lambda: wl.bf16_kv(wl.c2_dense_8k()),
+    "c3b": lambda: wl.bf16_kv(wl.c3_dense_128k(wl.PER_TOKEN)),
+    "c4b": lambda: wl.bf16_kv(wl.c4_spec("uniform")),
+    "c5b": lambda: wl.bf16_kv(wl.c5_sparse(False)),
 }
 
 
@@ -59,15 +64,23 @@ class Layers:
         self.w, self.n, self.dev = w, n, dev
         NB, Hkv = w.num_blocks, w.Hkv
         tot = NB * n
-        self.kc = torch.empty(tot, Hkv, 16384, dtype=torch.uint8, device=dev)
+        bf = w.kv_dtype == "bf16"
+        self.kc = torch.empty(tot, Hkv, 16384, dtype=torch.int16 if bf else torch.uint8, device=dev)
         self.vc = torch.empty_like(self.kc)
         self.ks = torch.empty(tot, Hkv, 128, dtype=torch.float32, device=dev)
         self.vs = torch.empty_like(self.ks)
         g = torch.Generator(device=dev)
         g.manual_seed(w.seed)
-        # unwritten slots hold random finite codes and large scales
-        self.kc[:NB].random_(0, 0x7F, generator=g)
-        self.vc[:NB].random_(0, 0x7F, generator=g)
+        # unwritten slots hold random finite codes and large scales (bf16:
+        # random bit patterns); no scales for a bf16 cache
+        if bf:
+            self.kc[:NB].random_(-32768, 32768, generator=g)
+            self.vc[:NB].random_(-32768, 32768, generator=g)
+            self.kc = self.kc.view(torch.bfloat16)
+            self.vc = self.vc.view(torch.bfloat16)
+        else:
+            self.kc[:NB].random_(0, 0x7F, generator=g)
+            self.vc[:NB].random_(0, 0x7F, generator=g)
         self.ks[:NB].fill_(1e3)
         self.vs[:NB].fill_(1e3)
         self.mode = w.mode
@@ -235,11 +248,19 @@ def cpu_baseline(w, layers, budget_s=12.0):
         sc_k = np.array([w.k_scalar], np.float32)
         sc_v = np.array([w.v_scalar], np.float32)
 
+        bf = w.kv_dtype == "bf16"
+
+        def write(k, v, slots, kc, vc, ka, va):
+            if bf:
+                owr.write_bf16_ref(k, v, slots, kc, vc, w.Hkv)
+            else:
+                owr.quant_write_ref(k, v, slots, kc, vc, ka, va, w.mode, w.Hkv)
+
         def request_state(b):
             """untimed: the oracle's compact cache of request b (state, like the GPU cache)"""
             pages = [int(x) for x in w.written[b]]
             nb = len(pages) + 1
-            kc = np.zeros(nb * w.Hkv * 16384, np.uint8)
+            kc = np.zeros(nb * w.Hkv * 16384, np.uint16 if bf else np.uint8)
             vc = np.zeros_like(kc)
             ks = np.zeros(nb * w.Hkv * 128, np.float32)
             vs = np.zeros_like(ks)
@@ -248,8 +269,7 @@ def cpu_baseline(w, layers, budget_s=12.0):
             for ci, pg in enumerate(pages):
                 bt[0, pg] = ci
                 k, v = w.page_kv(b, pg)
-                owr.quant_write_ref(k, v, ci * 128 + np.arange(k.shape[0], dtype=np.int64), kc, vc,
-                                    ka, va, w.mode, w.Hkv)
+                write(k, v, ci * 128 + np.arange(k.shape[0], dtype=np.int64), kc, vc, ka, va)
             start, L = int(w.row_start[b]), int(w.q_lens[b])
             c = int(w.ctx[b])
             new_slots = np.array([bt[0, (c - L + i) // 128] * 128 + (c - L + i) % 128 for i in range(L)],
@@ -268,10 +288,9 @@ def cpu_baseline(w, layers, budget_s=12.0):
             cu = None if w.cu is None else np.array([0, L])
             # timed: the step on the CPU (write the new tokens, attend the rows)
             t0 = time.time()
-            owr.quant_write_ref(sk[start:start + L], sv[start:start + L], new_slots, kc, vc, ka, va,
-                                w.mode, w.Hkv)
+            write(sk[start:start + L], sv[start:start + L], new_slots, kc, vc, ka, va)
             ref = oatt.attention_ref(w.q[start:start + L], kc, vc, ka, va, bt, w.ctx[b:b + 1], cu, sp,
-                                     w.mode, w.Hkv)
+                                     w.mode, w.Hkv, kv_dtype=w.kv_dtype)
             t_used += time.time() - t0
             if n < len(reqs):
                 err, cos = compare(out0[rows], ref, what=f"bench check request {b}")
@@ -281,7 +300,7 @@ def cpu_baseline(w, layers, budget_s=12.0):
             else:
                 sel = {int(x) for r in rows for x in w.sparse[r] if 0 <= x < w.W}
                 toks = sum(min(128, int(w.ctx[b]) - 128 * x) for x in sel)
-            done_bytes += toks * w.Hkv * (256 + (8 if w.mode == wl.PER_TOKEN else 0))
+            done_bytes += toks * w.Hkv * (512 if bf else 256 + (8 if w.mode == wl.PER_TOKEN else 0))
             n += 1
     finally:
         if lim is not None:
@@ -292,7 +311,7 @@ def cpu_baseline(w, layers, budget_s=12.0):
         "cores": 1,
         "kind": "oracle",
         "sample": f"{n} request-steps over the first {len(reqs)} requests of {w.name} (write the "
-                  f"request's new tokens, dequantize its attended pages, fp64 softmax attention for its "
+                  f"request's new tokens, decode its attended pages, fp64 softmax attention for its "
                   f"rows), one host thread, {t_used:.1f} s timed",
         "check_max_abs_err": None if check is None else round(check[0], 6),
         "check_min_cos": None if check is None else round(check[1], 8),
@@ -330,7 +349,8 @@ def main():
     stream = torch.cuda.Stream()
     cfg = pa.make_config(w.Hkv, w.rows, w.B, w.W, topk=0 if w.sparse is None else w.sparse.shape[1],
                          ragged=w.cu is not None, max_q_len=int(w.q_lens.max()) if w.cu is not None else 0,
-                         scale_mode=w.mode, force_parts=args.force_parts)
+                         scale_mode=w.mode, force_parts=args.force_parts,
+                         kv_dtype=3 if w.kv_dtype == "bf16" else 1)
     layers.force_parts = args.force_parts
     layers.prefetch_depth = args.prefetch_depth
     layers.workgroup_waves = args.workgroup_waves
@@ -418,13 +438,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3-kv/bf16-mfma/f32-acc",
+        "dtype": ("bf16" if w.kv_dtype == "bf16" else "fp8e4m3") + "-kv/bf16-mfma/f32-acc",
         "data": "synthetic",
         "config": {
             "workload": w.name,
             "batch": w.B, "q_len": int(w.q_lens.max()), "rows": w.rows, "kv_heads": w.Hkv,
             "q_heads_per_kv": 16, "head_dim": 128, "page": 128,
             "context": [int(w.ctx.min()), int(w.ctx.max())],
+            "kv_dtype": w.kv_dtype,
             "scale_mode": ["none", "scalar", "per_token"][w.mode],
             "sparse_topk": 0 if w.sparse is None else int(w.sparse.shape[1]),
             "layers_rotated": n_layers,

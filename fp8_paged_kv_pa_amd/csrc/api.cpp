@@ -58,18 +58,18 @@ int check_tensor(const pa_tensor* t, const char* name) {
   return PA_OK;
 }
 
-// K or V cache: [num_blocks, Hkv, ...] with 16384 bytes per (block, head),
-// contiguous.
+// K or V cache: [num_blocks, Hkv, ...] with 16384 elements per (block,
+// head) -- FP8 bytes, or bf16 for the unquantized cache -- contiguous.
 int check_cache(const pa_tensor* t, const char* name, int64_t* nb, int64_t* hkv) {
   int rc = check_tensor(t, name);
   if (rc) return rc;
-  if (t->dtype != PA_DTYPE_U8 && t->dtype != PA_DTYPE_F8E4M3)
-    return fail(PA_ERR_DTYPE, std::string(name) + " must be uint8 or float8_e4m3fn");
+  if (t->dtype != PA_DTYPE_U8 && t->dtype != PA_DTYPE_F8E4M3 && t->dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_DTYPE, std::string(name) + " must be uint8, float8_e4m3fn or bfloat16");
   if (t->ndim < 3) return fail(PA_ERR_SHAPE, std::string(name) + " must be [num_blocks, Hkv, 16384]");
   int64_t inner = 1;
   for (int i = 2; i < t->ndim; ++i) inner *= t->shape[i];
   if (inner != kBlockBytes)
-    return fail(PA_ERR_SHAPE, std::string(name) + ": each (page, head) block must hold 16384 bytes (128-token pages, head_dim 128)");
+    return fail(PA_ERR_SHAPE, std::string(name) + ": each (page, head) block must hold 16384 elements (128-token pages, head_dim 128)");
   if (!contiguous(t)) return fail(PA_ERR_LAYOUT, std::string(name) + " must be contiguous");
   if (!aligned(t->data, 16)) return fail(PA_ERR_LAYOUT, std::string(name) + " must be 16-byte aligned");
   *nb = t->shape[0];
@@ -167,6 +167,9 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
     return fail(PA_ERR_UNSUPPORTED, "q has " + std::to_string(Hq) + " heads but the cache has " +
                                         std::to_string(hkv) + " KV heads: the group must be 16");
   if (mode < PA_SCALE_NONE || mode > PA_SCALE_PER_TOKEN) return fail(PA_ERR_INVALID_ARG, "unknown scale_mode");
+  const bool bf16kv = kc->dtype == PA_DTYPE_BF16;
+  if (bf16kv && mode != PA_SCALE_NONE)
+    return fail(PA_ERR_UNSUPPORTED, "a bfloat16 cache is unquantized: scale_mode must be PA_SCALE_NONE");
   if ((rc = check_scales(ks, vs, mode, nb, hkv))) return rc;
 
   if ((rc = check_tensor(bt, "block_table"))) return rc;
@@ -259,6 +262,7 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   a.parts = plan.parts_launched;
   a.ppp = plan.ppp;
   a.scale_mode = mode;
+  a.kv_bf16 = bf16kv ? 1 : 0;
   float sm = (opts && opts->sm_scale != 0.0f) ? opts->sm_scale : 1.0f / std::sqrt(float(kDim));
   a.sm_log2 = sm * 1.4426950408889634f;
 
@@ -323,8 +327,12 @@ int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tens
   if ((rc = check_cache(v_cache, "v_cache", &nb2, &hkv2))) return rc;
   if (nb2 != nb || hkv2 != hkv) return fail(PA_ERR_SHAPE, "k_cache and v_cache shapes differ");
   if (hkv != hkv_in) return fail(PA_ERR_SHAPE, "k_new has a different number of KV heads than the cache");
+  if (k_cache->dtype != v_cache->dtype) return fail(PA_ERR_DTYPE, "k_cache and v_cache dtypes differ");
   if (scale_mode < PA_SCALE_NONE || scale_mode > PA_SCALE_PER_TOKEN)
     return fail(PA_ERR_INVALID_ARG, "unknown scale_mode");
+  const bool bf16kv = k_cache->dtype == PA_DTYPE_BF16;
+  if (bf16kv && scale_mode != PA_SCALE_NONE)
+    return fail(PA_ERR_UNSUPPORTED, "a bfloat16 cache is unquantized: scale_mode must be PA_SCALE_NONE");
   if ((rc = check_scales(k_scale, v_scale, scale_mode, nb, hkv))) return rc;
   if (T == 0) return PA_OK;
 
@@ -336,6 +344,7 @@ int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tens
   a.v_tok_stride = v_new->stride[0];
   a.v_head_stride = v_new->stride[1];
   a.in_bf16 = k_new->dtype == PA_DTYPE_BF16;
+  a.out_bf16 = bf16kv ? 1 : 0;
   a.slots = static_cast<const int64_t*>(slot_mapping->data);
   a.k_cache = static_cast<uint8_t*>(k_cache->data);
   a.v_cache = static_cast<uint8_t*>(v_cache->data);

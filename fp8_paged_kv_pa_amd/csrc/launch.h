@@ -15,7 +15,7 @@ struct DecodeArgs {
   const uint16_t* q;          // bf16 [rows, Hq, 128]
   int64_t q_row_stride;       // elements
   int64_t q_head_stride;
-  const uint8_t* k_cache;     // [num_blocks, Hkv, 16384]
+  const uint8_t* k_cache;     // [num_blocks, Hkv, 16384] FP8 bytes or bf16 elements
   const uint8_t* v_cache;
   const float* k_scale;       // per-token [num_blocks, Hkv, 128] or scalar [1] or null
   const float* v_scale;
@@ -42,6 +42,7 @@ struct DecodeArgs {
   int32_t parts;              // partitions launched per unit
   int32_t ppp;                // pages / list entries per partition
   int32_t scale_mode;
+  int32_t kv_bf16;            // 1: unquantized bf16 cache (no scales)
   float sm_log2;              // sm_scale * log2(e)
 };
 
@@ -51,8 +52,9 @@ struct WriteArgs {
   int64_t k_tok_stride, k_head_stride;  // elements
   int64_t v_tok_stride, v_head_stride;
   int32_t in_bf16;            // 1: inputs are bf16, 0: f32
+  int32_t out_bf16;           // 1: the cache is bf16 (stored unquantized)
   const int64_t* slots;       // [T]
-  uint8_t* k_cache;
+  uint8_t* k_cache;           // FP8 bytes, or bf16 elements when out_bf16
   uint8_t* v_cache;
   float* k_scale;             // per-token output, scalar input, or null
   float* v_scale;

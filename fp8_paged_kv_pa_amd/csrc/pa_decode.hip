@@ -29,6 +29,10 @@
 // chunk exceeds it by more than 2^8, so P stays <= 256 and the rescale of
 // the accumulators is rare.  The four waves' partials merge through LDS at
 // the end; with one partition the workgroup writes bf16 output directly.
+//
+// The unquantized bf16 cache (the control the FP8 cache is measured
+// against) runs the same kernel: its pages keep the same chunking with
+// 2-byte elements, so each 16-byte load is one bf16 operand as is.
 #include <hip/hip_ext.h>
 
 #include "device_common.h"
@@ -42,9 +46,15 @@ constexpr float kLazyMax = 8.0f;  // log2 headroom before the running max moves
 constexpr int kAccPad = 132;      // LDS row pitch (floats) for the wave merge
 constexpr int kNoTokens = 1 << 30;  // token base of a position with nothing to read
 
+// One wave's 32-token chunk of a (page, KV head) block as loaded: 1 KiB
+// rows of K and V, 16 bytes per lane each (FP8: 4 rows of each, every
+// 16-byte piece two 8-byte operands; bf16: 8 rows, every piece one
+// operand), plus the chunk's per-token scales.
+template <bool BF>
 struct Chunk {
-  u32x4 k[4];
-  u32x4 v[4];
+  static constexpr int kRows = BF ? 8 : 4;
+  u32x4 k[kRows];
+  u32x4 v[kRows];
   f32x4 ks[2];
   f32x4 vs[2];
 };
@@ -71,10 +81,10 @@ __device__ __forceinline__ void request_rows(const DecodeArgs& a, int b, int* st
 
 // An empty asm that reads every register of a chunk: forces the compiler to
 // complete the chunk's loads here (used on paths that skip the chunk).
-template <bool PER_TOKEN>
-__device__ __forceinline__ void consume_chunk(const Chunk& c) {
+template <bool PER_TOKEN, bool BF>
+__device__ __forceinline__ void consume_chunk(const Chunk<BF>& c) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(c.k[i]), "v"(c.v[i]));
+  for (int i = 0; i < Chunk<BF>::kRows; ++i) asm volatile("" ::"v"(c.k[i]), "v"(c.v[i]));
   if constexpr (PER_TOKEN) asm volatile("" ::"v"(c.ks[0]), "v"(c.ks[1]), "v"(c.vs[0]), "v"(c.vs[1]));
 }
 
@@ -83,17 +93,19 @@ __device__ __forceinline__ void consume_chunk(const Chunk& c) {
 // the same number of load instructions is issued on every path (so the
 // compiler's wait counts stay exact across the prefetch ring) at almost no
 // memory traffic.
-template <bool PER_TOKEN>
-__device__ __forceinline__ void load_chunk(Chunk& c, const DecodeArgs& a, int64_t blk, bool valid,
+template <bool PER_TOKEN, bool BF>
+__device__ __forceinline__ void load_chunk(Chunk<BF>& c, const DecodeArgs& a, int64_t blk, bool valid,
                                            int chunk, int lane) {
-  const int64_t base = valid ? blk * 16384 + chunk * 4096 + lane * 16 : 0;
+  constexpr int64_t kBlockBytes = BF ? 32768 : 16384;  // one (page, head) block
+  constexpr int kChunkBytes = BF ? 8192 : 4096;        // one 32-token chunk of it
+  const int64_t base = valid ? blk * kBlockBytes + chunk * kChunkBytes + lane * 16 : 0;
   const int istep = valid ? 64 : 0;
   const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + base);
   const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_cache + base);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) c.k[i] = kp[istep * i];
+  for (int i = 0; i < Chunk<BF>::kRows; ++i) c.k[i] = kp[istep * i];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) c.v[i] = vp[istep * i];
+  for (int i = 0; i < Chunk<BF>::kRows; ++i) c.v[i] = vp[istep * i];
   if constexpr (PER_TOKEN) {
     const int g = lane >> 4;
     const int64_t sbase = valid ? blk * 128 + chunk * 32 + 4 * g : 0;
@@ -112,8 +124,16 @@ __device__ __forceinline__ void load_chunk(Chunk& c, const DecodeArgs& a, int64_
 typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
 __device__ __forceinline__ const_i32_ptr as_const(const int32_t* p) { return (const_i32_ptr)(p); }
 
-template <int RT, bool PER_TOKEN, bool SPARSE, int NBUF, int NW>
-__global__ __launch_bounds__(kWave * NW, (NW == 4 && NBUF <= 2 ? 2 : 1)) void pa_decode_main(DecodeArgs a) {
+// Two workgroups per CU (256 registers per lane) for the four-wave,
+// two-page-ring shapes; one for the rest -- including two-row bf16, whose
+// two 16 KiB-per-wave chunk buffers and two rows of accumulators need more.
+template <int RT, bool NBUF2_NW4, bool BF>
+constexpr int kMinBlocks = (NBUF2_NW4 && !(BF && RT == 2)) ? 2 : 1;
+
+template <int RT, bool PER_TOKEN, bool SPARSE, int NBUF, int NW, bool BF>
+__global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, BF>)) void pa_decode_main(
+    DecodeArgs a) {
+  static_assert(!(BF && PER_TOKEN), "a bf16 cache carries no scales");
   static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
   constexpr int S = NW / 4;  // pages streamed side by side (one per group of four waves)
   const int lane = threadIdx.x & (kWave - 1);
@@ -175,7 +195,7 @@ __global__ __launch_bounds__(kWave * NW, (NW == 4 && NBUF <= 2 ? 2 : 1)) void pa
   // The partition's first chunk and the query operands do not depend on the
   // context length: issue their loads now, so they travel together with the
   // context-length read instead of after it (masking handles the rest).
-  Chunk buf[NBUF];
+  Chunk<BF> buf[NBUF];
   int tb[NBUF];
   {
     int ln0 = s0, P0 = first_entry;
@@ -185,7 +205,7 @@ __global__ __launch_bounds__(kWave * NW, (NW == 4 && NBUF <= 2 ? 2 : 1)) void pa
     }
     const bool ok0 = P0 >= 0 && P0 < a.num_blocks;
     tb[0] = ok0 ? ln0 * 128 : kNoTokens;
-    load_chunk<PER_TOKEN>(buf[0], a, int64_t(P0) * a.hkv + h, ok0, cw, lane);
+    load_chunk<PER_TOKEN, BF>(buf[0], a, int64_t(P0) * a.hkv + h, ok0, cw, lane);
   }
   // query operands: B of S^T = K Q^T, lane = (head hr, dims 8g..8g+7 of
   // each 32-dim k-step)
@@ -264,28 +284,48 @@ __global__ __launch_bounds__(kWave * NW, (NW == 4 && NBUF <= 2 ? 2 : 1)) void pa
     return (!SPARSE && n == s0) ? first_entry : bt_c[ln];
   };
   auto valid_page = [&](int P) -> bool { return P >= 0 && P < a.num_blocks; };
-  auto process = [&](Chunk& c, int tbase) {
+  auto process = [&](Chunk<BF>& c, int tbase) {
     const int t0 = tbase + 32 * cw;
     if (t0 >= lim_max) {
       // nothing of this chunk is attended: still consume its registers so the
       // loads are complete on this path too
-      consume_chunk<PER_TOKEN>(c);
+      consume_chunk<PER_TOKEN, BF>(c);
       return;
     }
     const bool full = t0 + 32 <= lim_min;
 
     // token of this lane's score slot e: t0 + 16*(e/4) + 4g + e%4
     if (!full) {
-      // zero V bytes of tokens past the context: their bytes were never written
-      uint32_t m0 = 0, m1 = 0;
+      // zero V of tokens past the context: those slots were never written
+      // (a NaN there would survive a zero weight in the product)
+      if constexpr (BF) {
+        // word w holds slots 2w, 2w+1 of one dim
+        uint32_t m[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (t0 + 4 * g + e < lim_max) m0 |= 0xFFu << (8 * e);
-        if (t0 + 16 + 4 * g + e < lim_max) m1 |= 0xFFu << (8 * e);
-      }
+        for (int w = 0; w < 4; ++w) {
+          m[w] = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c.v[i][0] &= m0; c.v[i][1] &= m1; c.v[i][2] &= m0; c.v[i][3] &= m1;
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int e = 2 * w + s2;
+            if (t0 + 16 * (e >> 2) + 4 * g + (e & 3) < lim_max) m[w] |= 0xFFFFu << (16 * s2);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < Chunk<BF>::kRows; ++i) {
+          c.v[i][0] &= m[0]; c.v[i][1] &= m[1]; c.v[i][2] &= m[2]; c.v[i][3] &= m[3];
+        }
+      } else {
+        // bytes 0-3 of a dword: slots 0-3 (first 16 tokens), next dword slots 4-7
+        uint32_t m0 = 0, m1 = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (t0 + 4 * g + e < lim_max) m0 |= 0xFFu << (8 * e);
+          if (t0 + 16 + 4 * g + e < lim_max) m1 |= 0xFFu << (8 * e);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          c.v[i][0] &= m0; c.v[i][1] &= m1; c.v[i][2] &= m0; c.v[i][3] &= m1;
+        }
       }
     }
 
@@ -304,14 +344,20 @@ __global__ __launch_bounds__(kWave * NW, (NW == 4 && NBUF <= 2 ? 2 : 1)) void pa
     }
 
     // S^T = K Q^T for every row tile, k-step outer so each converted K
-    // operand (exact e4m3 -> bf16) serves all row tiles
+    // operand (exact e4m3 -> bf16, or the bf16 itself) serves all row tiles
     f32x4 st[RT][2];
 #pragma unroll
     for (int r = 0; r < RT; ++r) st[r][0] = st[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bf16x8 k0 = fp8x8_to_bf16x8(c.k[j >> 1][2 * (j & 1)], c.k[j >> 1][2 * (j & 1) + 1]);
-      const bf16x8 k1 = fp8x8_to_bf16x8(c.k[2 + (j >> 1)][2 * (j & 1)], c.k[2 + (j >> 1)][2 * (j & 1) + 1]);
+      bf16x8 k0, k1;  // k-step j of the first and second 16-token tile
+      if constexpr (BF) {
+        k0 = __builtin_bit_cast(bf16x8, c.k[j]);
+        k1 = __builtin_bit_cast(bf16x8, c.k[4 + j]);
+      } else {
+        k0 = fp8x8_to_bf16x8(c.k[j >> 1][2 * (j & 1)], c.k[j >> 1][2 * (j & 1) + 1]);
+        k1 = fp8x8_to_bf16x8(c.k[2 + (j >> 1)][2 * (j & 1)], c.k[2 + (j >> 1)][2 * (j & 1) + 1]);
+      }
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
         if (r >= nrows) break;
@@ -385,7 +431,9 @@ __global__ __launch_bounds__(kWave * NW, (NW == 4 && NBUF <= 2 ? 2 : 1)) void pa
     // row tiles
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      const bf16x8 vop = fp8x8_to_bf16x8(c.v[d >> 1][2 * (d & 1)], c.v[d >> 1][2 * (d & 1) + 1]);
+      bf16x8 vop;  // dims 16d..16d+15 of the chunk's 32 tokens
+      if constexpr (BF) vop = __builtin_bit_cast(bf16x8, c.v[d]);
+      else vop = fp8x8_to_bf16x8(c.v[d >> 1][2 * (d & 1)], c.v[d >> 1][2 * (d & 1) + 1]);
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
         if (r >= nrows) break;
@@ -406,7 +454,7 @@ __global__ __launch_bounds__(kWave * NW, (NW == 4 && NBUF <= 2 ? 2 : 1)) void pa
       const int P = raw_at(pos, ln);
       const bool ok = valid_page(P);
       tb[k] = ok ? ln * 128 : kNoTokens;
-      load_chunk<PER_TOKEN>(buf[k], a, int64_t(P) * a.hkv + h, ok, cw, lane);
+      load_chunk<PER_TOKEN, BF>(buf[k], a, int64_t(P) * a.hkv + h, ok, cw, lane);
     }
     // raw entry of the next position to load (s0 + (NBUF-1)*S) and the
     // logical page of the one after it
@@ -422,7 +470,7 @@ __global__ __launch_bounds__(kWave * NW, (NW == 4 && NBUF <= 2 ? 2 : 1)) void pa
         const int nl = nn + (NBUF - 1) * S;
         const bool ok = valid_page(P_next);
         tb[ls] = ok ? ln_next * 128 : kNoTokens;
-        load_chunk<PER_TOKEN>(buf[ls], a, int64_t(P_next) * a.hkv + h, ok, cw, lane);
+        load_chunk<PER_TOKEN, BF>(buf[ls], a, int64_t(P_next) * a.hkv + h, ok, cw, lane);
         // table reads for the following steps (checked one step later)
         ln_next = ln_after;
         P_next = raw_at(nl + S, ln_next);
@@ -601,27 +649,33 @@ __global__ __launch_bounds__(256) void pa_merge(DecodeArgs a) {
 
 // With events, the dispatch itself records them (start and end of this
 // kernel), so the measured time is the kernel's own, without marker packets.
-template <int RT, bool PT, bool SP, int NB, int NW>
+template <int RT, bool PT, bool SP, int NB, int NW, bool BF>
 void launch_main_t(const DecodeArgs& a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (e0 || e1)
-    hipExtLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB, NW>), dim3(uint32_t(grid)), dim3(kWave * NW), 0,
-                          s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB, NW, BF>), dim3(uint32_t(grid)), dim3(kWave * NW),
+                          0, s, e0, e1, 0, a);
   else
-    hipLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB, NW>), dim3(uint32_t(grid)), dim3(kWave * NW), 0, s,
-                       a);
+    hipLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB, NW, BF>), dim3(uint32_t(grid)), dim3(kWave * NW), 0,
+                       s, a);
 }
 
 // prefetch depth and workgroup width: eight waves (two pages side by side)
 // use the two-page ring; deeper rings are a four-wave tuning option.
-template <int RT, bool PT, bool SP>
+// A bf16 cache (twice the bytes per chunk) always uses the two-page ring,
+// and four waves when a workgroup carries two rows.
+template <int RT, bool PT, bool SP, bool BF = false>
 void launch_shape(const DecodeArgs& a, int depth, int waves, int64_t grid, hipStream_t s, hipEvent_t e0,
                   hipEvent_t e1) {
-  if (waves == 8) return launch_main_t<RT, PT, SP, 2, 8>(a, grid, s, e0, e1);
-  if constexpr (!SP) {
-    if (depth == 3) return launch_main_t<RT, PT, SP, 3, 4>(a, grid, s, e0, e1);
-    if (depth >= 4) return launch_main_t<RT, PT, SP, 4, 4>(a, grid, s, e0, e1);
+  if constexpr (BF && RT == 2) {
+    launch_main_t<RT, PT, SP, 2, 4, BF>(a, grid, s, e0, e1);
+  } else {
+    if (waves == 8) return launch_main_t<RT, PT, SP, 2, 8, BF>(a, grid, s, e0, e1);
+    if constexpr (!SP && !BF) {
+      if (depth == 3) return launch_main_t<RT, PT, SP, 3, 4, BF>(a, grid, s, e0, e1);
+      if (depth >= 4) return launch_main_t<RT, PT, SP, 4, 4, BF>(a, grid, s, e0, e1);
+    }
+    launch_main_t<RT, PT, SP, 2, 4, BF>(a, grid, s, e0, e1);
   }
-  launch_main_t<RT, PT, SP, 2, 4>(a, grid, s, e0, e1);
 }
 
 }  // namespace
@@ -631,10 +685,15 @@ hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool spa
   if (grid <= 0) return hipSuccess;
   const bool pt = a.scale_mode == PA_SCALE_PER_TOKEN;
   hipEvent_t e0 = ev_begin, e1 = ev_end;
-  // the one variant-selection table: (rows per group, per-token scales,
-  // sparse, prefetch depth, waves per workgroup)
+  // the one variant-selection table: (cache element type, rows per group,
+  // per-token scales, sparse, prefetch depth, waves per workgroup)
   const int d = depth, w = waves;
-  if (sparse) {
+  if (a.kv_bf16) {
+    // unquantized cache: never scaled
+    if (sparse) launch_shape<1, false, true, true>(a, d, w, grid, stream, e0, e1);
+    else if (a.rt == 1) launch_shape<1, false, false, true>(a, d, w, grid, stream, e0, e1);
+    else launch_shape<2, false, false, true>(a, d, w, grid, stream, e0, e1);
+  } else if (sparse) {
     if (pt) launch_shape<1, true, true>(a, d, w, grid, stream, e0, e1);
     else launch_shape<1, false, true>(a, d, w, grid, stream, e0, e1);
   } else if (a.rt == 1) {

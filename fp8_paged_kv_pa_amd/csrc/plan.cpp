@@ -27,11 +27,13 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
   if (c.num_kv_heads < 1 || c.num_kv_heads > kMaxKvHeads)
     return fail(err, PA_ERR_UNSUPPORTED, "num_kv_heads must be in [1, 64], got " +
                                              std::to_string(c.num_kv_heads));
-  if (c.kv_dtype != PA_DTYPE_U8 && c.kv_dtype != PA_DTYPE_F8E4M3)
-    return fail(err, PA_ERR_DTYPE, "KV cache must be uint8 or float8_e4m3fn bytes");
+  if (c.kv_dtype != PA_DTYPE_U8 && c.kv_dtype != PA_DTYPE_F8E4M3 && c.kv_dtype != PA_DTYPE_BF16)
+    return fail(err, PA_ERR_DTYPE, "KV cache must be uint8 / float8_e4m3fn bytes or bfloat16");
   if (c.scale_mode != PA_SCALE_NONE && c.scale_mode != PA_SCALE_SCALAR &&
       c.scale_mode != PA_SCALE_PER_TOKEN)
     return fail(err, PA_ERR_INVALID_ARG, "unknown scale_mode " + std::to_string(c.scale_mode));
+  if (c.kv_dtype == PA_DTYPE_BF16 && c.scale_mode != PA_SCALE_NONE)
+    return fail(err, PA_ERR_UNSUPPORTED, "a bfloat16 cache is unquantized: scale_mode must be PA_SCALE_NONE");
   if (c.rows < 0 || c.batch < 1 || c.max_pages < 1 || c.topk < 0)
     return fail(err, PA_ERR_SHAPE, "rows >= 0, batch >= 1, block-table width >= 1, topk >= 0 required");
   if (c.rows > kMaxRows)
@@ -55,6 +57,7 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
 
   Plan p;
   p.sparse = c.topk > 0;
+  p.bf16kv = c.kv_dtype == PA_DTYPE_BF16;
   const int64_t hkv = c.num_kv_heads;
   int64_t npages;
   if (p.sparse) {

@@ -48,6 +48,7 @@ struct Plan {
   int depth = 2;           // pages of KV in flight per wave (chunk-buffer ring)
   int waves = 4;           // waves per workgroup: 4 (one page at a time) or 8 (two side by side)
   bool sparse = false;
+  bool bf16kv = false;     // unquantized bf16 cache (32 KiB per page and head)
   bool merge = false;
   int64_t units = 0;       // dense: batch*Hkv*groups; sparse: rows*Hkv
   int64_t grid = 0;        // main-kernel workgroups (1-D)

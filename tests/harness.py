@@ -21,9 +21,15 @@ POISON_SCALE = 1e3
 
 def poison_arrays(w, nb=None):
     """Initial cache contents: random finite e4m3 codes and scales of 1e3,
-    so a read of anything the call should not touch shows in the output."""
+    so a read of anything the call should not touch shows in the output.
+    A bf16 cache gets random 16-bit patterns, NaN and infinities included:
+    a slot past the context that leaks into the output shows as non-finite."""
     nb = w.num_blocks if nb is None else nb
     rng = np.random.default_rng(w.seed + 99)
+    if w.kv_dtype == "bf16":
+        kc = rng.integers(0, 1 << 16, size=nb * w.Hkv * 16384, dtype=np.uint16)
+        vc = rng.integers(0, 1 << 16, size=nb * w.Hkv * 16384, dtype=np.uint16)
+        return kc, vc, None, None
     kc = rng.integers(0, 0x7F, size=nb * w.Hkv * 16384, dtype=np.uint8)
     vc = rng.integers(0, 0x7F, size=nb * w.Hkv * 16384, dtype=np.uint8)
     ks = np.full(nb * w.Hkv * 128, POISON_SCALE, dtype=np.float32)
@@ -38,7 +44,21 @@ class GpuCase:
         self.w = w
         self.dev = torch.device(device)
         nb, Hkv = w.num_blocks, w.Hkv
-        if poison:
+        if w.kv_dtype == "bf16":
+            # poison drawn on the device (a 128K-context bf16 cache is GiBs):
+            # every 16-bit pattern, NaN and infinities included
+            kv_dtype = torch.bfloat16
+            self.kc = torch.zeros(nb, Hkv, 16384, dtype=torch.int16, device=self.dev)
+            self.vc = torch.zeros_like(self.kc)
+            if poison:
+                g = torch.Generator(device=self.dev)
+                g.manual_seed(w.seed + 99)
+                for t in (self.kc, self.vc):
+                    t.random_(-32768, 32768, generator=g)
+            self.kc = self.kc.view(torch.bfloat16)
+            self.vc = self.vc.view(torch.bfloat16)
+            self.ks = self.vs = None
+        elif poison:
             kc, vc, ks, vs = poison_arrays(w)
             self.kc = torch.from_numpy(kc).to(self.dev).view(nb, Hkv, 16384)
             self.vc = torch.from_numpy(vc).to(self.dev).view(nb, Hkv, 16384)
@@ -94,6 +114,11 @@ def oracle_cache(w):
     """The oracle's cache for a (small) workload: poison, then every written
     page through the reference writer."""
     kc, vc, ks, vs = poison_arrays(w)
+    if w.kv_dtype == "bf16":
+        for b in range(w.B):
+            k, v, s = w.request_kv(b)
+            owr.write_bf16_ref(k, v, s, kc, vc, w.Hkv)
+        return kc, vc, None, None, None, None
     ks_in = np.array([w.k_scalar], np.float32)
     vs_in = np.array([w.v_scalar], np.float32)
     for b in range(w.B):
@@ -113,7 +138,7 @@ def oracle_out(w, cache=None, rows_subset=None, sm_scale=None):
     cache = oracle_cache(w) if cache is None else cache
     kc, vc, _, _, ksa, vsa = cache
     return oatt.attention_ref(w.q, kc, vc, ksa, vsa, w.block_table, w.ctx, w.cu, w.sparse, w.mode,
-                              w.Hkv, sm_scale=sm_scale, rows_subset=rows_subset)
+                              w.Hkv, sm_scale=sm_scale, rows_subset=rows_subset, kv_dtype=w.kv_dtype)
 
 
 def compact_request_oracle(w, b, rows):
@@ -122,7 +147,8 @@ def compact_request_oracle(w, b, rows):
     pages = [int(n) for n in w.written[b]]
     nb = len(pages)
     Hkv = w.Hkv
-    kc = np.zeros(nb * Hkv * 16384, np.uint8)
+    bf = w.kv_dtype == "bf16"
+    kc = np.zeros(nb * Hkv * 16384, np.uint16 if bf else np.uint8)
     vc = np.zeros_like(kc)
     ks = np.zeros(nb * Hkv * 128, np.float32)
     vs = np.zeros_like(ks)
@@ -133,7 +159,9 @@ def compact_request_oracle(w, b, rows):
         bt[0, n] = ci
         k, v = w.page_kv(b, n)
         slots = ci * 128 + np.arange(k.shape[0], dtype=np.int64)
-        if w.mode == wl.SCALAR:
+        if bf:
+            owr.write_bf16_ref(k, v, slots, kc, vc, Hkv)
+        elif w.mode == wl.SCALAR:
             owr.quant_write_ref(k, v, slots, kc, vc, ks_in, vs_in, w.mode, Hkv)
         else:
             owr.quant_write_ref(k, v, slots, kc, vc, ks, vs, w.mode, Hkv)
@@ -145,7 +173,7 @@ def compact_request_oracle(w, b, rows):
     ksa, vsa = (ks_in, vs_in) if w.mode == wl.SCALAR else ((None, None) if w.mode == wl.NONE else (ks, vs))
     sel = [r - start for r in rows]
     return oatt.attention_ref(q, kc, vc, ksa, vsa, bt, w.ctx[b:b + 1], cu, sp, w.mode, Hkv,
-                              rows_subset=sel)
+                              rows_subset=sel, kv_dtype=w.kv_dtype)
 
 
 def compare(gpu_bf16, ref64, atol=1e-2, cos_min=0.9999, what=""):

@@ -51,8 +51,12 @@ int main() {
     CHECK(make_plan(c, &p, &err) == PA_ERR_UNSUPPORTED, "dim");
     c = base(); c.page_size = 16;
     CHECK(make_plan(c, &p, &err) == PA_ERR_UNSUPPORTED, "page");
-    c = base(); c.kv_dtype = PA_DTYPE_BF16;
+    c = base(); c.kv_dtype = PA_DTYPE_F32;
     CHECK(make_plan(c, &p, &err) == PA_ERR_DTYPE, "dtype");
+    c = base(); c.kv_dtype = PA_DTYPE_BF16;  // unquantized cache: scales refused
+    CHECK(make_plan(c, &p, &err) == PA_ERR_UNSUPPORTED, "bf16 with scales");
+    c.scale_mode = PA_SCALE_NONE;
+    CHECK(make_plan(c, &p, &err) == PA_OK && p.bf16kv, "bf16 without scales");
     c = base(); c.scale_mode = 9;
     CHECK(make_plan(c, &p, &err) == PA_ERR_INVALID_ARG, "mode");
     c = base(); c.rows = 121; c.batch = 31;

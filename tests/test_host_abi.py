@@ -49,13 +49,25 @@ def cfg(**kw):
 
 @pytest.mark.parametrize("field,value,status", [
     ("group_size", 8, -5), ("head_dim", 64, -5), ("page_size", 16, -5),
-    ("num_kv_heads", 0, -5), ("kv_dtype", 3, -2), ("scale_mode", 7, -1),
+    ("num_kv_heads", 0, -5), ("kv_dtype", 4, -2), ("scale_mode", 7, -1),
 ])
 def test_geometry_refused_up_front(field, value, status):
     c = cfg()
     setattr(c, field, value)
     assert pa.pa_query_support(c) == status
     assert pa.pa_last_error()
+
+
+def test_bf16_cache_only_without_scales():
+    """The unquantized bf16 cache is served with scale_mode NONE only."""
+    assert pa.pa_query_support(cfg(kv_dtype=3, scale_mode=pa.SCALE_NONE)) == 0
+    assert pa.pa_query_support(cfg(kv_dtype=3, scale_mode=pa.SCALE_PER_TOKEN)) == -5
+    assert "unquantized" in pa.pa_last_error()
+    assert pa.pa_query_support(cfg(kv_dtype=3, scale_mode=pa.SCALE_SCALAR)) == -5
+    # same plan and scratch as the FP8 cache of the same shape
+    a = pa.pa_plan_describe(cfg(kv_dtype=3, scale_mode=pa.SCALE_NONE, rows=124, batch=31, max_pages=256))
+    b = pa.pa_plan_describe(cfg(rows=124, batch=31, max_pages=256))
+    assert a == b
 
 
 def test_non_divisible_rows_without_cu_is_refused():
@@ -150,10 +162,25 @@ def _call_decode(t):
     (dict(q=_host_tensor((6, 16, 128), torch.bfloat16), out=_host_tensor((6, 16, 128), torch.bfloat16)), -3),
     (dict(q=_host_tensor((4, 16, 130), torch.bfloat16)[:, :, :128]), -4),
     (dict(mode=5), -1),
+    # bf16 caches: 16384 elements per block, no scales, both caches alike
+    (dict(k=_host_tensor((8, 1, 16384), torch.bfloat16), v=_host_tensor((8, 1, 16384), torch.bfloat16)), -5),
+    (dict(k=_host_tensor((8, 1, 16384), torch.bfloat16)), -2),
+    (dict(k=_host_tensor((8, 1, 8192), torch.bfloat16), v=_host_tensor((8, 1, 8192), torch.bfloat16),
+          mode=0), -3),
 ])
 def test_decode_refuses_bad_descriptors_before_launch(over, status):
     assert _call_decode(_decode_args(**over)) == status
     assert pa.pa_last_error()
+
+
+def test_decode_accepts_bf16_cache_descriptors_on_the_host():
+    """A well-formed bf16-cache call passes every host check; with zero
+    rows nothing is launched, so this runs without a GPU."""
+    t = _decode_args(q=_host_tensor((0, 16, 128), torch.bfloat16),
+                     out=_host_tensor((0, 16, 128), torch.bfloat16),
+                     k=_host_tensor((8, 1, 16384), torch.bfloat16),
+                     v=_host_tensor((8, 1, 16384), torch.bfloat16), ks=None, vs=None, mode=0)
+    assert _call_decode(t) == 0, pa.pa_last_error()
 
 
 def test_write_refuses_bad_descriptors_before_launch():
@@ -168,3 +195,16 @@ def test_write_refuses_bad_descriptors_before_launch():
     d = [_lib.desc(x) for x in (k2, k2, _host_tensor((3,), torch.int64), kc, kc, ks, ks)]
     assert lib.kv_quant_write(*[_lib.ref(x) for x in d], 2, None) == -3
     assert "KV heads" in pa.pa_last_error()
+
+
+def test_write_to_bf16_cache_refuses_scales():
+    lib = pa.load()
+    k = _host_tensor((3, 1, 128), torch.float32)
+    slots = _host_tensor((3,), torch.int64)
+    kc = _host_tensor((2, 1, 16384), torch.bfloat16)
+    ks = _host_tensor((2, 1, 128), torch.float32)
+    d = [_lib.desc(x) for x in (k, k, slots, kc, kc, ks, ks)]
+    assert lib.kv_quant_write(*[_lib.ref(x) for x in d], 2, None) == -5
+    u8 = _host_tensor((2, 1, 16384), torch.uint8)
+    d = [_lib.desc(x) for x in (k, k, slots, kc, u8, ks, ks)]
+    assert lib.kv_quant_write(*[_lib.ref(x) for x in d], 0, None) == -2

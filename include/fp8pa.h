@@ -41,6 +41,15 @@
  *          4096*c + 1024*(delta/2) + 16*(16*g + r) + 8*(delta%2) + e
  *     so each 32-token chunk is one contiguous 4 KiB run and every aligned
  *     16-byte piece is one lane's matrix-core operand.
+ *   Unquantized control (the BF16 KV cache the FP8 cache is compared
+ *   against, [ATOM-2710] "Test Result"): k_cache, v_cache bfloat16
+ *     [num_blocks, Hkv, 16384] contiguous, block (p, h) at element
+ *     (p*Hkv + h)*16384, element offsets with the same c, tau, r, j, g, u,
+ *     w, e, delta as above:
+ *       K: 4096*c + 512*(4*tau + j) + 8*(16*g + r) + u
+ *       V: 4096*c + 512*delta + 8*(16*g + r) + e
+ *     (each 32-token chunk one 8 KiB run, each 16-byte piece one operand).
+ *     A bf16 cache has no scales: scale_mode must be PA_SCALE_NONE.
  *   k_scale, v_scale:
  *     PA_SCALE_PER_TOKEN: float32 [num_blocks, Hkv, 128] contiguous, the
  *       scale of (page, KV head, token slot) ([ATOM-2614] "Problem": one
@@ -124,7 +133,8 @@ typedef struct pa_decode_opts {
                            /* flight per wave (tuning; depths above 2 apply   */
                            /* to dense calls with 4-wave workgroups)          */
   int32_t workgroup_waves; /* 0 => plan chooses; 4 (a workgroup streams one   */
-                           /* page at a time) or 8 (two pages side by side)   */
+                           /* page at a time) or 8 (two pages side by side;   */
+                           /* two-row calls over a bf16 cache always use 4)   */
 } pa_decode_opts;
 
 /* Host-side description of a decode call, for capability queries, planning
@@ -134,7 +144,8 @@ typedef struct pa_config {
   int32_t group_size;      /* query heads per KV head: must be 16            */
   int32_t head_dim;        /* must be 128                                    */
   int32_t page_size;       /* must be 128                                    */
-  int32_t kv_dtype;        /* PA_DTYPE_U8 or PA_DTYPE_F8E4M3                 */
+  int32_t kv_dtype;        /* PA_DTYPE_U8, PA_DTYPE_F8E4M3, or PA_DTYPE_BF16 */
+                           /* (unquantized; scale_mode must be NONE)         */
   int32_t scale_mode;      /* pa_scale_mode                                  */
   int64_t rows;            /* query rows (sum of q_len)                      */
   int64_t batch;           /* requests                                       */
@@ -170,8 +181,9 @@ typedef struct pa_plan_info {
  *   q             bf16 [rows, 16*Hkv, 128], last dim contiguous, 16-byte
  *                 aligned rows.
  *   k_cache,
- *   v_cache       u8/f8e4m3 [num_blocks, Hkv, 16384] contiguous (layout
- *                 above), num_blocks >= 1.
+ *   v_cache       u8/f8e4m3 (or bf16, unquantized) [num_blocks, Hkv, 16384]
+ *                 contiguous (layouts above), both of one dtype,
+ *                 num_blocks >= 1.
  *   k_scale,
  *   v_scale       see "scale" above, per scale_mode.
  *   block_table   int32 [batch, W]: physical page of each logical page.  Only
@@ -217,7 +229,10 @@ int pa_decode_ex(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* 
  *   k_new, v_new  f32 or bf16 [T, Hkv, 128], last dim contiguous.
  *   slot_mapping  int64 [T]: page*128 + token slot; negative => skip the
  *                 token; a slot past the cache is skipped too.
- *   k_cache, v_cache  as in pa_decode (written at the named slots only).
+ *   k_cache, v_cache  as in pa_decode (written at the named slots only).  A
+ *                 bf16 cache stores each value rounded to bf16 (nearest,
+ *                 ties to even; bf16 inputs unchanged; NaN stays NaN, quiet,
+ *                 sign kept) and takes scale_mode NONE only.
  *   k_scale, v_scale  PER_TOKEN: outputs, f32 [num_blocks, Hkv, 128], scale =
  *                 fl32(amax/448) of the token's 128 values (an all-zero row
  *                 stores 0).  SCALAR: inputs, one f32 each, > 0.  NONE: unused.

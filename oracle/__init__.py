@@ -21,6 +21,9 @@ What it computes is the plain definition, written out slowly and in fp64:
                    for single-row, uniform multi-row, ragged and
                    block-sparse decode, plus the split-K partial/merge form
                    used only to pin the merge identity.
+* ``indexer``   -- the sparse indexer that produces the block-sparse page
+                   lists: per-page log2-sum-exp block scores over the fp8
+                   index cache, and the per-row top-k rule.
 
 Sources (web pages about serving MiniMax-M3 with an FP8 KV cache on AMD
 GPUs):
@@ -30,11 +33,12 @@ GPUs):
 * ROCm/ATOM pull request 2710 (FlyDSL paged decode on gfx1250) and its
   review: split-K scratch shapes and capacity buckets ("Must fix" item 1).
 * ROCm/ATOM pull request 2122, "fix(minimax-m3): unblock fp8 KV cache and
-  EAGLE3 spec decode on the vLLM plugin": section 2 gives the multi-row
-  causal cutoff and the ragged-segment rule.
+  EAGLE3 spec decode on the vLLM plugin": section 1 gives the fp8 index
+  cache and the block-score product, section 2 the multi-row causal cutoff
+  and the ragged-segment rule.
 * vllm-project/vllm pull request 52060, "[ROCm][Perf] Fold scalar KV scales
   in MiniMax-M3 sparse attention": section "Suggested Fix" gives the scalar
   scale fold; "Test Plan" compares against a dequantized reference.
 """
 
-from . import bf16, e4m3, layout, writer, attention  # noqa: F401
+from . import bf16, e4m3, layout, writer, attention, indexer  # noqa: F401

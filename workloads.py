@@ -115,6 +115,44 @@ class Workload:
                 np.stack(vs) if vs else np.zeros((0, self.Hkv, DIM), np.float32),
                 np.asarray(ss, dtype=np.int64))
 
+    # ---- sparse-indexer inputs (index keys and index queries) -------------
+    def index_page_codes(self, b: int, n: int) -> np.ndarray:
+        """uint8 [cnt, 128] index-key codes of the valid tokens of logical
+        page n of request b: random sign, magnitude code uniform in
+        [0x28, 0x40) (e4m3fn magnitudes 0.25 .. 1.875).  Random bytes only."""
+        cnt = int(min(PAGE, int(self.ctx[b]) - n * PAGE))
+        g = np.random.default_rng([self.seed, 11, b, n])
+        mag = g.integers(0x28, 0x40, size=(cnt, DIM), dtype=np.uint8)
+        sign = g.integers(0, 2, size=(cnt, DIM), dtype=np.uint8) << 7
+        return mag | sign
+
+    def index_queries(self) -> np.ndarray:
+        """float32 (bf16-exact) [rows, 128] index queries."""
+        g = np.random.default_rng([self.seed, 13])
+        return bf16_round(g.standard_normal((self.rows, DIM), dtype=np.float32))
+
+    def index_cache(self, poison: bool = True, num_blocks: Optional[int] = None,
+                    page_map=None) -> np.ndarray:
+        """Flat uint8 index cache of shape (num_blocks, 128, 128), token-major:
+        every page of every context filled, the rest random bytes (NaN codes
+        included) or zero.  page_map: optional {(b, n): physical page} to
+        build a compact cache instead of using the block table."""
+        nb = self.num_blocks if num_blocks is None else num_blocks
+        if poison:
+            cache = np.random.default_rng([self.seed, 17]).integers(0, 256, size=nb * PAGE * DIM,
+                                                                     dtype=np.uint8)
+        else:
+            cache = np.zeros(nb * PAGE * DIM, np.uint8)
+        view = cache.reshape(nb, PAGE, DIM)
+        for b in range(self.B):
+            npages = min((int(self.ctx[b]) + PAGE - 1) // PAGE, self.W)
+            for n in range(npages):
+                P = int(self.block_table[b, n]) if page_map is None else page_map.get((b, n), -1)
+                if 0 <= P < nb:
+                    codes = self.index_page_codes(b, n)
+                    view[P, :codes.shape[0]] = codes
+        return cache
+
     def kv_bytes_attended(self) -> int:
         """Algorithmic KV bytes one decode call must read: every distinct
         (request, KV head, attended token) once, 256 code bytes plus 8 scale
@@ -254,3 +292,21 @@ def bf16_kv(w: Workload) -> Workload:
     """The same workload over an unquantized bf16 cache (no scales): the
     same queries, contexts, tables and K/V draws."""
     return replace(w, name=w.name + "_bf16", kv_dtype="bf16", mode=NONE)
+
+
+def index_workload(kind="c5"):
+    """Sparse-indexer shapes.  'c5': the block-sparse decode shape (batch 16,
+    q_len 1, context 131072, 16384-page pool) with top-32 over all 1024
+    pages; 'spec': 31 requests with q_len 4, contexts in [4096, 32768],
+    top-32; 'ragged': the same requests with q_lens 4 except one request of
+    1 row."""
+    if kind == "c5":
+        w = _make("index_c5", 20266, [131072] * 16, [1] * 16, 1, 16384, False)
+    else:
+        rng = np.random.default_rng(20267 + 100000)
+        ctx = rng.integers(4096, 32769, size=31)
+        ql = np.full(31, 4)
+        if kind == "ragged":
+            ql[int(rng.integers(0, 31))] = 1
+        w = _make("index_" + kind, 20267, ctx, ql, 1, 8192, kind == "ragged", W=256)
+    return w

@@ -62,6 +62,17 @@ def kv_quant_write(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scal
     check(lib.kv_quant_write(*[ref(x) for x in d], int(scale_mode), stream_handle(stream)))
 
 
+def pa_index_topk(q_idx, index_cache, block_table, context_lens, cu_seqlens_q, sparse_page_idx,
+                  block_scores, sm_scale=0.0, max_q_len=0, stream=None):
+    """Block scores and per-row top-k pages (see ``pa_index_topk`` in include/fp8pa.h)."""
+    lib = load()
+    d = [desc(t) for t in (q_idx, index_cache, block_table, context_lens, cu_seqlens_q)]
+    ds, db = desc(sparse_page_idx), desc(block_scores)
+    check(lib.pa_index_topk(*[ref(x) for x in d], int(max_q_len), float(sm_scale), ref(ds), ref(db),
+                            stream_handle(stream)))
+    return sparse_page_idx
+
+
 def make_config(num_kv_heads, rows, batch, max_pages, topk=0, ragged=False, max_q_len=0,
                 scale_mode=SCALE_PER_TOKEN, kv_dtype=1, force_parts=0, group_size=GROUP_SIZE,
                 head_dim=HEAD_DIM, page_size=PAGE_SIZE):

@@ -92,7 +92,7 @@ class PaPlanInfo(ctypes.Structure):
     ]
 
 
-EXPORTS = ("pa_decode", "pa_decode_ex", "kv_quant_write", "pa_query_support",
+EXPORTS = ("pa_decode", "pa_decode_ex", "kv_quant_write", "pa_index_topk", "pa_query_support",
            "pa_plan_describe", "pa_reserve", "pa_release", "pa_last_error")
 
 _lib = None
@@ -116,6 +116,8 @@ def load():
     lib.pa_decode_ex.restype = ctypes.c_int
     lib.kv_quant_write.argtypes = [T, T, T, T, T, T, T, ctypes.c_int, vp]
     lib.kv_quant_write.restype = ctypes.c_int
+    lib.pa_index_topk.argtypes = [T, T, T, T, T, ctypes.c_int, ctypes.c_float, T, T, vp]
+    lib.pa_index_topk.restype = ctypes.c_int
     lib.pa_query_support.argtypes = [P(PaConfig)]
     lib.pa_query_support.restype = ctypes.c_int
     lib.pa_plan_describe.argtypes = [P(PaConfig), P(PaPlanInfo)]

@@ -10,6 +10,7 @@
 // and scratch shapes, allocated where the memory accounting can see them).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -355,6 +356,102 @@ int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tens
   a.hkv = int32_t(hkv);
   a.scale_mode = scale_mode;
   hipError_t he = launch_write(a, reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return fail(PA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(he));
+  return PA_OK;
+}
+
+int pa_index_topk(const pa_tensor* q_idx, const pa_tensor* index_cache, const pa_tensor* block_table,
+                  const pa_tensor* context_lens, const pa_tensor* cu_seqlens_q, int max_q_len, float sm_scale,
+                  pa_tensor* sparse_page_idx, pa_tensor* block_scores, void* stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_tensor(q_idx, "q_idx"))) return rc;
+  if (q_idx->dtype != PA_DTYPE_BF16) return fail(PA_ERR_DTYPE, "q_idx must be bfloat16");
+  if (q_idx->ndim != 2 || q_idx->shape[1] != kDim)
+    return fail(PA_ERR_SHAPE, "q_idx must be [rows, 128]");
+  const int64_t rows = q_idx->shape[0];
+  if (q_idx->stride[1] != 1 || q_idx->stride[0] % 8 || !aligned(q_idx->data, 16))
+    return fail(PA_ERR_LAYOUT, "q_idx: last dim contiguous, row stride a multiple of 8, 16-byte aligned");
+  if ((rc = check_tensor(index_cache, "index_cache"))) return rc;
+  if (index_cache->dtype != PA_DTYPE_U8 && index_cache->dtype != PA_DTYPE_F8E4M3)
+    return fail(PA_ERR_DTYPE, "index_cache must be uint8 or float8_e4m3fn");
+  if (index_cache->ndim < 2) return fail(PA_ERR_SHAPE, "index_cache must be [num_blocks, 128, 128]");
+  int64_t inner = 1;
+  for (int i = 1; i < index_cache->ndim; ++i) inner *= index_cache->shape[i];
+  if (inner != kBlockBytes) return fail(PA_ERR_SHAPE, "index_cache: each page must hold 128 x 128 bytes");
+  if (!contiguous(index_cache) || !aligned(index_cache->data, 16))
+    return fail(PA_ERR_LAYOUT, "index_cache must be contiguous and 16-byte aligned");
+  const int64_t nb = index_cache->shape[0];
+  if (nb < 1) return fail(PA_ERR_SHAPE, "the index cache must hold at least one page");
+
+  if ((rc = check_tensor(block_table, "block_table"))) return rc;
+  if (block_table->dtype != PA_DTYPE_I32 || block_table->ndim != 2)
+    return fail(PA_ERR_DTYPE, "block_table must be int32 [batch, W]");
+  if (block_table->stride[1] != 1) return fail(PA_ERR_LAYOUT, "block_table rows must be contiguous");
+  const int64_t B = block_table->shape[0], W = block_table->shape[1];
+  if (B < 1 || W < 1) return fail(PA_ERR_SHAPE, "block_table needs batch >= 1 and width >= 1");
+  if ((rc = check_tensor(context_lens, "context_lens"))) return rc;
+  if (context_lens->dtype != PA_DTYPE_I32 || context_lens->ndim != 1 || context_lens->shape[0] != B ||
+      (B > 1 && context_lens->stride[0] != 1))
+    return fail(PA_ERR_SHAPE, "context_lens must be contiguous int32 [batch]");
+  const bool ragged = cu_seqlens_q != nullptr && cu_seqlens_q->data != nullptr;
+  if (ragged) {
+    if ((rc = check_tensor(cu_seqlens_q, "cu_seqlens_q"))) return rc;
+    if (cu_seqlens_q->dtype != PA_DTYPE_I32 || cu_seqlens_q->ndim != 1 || cu_seqlens_q->shape[0] != B + 1 ||
+        cu_seqlens_q->stride[0] != 1)
+      return fail(PA_ERR_SHAPE, "cu_seqlens_q must be contiguous int32 [batch + 1]");
+  } else if (rows % B != 0) {
+    return fail(PA_ERR_SHAPE, "rows " + std::to_string(rows) + " not divisible by batch " + std::to_string(B) +
+                                  " and no cu_seqlens_q: a ragged segment needs cu_seqlens_q");
+  }
+  if (max_q_len < 0) return fail(PA_ERR_INVALID_ARG, "max_q_len must be >= 0");
+  if ((rc = check_tensor(sparse_page_idx, "sparse_page_idx"))) return rc;
+  if (sparse_page_idx->dtype != PA_DTYPE_I32 || sparse_page_idx->ndim != 2 || sparse_page_idx->shape[0] != rows ||
+      sparse_page_idx->stride[1] != 1)
+    return fail(PA_ERR_SHAPE, "sparse_page_idx must be int32 [rows, topk] with contiguous rows");
+  const int64_t topk = sparse_page_idx->shape[1];
+  if (topk < 1) return fail(PA_ERR_SHAPE, "topk must be >= 1");
+  if (rows > 1 && sparse_page_idx->stride[0] < topk)
+    return fail(PA_ERR_LAYOUT, "sparse_page_idx rows must not overlap");
+  if ((rc = check_tensor(block_scores, "block_scores"))) return rc;
+  if (block_scores->dtype != PA_DTYPE_F32 || block_scores->ndim != 2 || block_scores->shape[0] != rows ||
+      block_scores->shape[1] != W || block_scores->stride[1] != 1)
+    return fail(PA_ERR_SHAPE, "block_scores must be float32 [rows, W] with contiguous rows");
+  if (rows > 1 && block_scores->stride[0] < W) return fail(PA_ERR_LAYOUT, "block_scores rows must not overlap");
+  if (rows > kMaxRows) return fail(PA_ERR_CAPACITY, "rows above " + std::to_string(kMaxRows));
+  if (B > kMaxBatch) return fail(PA_ERR_CAPACITY, "batch above " + std::to_string(kMaxBatch));
+  if (W > kMaxPages) return fail(PA_ERR_CAPACITY, "block-table width above " + std::to_string(kMaxPages));
+  if (topk > kMaxTopk) return fail(PA_ERR_CAPACITY, "topk above " + std::to_string(kMaxTopk));
+  int64_t lmax = ragged ? (max_q_len > 0 ? std::min<int64_t>(max_q_len, rows) : rows) : rows / B;
+  lmax = std::max<int64_t>(lmax, 1);
+  const int64_t groups = (lmax + 15) / 16;
+  const int64_t grid = index_score_grid(B * groups, int32_t(W));
+  if (grid > int64_t(0x7FFFFFFF))
+    return fail(PA_ERR_CAPACITY, "batch x 16-row groups x pages exceeds one launch; give max_q_len");
+  if (rows == 0) return PA_OK;
+
+  IndexArgs a{};
+  a.q = static_cast<const uint16_t*>(q_idx->data);
+  a.q_row_stride = q_idx->stride[0];
+  a.index_cache = static_cast<const uint8_t*>(index_cache->data);
+  a.num_blocks = nb;
+  a.block_table = static_cast<const int32_t*>(block_table->data);
+  a.bt_stride = block_table->stride[0];
+  a.context_lens = static_cast<const int32_t*>(context_lens->data);
+  a.cu_seqlens_q = ragged ? static_cast<const int32_t*>(cu_seqlens_q->data) : nullptr;
+  a.scores = static_cast<float*>(block_scores->data);
+  a.score_stride = block_scores->stride[0];
+  a.out_idx = static_cast<int32_t*>(sparse_page_idx->data);
+  a.out_stride = sparse_page_idx->stride[0];
+  a.rows = int32_t(rows);
+  a.batch = int32_t(B);
+  a.width = int32_t(W);
+  a.topk = int32_t(topk);
+  a.uniform_q_len = ragged ? 0 : int32_t(rows / B);
+  a.groups = int32_t(groups);
+  const float sm = sm_scale != 0.0f ? sm_scale : 1.0f / std::sqrt(float(kDim));
+  a.sm_log2 = sm * 1.4426950408889634f;
+  hipError_t he = launch_index(a, grid, reinterpret_cast<hipStream_t>(stream));
   if (he != hipSuccess) return fail(PA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(he));
   return PA_OK;
 }

@@ -64,10 +64,36 @@ struct WriteArgs {
   int32_t scale_mode;
 };
 
+// Arguments of the sparse-indexer kernels (block scores, then top-k).
+struct IndexArgs {
+  const uint16_t* q;          // bf16 [rows, 128] index queries
+  int64_t q_row_stride;       // elements
+  const uint8_t* index_cache; // e4m3fn [num_blocks, 128 tokens, 128 dims], token-major
+  int64_t num_blocks;
+  const int32_t* block_table; // [batch, W]
+  int64_t bt_stride;
+  const int32_t* context_lens;  // [batch]
+  const int32_t* cu_seqlens_q;  // [batch+1] or null (uniform)
+  float* scores;              // f32 [rows, W] (output and work buffer)
+  int64_t score_stride;
+  int32_t* out_idx;           // int32 [rows, topk]
+  int64_t out_stride;
+  int32_t rows;
+  int32_t batch;
+  int32_t width;              // W
+  int32_t topk;
+  int32_t uniform_q_len;      // rows/batch when cu_seqlens_q is null
+  int32_t groups;             // 16-row groups per request
+  float sm_log2;              // sm_scale * log2(e)
+};
+
 // Launchers (defined with their kernels).  Return hipSuccess or the launch
 // error.
 hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool sparse, int depth, int waves,
                          hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_index(const IndexArgs& a, int64_t score_grid, hipStream_t stream);
+// Workgroups of the block-score kernel for `units` (request, 16-row group) pairs.
+int64_t index_score_grid(int64_t units, int32_t width);
 
 }  // namespace fp8pa

@@ -245,6 +245,41 @@ int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new,
                    const pa_tensor* slot_mapping, pa_tensor* k_cache, pa_tensor* v_cache,
                    pa_tensor* k_scale, pa_tensor* v_scale, int scale_mode, void* stream);
 
+/*
+ * pa_index_topk -- the sparse indexer that produces sparse_page_idx for the
+ * block-sparse pa_decode ([ATOM-2122] section 1: the index cache is
+ * float8_e4m3fn (num_blocks, 128, 128) and the block score is the fp32
+ * product of the index query with the fp8 keys times sm_scale*log2(e);
+ * section 2: row i of a q_len-L request sees ctx - L + i + 1 tokens).
+ *
+ *   q_idx         bf16 [rows, 128], one index query per row; last dim
+ *                 contiguous, row stride a multiple of 8, 16-byte aligned.
+ *   index_cache   u8/f8e4m3 [num_blocks, 128, 128] contiguous, token-major:
+ *                 the key of (page p, token slot o) is the 128 bytes at
+ *                 (p*128 + o)*128.  No scale (codes are the key values).
+ *   block_table, context_lens, cu_seqlens_q, max_q_len
+ *                 as in pa_decode / pa_decode_opts (the same row rules;
+ *                 max_q_len only sizes the launch of a ragged call).
+ *   sm_scale      0 => 1/sqrt(128).
+ *   sparse_page_idx  int32 [rows, topk] output, contiguous rows: the row's
+ *                 topk highest-scoring logical pages (ties to the lower page)
+ *                 in ascending order, padded with -1 when fewer pages have a
+ *                 visible token.  1 <= topk <= 4096.
+ *   block_scores  float32 [rows, W] output, contiguous rows, caller-owned
+ *                 (also the buffer between the two kernels): score of
+ *                 logical page n for the row = log2 of the sum over its
+ *                 visible tokens of 2^(sm_scale*log2(e)*<q, k_t>); -inf for
+ *                 a page with no visible token or an id outside the cache
+ *                 (so every entry past the row's last visible page is -inf).
+ *   stream        hipStream_t.
+ * Two kernels (scores, then top-k), asynchronous, no allocation (capturable).
+ * Returns PA_OK or a pa_status; every check happens before launch.
+ */
+int pa_index_topk(const pa_tensor* q_idx, const pa_tensor* index_cache,
+                  const pa_tensor* block_table, const pa_tensor* context_lens,
+                  const pa_tensor* cu_seqlens_q, int max_q_len, float sm_scale,
+                  pa_tensor* sparse_page_idx, pa_tensor* block_scores, void* stream);
+
 /* pa_query_support -- can this configuration be served?  Call at startup
  * to refuse a configuration before serving it ([ATOM-2710] review "Should
  * fix" 2).  PA_OK or the error pa_decode would return. */

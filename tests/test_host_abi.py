@@ -208,3 +208,50 @@ def test_write_to_bf16_cache_refuses_scales():
     u8 = _host_tensor((2, 1, 16384), torch.uint8)
     d = [_lib.desc(x) for x in (k, k, slots, kc, u8, ks, ks)]
     assert lib.kv_quant_write(*[_lib.ref(x) for x in d], 0, None) == -2
+
+
+def _index_args(**over):
+    t = dict(
+        q=_host_tensor((4, 128), torch.bfloat16),
+        cache=_host_tensor((8, 128, 128), torch.uint8),
+        bt=_host_tensor((4, 3), torch.int32),
+        ctx=_host_tensor((4,), torch.int32),
+        cu=None,
+        idx=_host_tensor((4, 32), torch.int32),
+        scores=_host_tensor((4, 3), torch.float32),
+        max_q_len=0,
+    )
+    t.update(over)
+    return t
+
+
+def _call_index(t):
+    lib = pa.load()
+    d = [_lib.desc(t[k]) for k in ("q", "cache", "bt", "ctx", "cu")]
+    di, ds = _lib.desc(t["idx"]), _lib.desc(t["scores"])
+    return lib.pa_index_topk(*[_lib.ref(x) for x in d], t["max_q_len"], 0.0, _lib.ref(di), _lib.ref(ds), None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=_host_tensor((4, 128), torch.float32)), -2),
+    (dict(q=_host_tensor((4, 64), torch.bfloat16)), -3),
+    (dict(cache=_host_tensor((8, 128, 64), torch.uint8)), -3),
+    (dict(cache=_host_tensor((8, 128, 128), torch.bfloat16)), -2),
+    (dict(bt=_host_tensor((4, 3), torch.int64)), -2),
+    (dict(ctx=_host_tensor((3,), torch.int32)), -3),
+    (dict(q=_host_tensor((6, 128), torch.bfloat16), idx=_host_tensor((6, 32), torch.int32),
+          scores=_host_tensor((6, 3), torch.float32)), -3),  # 6 rows over 4 requests, no cu
+    (dict(idx=_host_tensor((4, 0), torch.int32)), -3),
+    (dict(idx=_host_tensor((4, 5000), torch.int32)), -6),
+    (dict(scores=_host_tensor((4, 4), torch.float32)), -3),
+    (dict(max_q_len=-1), -1),
+])
+def test_index_topk_refuses_bad_descriptors_before_launch(over, status):
+    assert _call_index(_index_args(**over)) == status
+    assert pa.pa_last_error()
+
+
+def test_index_topk_accepts_a_well_formed_empty_call():
+    t = _index_args(q=_host_tensor((0, 128), torch.bfloat16), idx=_host_tensor((0, 32), torch.int32),
+                    scores=_host_tensor((0, 3), torch.float32))
+    assert _call_index(t) == 0, pa.pa_last_error()

@@ -49,7 +49,10 @@ CONFIGS = {
     "c3b": lambda: wl.bf16_kv(wl.c3_dense_128k(wl.PER_TOKEN)),
     "c4b": lambda: wl.bf16_kv(wl.c4_spec("uniform")),
     "c5b": lambda: wl.bf16_kv(wl.c5_sparse(False)),
+    # the sparse indexer in the step: write, index top-32, block-sparse decode
+    "c5i": lambda: wl.index_workload("c5"),
 }
+INDEX_TOPK = {"c5i": 32}
 
 
 def log(*a):
@@ -60,8 +63,9 @@ class Layers:
     """The workload's cache replicated over `n` layers in one allocation;
     layer l's block table points at pool pages [l*NB, (l+1)*NB)."""
 
-    def __init__(self, w, n, dev):
+    def __init__(self, w, n, dev, index_topk=0):
         self.w, self.n, self.dev = w, n, dev
+        self.index_topk = index_topk
         NB, Hkv = w.num_blocks, w.Hkv
         tot = NB * n
         bf = w.kv_dtype == "bf16"
@@ -120,21 +124,52 @@ class Layers:
         self.step_v = torch.from_numpy(v).to(dev)
         self.step_slots = [torch.from_numpy(s + np.int64(l * NB * 128)).to(dev) for l in range(n)]
         self.max_q_len = int(w.q_lens.max())
+        if index_topk:
+            # index cache over the same pages (layer l at pool pages l*NB ...),
+            # index queries, and per-layer score and list buffers
+            t1 = time.time()
+            self.icache = torch.empty(tot, 128, 128, dtype=torch.uint8, device=dev)
+            self.icache[:NB].copy_(torch.from_numpy(w.index_cache().reshape(NB, 128, 128)))
+            for l in range(1, n):
+                self.icache[l * NB:(l + 1) * NB].copy_(self.icache[:NB])
+            self.q_idx = torch.from_numpy(w.index_queries()).to(dev).to(torch.bfloat16)
+            self.scores = [torch.empty(w.rows, w.W, dtype=torch.float32, device=dev) for _ in range(n)]
+            self.lists = [torch.empty(w.rows, index_topk, dtype=torch.int32, device=dev) for _ in range(n)]
+            torch.cuda.synchronize()
+            log(f"index cache x {n} layers ready in {time.time() - t1:.1f}s")
 
     force_parts = 0
     prefetch_depth = 0
     workgroup_waves = 0
 
-    def step(self, l, ev=None):
+    def step(self, l, ev=None, ev_index=None):
         pa.kv_quant_write(self.step_k, self.step_v, self.step_slots[l], self.kc, self.vc,
                           self.ks_arg, self.vs_arg, self.mode)
+        sp = self.sp
+        if self.index_topk:
+            if ev_index is not None:
+                ev_index[0].record()
+            pa.pa_index_topk(self.q_idx, self.icache, self.bt[l], self.ctx, self.cu, self.lists[l],
+                             self.scores[l], max_q_len=self.max_q_len if self.cu is not None else 0)
+            if ev_index is not None:
+                ev_index[1].record()
+            sp = self.lists[l]
         pa.pa_decode_ex(self.q[l], self.kc, self.vc, self.ks_arg, self.vs_arg, self.bt[l], self.ctx,
-                        self.cu, self.sp, self.mode, self.out[l],
+                        self.cu, sp, self.mode, self.out[l],
                         max_q_len=self.max_q_len if self.cu is not None else 0,
                         force_parts=self.force_parts, prefetch_depth=self.prefetch_depth,
                         workgroup_waves=self.workgroup_waves,
                         main_begin_event=None if ev is None else ev[0],
                         main_end_event=None if ev is None else ev[1])
+
+
+def index_bytes(w, topk):
+    """Bytes one pa_index_topk call must move: the index keys of every
+    visible page once per request (the rows of a request share each read),
+    the index queries, the score matrix written and read back, the lists
+    written, and the block-table entries."""
+    pages = sum(min((int(c) + 127) // 128, w.W) for c in w.ctx)
+    return pages * 128 * 128 + w.rows * 128 * 2 + 2 * w.rows * w.W * 4 + w.rows * topk * 4 + 4 * pages
 
 
 def algorithmic_bytes(w):
@@ -225,13 +260,15 @@ def hbm_probe(dev, gib=4, same_bytes=None):
     return round(best, 1), best_small
 
 
-def cpu_baseline(w, layers, budget_s=12.0):
+def cpu_baseline(w, layers, budget_s=12.0, index_topk=0):
     """The oracle, as it stands, on one core: the same step -- write the
-    step's new tokens of a request, then attend that request's rows over its
+    step's new tokens of a request, (with the indexer: score every visible
+    page and take the top-k,) then attend that request's rows over its
     cache -- for requests of the workload, repeated until about `budget_s`
     seconds of CPU work.  The oracle's cache for a request is prepared
     untimed (it is state, as the GPU cache is).  The GPU's layer-0 output for
-    the same rows is checked against the oracle's."""
+    the same rows is checked against the oracle's (and, with the indexer,
+    the GPU's page lists against the oracle's)."""
     try:
         from threadpoolctl import threadpool_limits
     except Exception:  # pragma: no cover
@@ -239,6 +276,7 @@ def cpu_baseline(w, layers, budget_s=12.0):
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from harness import compare
     from oracle import attention as oatt
+    from oracle import indexer as oidx
     from oracle import writer as owr
 
     lim = threadpool_limits(1) if threadpool_limits else None
@@ -274,25 +312,37 @@ def cpu_baseline(w, layers, budget_s=12.0):
             c = int(w.ctx[b])
             new_slots = np.array([bt[0, (c - L + i) // 128] * 128 + (c - L + i) % 128 for i in range(L)],
                                  dtype=np.int64)
-            return kc, vc, ka, va, bt, new_slots
+            icache = None
+            if index_topk:
+                pm = {(b, pg): ci for ci, pg in enumerate(pages)}
+                icache = w.index_cache(poison=False, num_blocks=nb, page_map=pm)
+            return kc, vc, ka, va, bt, new_slots, icache
 
-        reqs = list(range(min(w.B, 4)))
+        reqs = list(range(min(w.B, 2 if index_topk else 4)))
         state = {b: request_state(b) for b in reqs}
+        q_idx = w.index_queries() if index_topk else None
+        gpu_lists = layers.lists[0].cpu().numpy() if index_topk else None
+        lists_equal = True
         done_bytes, t_used, n, check = 0, 0.0, 0, None
         while (t_used < budget_s and n < 4096) or n < len(reqs):
             b = reqs[n % len(reqs)]
-            kc, vc, ka, va, bt, new_slots = state[b]
+            kc, vc, ka, va, bt, new_slots, icache = state[b]
             start, L = int(w.row_start[b]), int(w.q_lens[b])
             rows = list(range(start, start + L))
             sp = None if w.sparse is None else w.sparse[start:start + L]
             cu = None if w.cu is None else np.array([0, L])
-            # timed: the step on the CPU (write the new tokens, attend the rows)
+            # timed: the step on the CPU (write the new tokens, [index,] attend the rows)
             t0 = time.time()
             write(sk[start:start + L], sv[start:start + L], new_slots, kc, vc, ka, va)
+            if index_topk:
+                sc = oidx.block_scores_ref(q_idx[start:start + L], icache, bt, w.ctx[b:b + 1], cu)
+                sp = oidx.topk_ref(sc, index_topk)
             ref = oatt.attention_ref(w.q[start:start + L], kc, vc, ka, va, bt, w.ctx[b:b + 1], cu, sp,
                                      w.mode, w.Hkv, kv_dtype=w.kv_dtype)
             t_used += time.time() - t0
-            if n < len(reqs):
+            if index_topk and n < len(reqs):
+                lists_equal &= bool(np.array_equal(sp, gpu_lists[start:start + L]))
+            if n < len(reqs) and (not index_topk or np.array_equal(sp, gpu_lists[start:start + L])):
                 err, cos = compare(out0[rows], ref, what=f"bench check request {b}")
                 check = (err, cos) if check is None else (max(err, check[0]), min(cos, check[1]))
             if w.sparse is None:
@@ -301,6 +351,8 @@ def cpu_baseline(w, layers, budget_s=12.0):
                 sel = {int(x) for r in rows for x in w.sparse[r] if 0 <= x < w.W}
                 toks = sum(min(128, int(w.ctx[b]) - 128 * x) for x in sel)
             done_bytes += toks * w.Hkv * (512 if bf else 256 + (8 if w.mode == wl.PER_TOKEN else 0))
+            if index_topk:
+                done_bytes += min((int(w.ctx[b]) + 127) // 128, w.W) * 128 * 128
             n += 1
     finally:
         if lim is not None:
@@ -311,9 +363,13 @@ def cpu_baseline(w, layers, budget_s=12.0):
         "cores": 1,
         "kind": "oracle",
         "sample": f"{n} request-steps over the first {len(reqs)} requests of {w.name} (write the "
-                  f"request's new tokens, decode its attended pages, fp64 softmax attention for its "
-                  f"rows), one host thread, {t_used:.1f} s timed",
+                  f"request's new tokens, "
+                  + (f"score its visible pages on the index cache and take the top-{index_topk}, "
+                     if index_topk else "")
+                  + f"decode its attended pages, fp64 softmax attention for its rows), one host thread, "
+                  f"{t_used:.1f} s timed",
         "check_max_abs_err": None if check is None else round(check[0], 6),
+        **({"check_index_lists_equal": lists_equal} if index_topk else {}),
         "check_min_cos": None if check is None else round(check[1], 8),
     }
 
@@ -342,12 +398,21 @@ def main():
     torch.cuda.set_device(dev)
 
     w = CONFIGS[args.config]()
+    index_topk = INDEX_TOPK.get(args.config, 0)
+    idx_bytes = index_bytes(w, index_topk) if index_topk else 0
+    if index_topk:
+        # the decode attends the indexer's lists: size its bytes for full pages
+        # now, recomputed from the lists the indexer produced after warmup
+        w.sparse = np.zeros((w.rows, index_topk), np.int32)
     kv_bytes, alg_bytes = algorithmic_bytes(w)
-    n_layers = args.layers or max(1, min(64, int(math.ceil(1.0e9 / max(kv_bytes, 1)))))
-    layers = Layers(w, n_layers, dev)
+    n_layers = args.layers or max(1, min(64, int(math.ceil(1.0e9 / max(kv_bytes + idx_bytes, 1)))))
+    if index_topk:
+        w.sparse = None
+    layers = Layers(w, n_layers, dev, index_topk)
 
     stream = torch.cuda.Stream()
-    cfg = pa.make_config(w.Hkv, w.rows, w.B, w.W, topk=0 if w.sparse is None else w.sparse.shape[1],
+    cfg = pa.make_config(w.Hkv, w.rows, w.B, w.W,
+                         topk=index_topk or (0 if w.sparse is None else w.sparse.shape[1]),
                          ragged=w.cu is not None, max_q_len=int(w.q_lens.max()) if w.cu is not None else 0,
                          scale_mode=w.mode, force_parts=args.force_parts,
                          kv_dtype=3 if w.kv_dtype == "bf16" else 1)
@@ -363,6 +428,10 @@ def main():
         for i in range(max(W, n_layers)):   # warm up eagerly (also first-touch)
             layers.step(i % n_layers)
     torch.cuda.synchronize()
+    if index_topk:
+        # the pages the decode attends are the ones the indexer chose
+        w.sparse = layers.lists[0].cpu().numpy()
+        kv_bytes, alg_bytes = algorithmic_bytes(w)
 
     # one graph per G consecutive steps (layers 0..G-1)
     graph = torch.cuda.CUDAGraph()
@@ -400,6 +469,8 @@ def main():
     n_ev = min(max(K, 1), max(4 * n_layers, 32), 512)
     evs2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(n_ev)]
+    evs_idx = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_ev)] if index_topk else [None] * n_ev
     with torch.cuda.stream(stream):
         for a, b in evs2:
             a.record()
@@ -407,14 +478,15 @@ def main():
         torch.cuda.synchronize()
         torch.cuda._sleep(int(2e8))
         for i, ev in enumerate(evs2):
-            layers.step(i % n_layers, ev)
+            layers.step(i % n_layers, ev, evs_idx[i])
     torch.cuda.synchronize()
     main_ms = [a.elapsed_time(b) for a, b in evs2]
     timing = (f"HIP events recorded around each main-kernel launch on the launch stream, {n_ev} "
               f"steps queued behind a spin kernel")
     main_avg_ms = float(np.mean(main_ms))
     achieved = alg_bytes / (main_avg_ms * 1e-3) / 1e9
-    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    value = (kv_bytes + idx_bytes) / (ms_per_step * 1e-3) / 1e9
+    index_avg_ms = float(np.mean([a.elapsed_time(b) for a, b in evs_idx])) if index_topk else None
     tokens_per_s = w.attended_tokens() * w.Hkv / (ms_per_step * 1e-3)
 
     if args.calib_copy:
@@ -424,8 +496,8 @@ def main():
             torch.mul(x, 1.0, out=y)
         torch.cuda.synchronize()
 
-    probe, probe_same = hbm_probe(dev, same_bytes=alg_bytes) or (None, None)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, layers)
+    probe, probe_same = hbm_probe(dev, same_bytes=idx_bytes if index_topk else alg_bytes) or (None, None)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, layers, index_topk=index_topk)
 
     res = {
         "metric": "decode attention KV GB/s & % HBM roofline (attended tokens/s), 1 MI355X",
@@ -473,6 +545,25 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if index_topk:
+        # the indexer reads 16x the decode's bytes here: it is the dominant kernel
+        ia = idx_bytes / (index_avg_ms * 1e-3) / 1e9
+        res["config"]["index_topk"] = index_topk
+        res["config"]["index_bytes_per_step"] = int(idx_bytes)
+        res["decode_main"] = {k: res["roofline"][k] for k in ("achieved", "frac", "avg_launch_us",
+                                                               "algorithmic_bytes_per_launch")}
+        res["roofline"].update({
+            "kernel": "pa_index_topk (index_score_kernel + index_topk_kernel)",
+            "achieved": round(ia, 1),
+            "frac": round(ia / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(index_avg_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(idx_bytes),
+            "timing": f"torch events on the launch stream around each pa_index_topk call, {n_ev} steps "
+                      f"queued behind a spin kernel",
+            "frac_of_probe": None if not probe else round(ia / probe, 4),
+            "frac_of_same_bytes_probe": None if not probe_same else round(ia / probe_same, 4),
+        })
     print(json.dumps(res), flush=True)
 
 

@@ -33,7 +33,8 @@ namespace fp8pa {
 namespace {
 
 constexpr int kIdxWaves = 4;     // pages per score workgroup (one per wave)
-constexpr int kTopkThreads = 256;
+constexpr int kTopkThreads = 256;  // one thread per radix bin in the digit search
+constexpr int kStageKeys = 8192;   // rows with up to this many pages keep their keys in LDS
 
 typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
 __device__ __forceinline__ const_i32_ptr as_const(const int32_t* p) { return (const_i32_ptr)(p); }
@@ -170,6 +171,7 @@ __global__ __launch_bounds__(kTopkThreads) void index_topk_kernel(IndexArgs a) {
   __shared__ int hist[256];
   __shared__ int sm_wave[kTopkThreads / kWave];
   __shared__ uint32_t sm_sel[2];  // threshold digit result, remaining count
+  __shared__ uint32_t sm_keys[kStageKeys];
   const int row = blockIdx.x;
   const int t = threadIdx.x;
 
@@ -195,12 +197,21 @@ __global__ __launch_bounds__(kTopkThreads) void index_topk_kernel(IndexArgs a) {
   int32_t* orow = a.out_idx + int64_t(row) * a.out_stride;
   const int k = a.topk;
 
+  // keys of the row: staged once in LDS (coalesced read) when they fit,
+  // else read from the score matrix on every pass
+  const bool staged = n <= kStageKeys;
+  if (staged) {
+    for (int i = t; i < n; i += kTopkThreads) sm_keys[i] = score_key(srow[i]);
+    __syncthreads();
+  }
+  auto key_at = [&](int i) -> uint32_t { return staged ? sm_keys[i] : score_key(srow[i]); };
+
   // this thread's contiguous slice of the row's pages
   const int chunk = (n + kTopkThreads - 1) / kTopkThreads;
   const int c0 = min(n, t * chunk), c1 = min(n, c0 + chunk);
 
   int fin = 0;
-  for (int i = c0; i < c1; ++i) fin += srow[i] > -INFINITY;
+  for (int i = c0; i < c1; ++i) fin += key_at(i) != 0u;
   int total_fin;
   block_exclusive_scan(fin, &total_fin, sm_wave);
 
@@ -214,19 +225,21 @@ __global__ __launch_bounds__(kTopkThreads) void index_topk_kernel(IndexArgs a) {
       for (int i = t; i < 256; i += kTopkThreads) hist[i] = 0;
       __syncthreads();
       for (int i = c0; i < c1; ++i) {
-        const uint32_t key = score_key(srow[i]);
+        const uint32_t key = key_at(i);
         if (key != 0u && (key & mask) == prefix) atomicAdd(&hist[(key >> sh) & 255u], 1);
       }
       __syncthreads();
-      if (t == 0) {
-        // highest digit D with count(digit > D) < rem <= count(digit >= D)
-        int above = 0, D = 255;
-        for (; D > 0; --D) {
-          if (above + hist[D] >= rem) break;
-          above += hist[D];
+      // the digit D with count(digit > D) < rem <= count(digit >= D): thread
+      // t holds digit 255 - t, an exclusive scan gives count(digit > D)
+      {
+        const int D = 255 - t;
+        const int cnt = hist[D];
+        int tot;
+        const int above = block_exclusive_scan(cnt, &tot, sm_wave);
+        if (above < rem && rem <= above + cnt) {
+          sm_sel[0] = uint32_t(D);
+          sm_sel[1] = uint32_t(rem - above);
         }
-        sm_sel[0] = uint32_t(D);
-        sm_sel[1] = uint32_t(rem - above);
       }
       __syncthreads();
       prefix |= sm_sel[0] << sh;
@@ -241,7 +254,7 @@ __global__ __launch_bounds__(kTopkThreads) void index_topk_kernel(IndexArgs a) {
   // pass 1: counts; pass 2: write the chosen pages in ascending order
   int gt = 0, eq = 0;
   for (int i = c0; i < c1; ++i) {
-    const uint32_t key = score_key(srow[i]);
+    const uint32_t key = key_at(i);
     if (total_fin > k) {
       gt += key > thr;
       eq += key == thr;
@@ -256,7 +269,7 @@ __global__ __launch_bounds__(kTopkThreads) void index_topk_kernel(IndexArgs a) {
   int pos = block_exclusive_scan(gt + take_eq, &total_sel, sm_wave);
   int eq_left = take_eq;
   for (int i = c0; i < c1; ++i) {
-    const uint32_t key = score_key(srow[i]);
+    const uint32_t key = key_at(i);
     bool pick;
     if (total_fin > k) {
       pick = key > thr || (key == thr && eq_left > 0);

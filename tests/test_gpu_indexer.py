@@ -168,3 +168,14 @@ def test_index_full_size_sampled_rows(kind):
             chosen = idx[r][idx[r] >= 0]
             rest = np.setdiff1d(np.nonzero(fin)[0], chosen)
             assert ref[i, chosen].min() >= ref[i, rest].max() - 2 * ATOL
+
+
+def test_rows_too_long_for_lds_staging():
+    """A row that sees more than 8192 pages: the top-k kernel reads the
+    score matrix on every pass instead of staging the keys."""
+    w = wl.small_case(seed=509, ctx=[8300 * 128 - 5, 300], q_lens=[1, 1])
+    print("long row case", w.W, flush=True)
+    case = IndexCase(w, 64)
+    idx, scores = case.run()
+    ref = oidx.block_scores_ref(case.q_np, case.cache_np, w.block_table, w.ctx)
+    check(case, idx, scores, ref, "8300-page row")

@@ -17,6 +17,7 @@ MAX_DIMS = 6
 
 DTYPE_U8, DTYPE_F8E4M3, DTYPE_BF16, DTYPE_F32, DTYPE_I32, DTYPE_I64 = 1, 2, 3, 4, 5, 6
 SCALE_NONE, SCALE_SCALAR, SCALE_PER_TOKEN = 0, 1, 2
+MERGE_PLAN, MERGE_SEPARATE, MERGE_IN_KERNEL = 0, 1, 2
 
 STATUS = {
     0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_DTYPE", -3: "PA_ERR_SHAPE",
@@ -53,6 +54,7 @@ class PaDecodeOpts(ctypes.Structure):
         ("main_end_event", ctypes.c_void_p),
         ("prefetch_depth", ctypes.c_int32),
         ("workgroup_waves", ctypes.c_int32),
+        ("merge_mode", ctypes.c_int32),
     ]
 
 
@@ -71,7 +73,7 @@ class PaConfig(ctypes.Structure):
         ("ragged", ctypes.c_int32),
         ("max_q_len", ctypes.c_int32),
         ("force_parts", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("merge_mode", ctypes.c_int32),
     ]
 
 
@@ -88,7 +90,7 @@ class PaPlanInfo(ctypes.Structure):
         ("pages_bucket", ctypes.c_int64),
         ("scratch_bytes", ctypes.c_int64),
         ("merge", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("merge_in_kernel", ctypes.c_int32),
     ]
 
 

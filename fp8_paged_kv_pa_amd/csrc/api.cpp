@@ -100,24 +100,34 @@ int check_scales(const pa_tensor* ks, const pa_tensor* vs, int mode, int64_t nb,
 
 // ---------------------------------------------------------------------------
 // Scratch arenas, one per (device, stream).
+// Layout: [arrival counters, counter_bytes][split-K partials].  The counter
+// region has a fixed size per arena, so partials of one call never land
+// where a later call keeps counters; counters are zeroed on allocation and
+// every in-kernel merge puts its counters back to zero.
 struct Arena {
   void* ptr = nullptr;
-  size_t bytes = 0;
+  size_t bytes = 0;          // total
+  size_t counter_bytes = 0;  // leading counter region
 };
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Arena> g_arenas;
 
-int get_scratch(hipStream_t stream, size_t need, void** out) {
-  *out = nullptr;
-  if (need == 0) return PA_OK;
+int get_scratch(hipStream_t stream, size_t need_counters, size_t need_partials, uint32_t** counters,
+                void** partials) {
+  *counters = nullptr;
+  *partials = nullptr;
+  if (need_counters == 0 && need_partials == 0) return PA_OK;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
   std::lock_guard<std::mutex> lk(g_mu);
   Arena& ar = g_arenas[{dev, reinterpret_cast<void*>(stream)}];
-  if (ar.bytes >= need) {
-    *out = ar.ptr;
+  if (ar.ptr && ar.counter_bytes >= need_counters && ar.bytes - ar.counter_bytes >= need_partials) {
+    *counters = static_cast<uint32_t*>(ar.ptr);
+    *partials = static_cast<char*>(ar.ptr) + ar.counter_bytes;
     return PA_OK;
   }
+  const size_t cnt = std::max(ar.counter_bytes, need_counters);
+  const size_t need = cnt + std::max(ar.ptr ? ar.bytes - ar.counter_bytes : size_t(0), need_partials);
   hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(stream, &st) != hipSuccess) return fail(PA_ERR_HIP, "hipStreamIsCapturing failed");
   if (st != hipStreamCaptureStatusNone)
@@ -132,13 +142,22 @@ int get_scratch(hipStream_t stream, size_t need, void** out) {
     hipFree(ar.ptr);
     ar.ptr = nullptr;
     ar.bytes = 0;
+    ar.counter_bytes = 0;
   }
   if (hipMalloc(&ar.ptr, sz) != hipSuccess) {
     ar.ptr = nullptr;
     return fail(PA_ERR_HIP, "hipMalloc of " + std::to_string(sz) + " bytes of split-K scratch failed");
   }
+  // counters must start at zero (never reached under capture: growth is refused there)
+  if (hipMemsetAsync(ar.ptr, 0, cnt, stream) != hipSuccess) {
+    hipFree(ar.ptr);
+    ar.ptr = nullptr;
+    return fail(PA_ERR_HIP, "clearing the split-K counters failed");
+  }
   ar.bytes = sz;
-  *out = ar.ptr;
+  ar.counter_bytes = cnt;
+  *counters = static_cast<uint32_t*>(ar.ptr);
+  *partials = static_cast<char*>(ar.ptr) + cnt;
   return PA_OK;
 }
 
@@ -216,6 +235,7 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   cfg.ragged = ragged ? 1 : 0;
   cfg.max_q_len = opts ? opts->max_q_len : 0;
   cfg.force_parts = opts ? opts->force_parts : 0;
+  cfg.merge_mode = opts ? opts->merge_mode : 0;
   if (opts && (opts->prefetch_depth < 0 || opts->prefetch_depth > 4))
     return fail(PA_ERR_INVALID_ARG, "prefetch_depth must be in [0, 4]");
   if (opts && opts->workgroup_waves != 0 && opts->workgroup_waves != 4 && opts->workgroup_waves != 8)
@@ -226,8 +246,11 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   if (rows == 0) return PA_OK;
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  uint32_t* counters = nullptr;
   void* scratch = nullptr;
-  if ((rc = get_scratch(stream, size_t(plan.scratch_bytes), &scratch))) return rc;
+  if ((rc = get_scratch(stream, size_t(plan.counter_bytes), size_t(plan.scratch_bytes - plan.counter_bytes),
+                        &counters, &scratch)))
+    return rc;
 
   DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q->data);
@@ -250,6 +273,7 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
     const int64_t pairs = int64_t(plan.parts_launched) * rows * Hq;
     a.part_ml = static_cast<float*>(scratch);
     a.part_acc = static_cast<float*>(scratch) + 2 * pairs;
+    a.unit_count = plan.fused_merge ? counters : nullptr;
   }
   a.num_blocks = nb;
   a.hkv = int32_t(hkv);
@@ -264,6 +288,8 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   a.ppp = plan.ppp;
   a.scale_mode = mode;
   a.kv_bf16 = bf16kv ? 1 : 0;
+  a.xcd_grouped = plan.xcd_grouped ? 1 : 0;
+  a.nq = int32_t(plan.nq);
   float sm = (opts && opts->sm_scale != 0.0f) ? opts->sm_scale : 1.0f / std::sqrt(float(kDim));
   a.sm_log2 = sm * 1.4426950408889634f;
 
@@ -484,8 +510,10 @@ int pa_reserve(const pa_config* cfg, void* stream) {
   std::string err;
   int rc = make_plan(*cfg, &p, &err);
   if (rc) return fail(rc, err);
+  uint32_t* c = nullptr;
   void* s = nullptr;
-  return get_scratch(reinterpret_cast<hipStream_t>(stream), size_t(p.scratch_bytes), &s);
+  return get_scratch(reinterpret_cast<hipStream_t>(stream), size_t(p.counter_bytes),
+                     size_t(p.scratch_bytes - p.counter_bytes), &c, &s);
 }
 
 int pa_release(void) {

@@ -30,6 +30,7 @@ struct DecodeArgs {
   int64_t out_head_stride;
   float* part_ml;             // scratch: (m, l) float2 [parts][rows][Hq]
   float* part_acc;            // scratch: float [parts][rows][Hq][128]
+  uint32_t* unit_count;       // scratch: per-unit arrival counters (in-kernel merge), or null
   int64_t num_blocks;
   int32_t hkv;
   int32_t rows;
@@ -43,6 +44,8 @@ struct DecodeArgs {
   int32_t ppp;                // pages / list entries per partition
   int32_t scale_mode;
   int32_t kv_bf16;            // 1: unquantized bf16 cache (no scales)
+  int32_t xcd_grouped;        // 1: dense grid with a (request, head, partition)'s row groups on one XCD
+  int32_t nq;                 // (request, KV head, partition) triples when xcd_grouped
   float sm_log2;              // sm_scale * log2(e)
 };
 

@@ -130,11 +130,111 @@ __device__ __forceinline__ const_i32_ptr as_const(const int32_t* p) { return (co
 template <int RT, bool NBUF2_NW4, bool BF>
 constexpr int kMinBlocks = (NBUF2_NW4 && !(BF && RT == 2)) ? 2 : 1;
 
+// In-kernel log-sum-exp merge.  Every partition of a unit (request or
+// row, KV head, row group) bumps the unit's counter once its partial is
+// visible to the whole device; the partition that sees parts-1 knows every
+// partial is written and merges them (the same arithmetic as pa_merge, in
+// partition order), then puts the counter back to 0 for the next call.
+// Threads < 256: (head oh, 8 dims od) as in the wave merge.  sm_w holds
+// 16 x kMaxParts weights (LDS of the finished wave merge).
+constexpr int kMaxMergeParts = 256;
+constexpr int kMergeChunk = 8;  // partitions whose accumulators are loaded together
+
+__device__ void merge_if_last(const DecodeArgs& a, int64_t unit, int row0, int nrows, int h, float* sm_w) {
+  __shared__ int sm_last;
+  // The barrier completes every wave's partial stores; one device-scope
+  // fence by thread 0 then publishes them all (a fence writes back and
+  // invalidates the XCD's L2, so it is issued once per workgroup, not per
+  // wave).
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();  // release
+    const bool last = atomicAdd(a.unit_count + unit, 1u) == uint32_t(a.parts - 1);
+    if (last) __threadfence();  // acquire: every other partition's partial
+    sm_last = last;
+  }
+  __syncthreads();
+  if (!sm_last) return;
+  const int t = threadIdx.x;
+  const int li = t & 15;          // this thread's share of the partitions: li, li+16, ...
+  const int oh = (t >> 4) & 15;
+  const int od = li * 8;
+  const int P = a.parts;
+  const int Hq = 16 * a.hkv;
+  const int64_t stride_p = int64_t(a.rows) * Hq;
+  float v_fold = 1.0f;
+  if (a.scale_mode != PA_SCALE_PER_TOKEN && a.v_scale) v_fold = *a.v_scale;
+  for (int r = 0; r < nrows; ++r) {
+    const int row = row0 + r;
+    const int64_t base = int64_t(row) * Hq + 16 * h + oh;
+    float M = -INFINITY, L = 0.0f;
+    if (t < 256) {
+      float2 ml[kMaxMergeParts / 16];
+#pragma unroll
+      for (int i = 0; i < kMaxMergeParts / 16; ++i) {
+        const int p = li + 16 * i;
+        ml[i] = p < P ? *reinterpret_cast<const float2*>(a.part_ml + 2 * (p * stride_p + base))
+                      : float2{-INFINITY, 0.0f};
+        M = fmaxf(M, ml[i].x);
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 16));
+#pragma unroll
+      for (int i = 0; i < kMaxMergeParts / 16; ++i) {
+        const int p = li + 16 * i;
+        const float w = (M == -INFINITY || ml[i].x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml[i].x - M);
+        L += w * ml[i].y;
+        if (p < P) sm_w[oh * kMaxMergeParts + p] = w;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) L += __shfl_xor(L, o, 16);
+    }
+    __syncthreads();
+    if (t < 256) {
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      for (int p0 = 0; p0 < P; p0 += kMergeChunk) {
+        f32x4 v0[kMergeChunk], v1[kMergeChunk];
+#pragma unroll
+        for (int j = 0; j < kMergeChunk; ++j) {
+          const int p = min(p0 + j, P - 1);
+          const f32x4* ap = reinterpret_cast<const f32x4*>(a.part_acc + (p * stride_p + base) * 128 + od);
+          v0[j] = ap[0];
+          v1[j] = ap[1];
+        }
+#pragma unroll
+        for (int j = 0; j < kMergeChunk; ++j) {
+          // an empty partition has weight 0 and unwritten accumulators: skip, never multiply
+          const float w = p0 + j < P ? sm_w[oh * kMaxMergeParts + p0 + j] : 0.0f;
+          if (w != 0.0f) {
+            s0 += w * v0[j];
+            s1 += w * v1[j];
+          }
+        }
+      }
+      const float inv = L > 0.0f ? v_fold / L : 0.0f;
+      uint32_t packed[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        packed[e] = uint32_t(f32_to_bf16_rne(s0[2 * e] * inv)) | (uint32_t(f32_to_bf16_rne(s0[2 * e + 1] * inv)) << 16);
+        packed[2 + e] =
+            uint32_t(f32_to_bf16_rne(s1[2 * e] * inv)) | (uint32_t(f32_to_bf16_rne(s1[2 * e + 1] * inv)) << 16);
+      }
+      uint16_t* op = a.out + int64_t(row) * a.out_row_stride + int64_t(16 * h + oh) * a.out_head_stride + od;
+      *reinterpret_cast<u32x4*>(op) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    }
+    __syncthreads();
+  }
+  if (t == 0) atomicExch(a.unit_count + unit, 0u);
+}
+
 template <int RT, bool PER_TOKEN, bool SPARSE, int NBUF, int NW, bool BF>
 __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, BF>)) void pa_decode_main(
     DecodeArgs a) {
   static_assert(!(BF && PER_TOKEN), "a bf16 cache carries no scales");
   static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
+  static_assert(NW * 16 * kAccPad >= 16 * kMaxMergeParts, "merge weights reuse the wave-merge LDS");
+  __shared__ float sm_ml[NW][RT][16][2];
+  __shared__ float sm_acc[NW][16][kAccPad];
   constexpr int S = NW / 4;  // pages streamed side by side (one per group of four waves)
   const int lane = threadIdx.x & (kWave - 1);
   // wave index as a provably uniform (scalar) value: table reads indexed by
@@ -146,8 +246,29 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   const int hr = lane & 15;  // query head within the GQA group
   const int Hq = 16 * a.hkv;
 
-  const int part = int(blockIdx.x % uint32_t(a.parts));
-  const int64_t unit = blockIdx.x / uint32_t(a.parts);
+  int part;
+  int64_t unit;
+  if (!SPARSE && a.xcd_grouped) {
+    // Row groups of one (request, KV head, partition) read the same pages:
+    // give them workgroup ids x + 8s, x + 8(s+1), ... -- consecutive
+    // dispatches on the same XCD (ids go round-robin over the 8 XCDs), so
+    // the second read of each page is an L2 hit.
+    const uint32_t x = blockIdx.x & 7u, s = blockIdx.x >> 3;
+    const uint32_t gi = s % uint32_t(a.groups);
+    const uint32_t q = (s / uint32_t(a.groups)) * 8u + x;  // (partition, request, KV head)
+    if (q >= uint32_t(a.nq)) return;                         // padding of the last XCD round
+    const uint32_t nbh = uint32_t(a.nq / a.parts);
+    part = int(q / nbh);
+    unit = int64_t(q % nbh) * a.groups + gi;
+  } else {
+    // partition-major: every request's first partitions (full ones) are
+    // dispatched before later (partial or empty) ones, so when there are
+    // more workgroups than slots the dispatcher hands the short ones to the
+    // CUs that finish first
+    const uint32_t units = uint32_t(gridDim.x / uint32_t(a.parts));
+    part = int(blockIdx.x / units);
+    unit = blockIdx.x % units;
+  }
 
   // ---- which rows, which request, which tokens -------------------------
   // The loads that decide the partition's work (context length, row range,
@@ -244,6 +365,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       const int64_t pi = (int64_t(part) * a.rows + row0 + r) * Hq + 16 * h + (threadIdx.x & 15);
       *reinterpret_cast<float2*>(a.part_ml + 2 * pi) = float2{-INFINITY, 0.0f};
     }
+    if (a.unit_count) merge_if_last(a, unit, row0, nrows, h, &sm_acc[0][0][0]);
     return;
   }
 
@@ -461,11 +583,15 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     int ln_next = logical_at(s0 + (NBUF - 1) * S);
     int P_next = raw_at(s0 + (NBUF - 1) * S, ln_next);
     int ln_after = logical_at(s0 + NBUF * S);
+    // Every step of an iteration runs, also past n1 (those positions were
+    // loaded as empty and take the skip path): an early exit between steps
+    // would leave the next step's loads pending at the loop latch, and the
+    // compiler would then wait for the current chunk before issuing the
+    // next one -- serializing the ring.
     for (int n = s0; n < n1; n += NBUF * S) {
 #pragma unroll
       for (int k = 0; k < NBUF; ++k) {
         const int nn = n + k * S;
-        if (nn >= n1) break;
         const int ls = (k + NBUF - 1) % NBUF;  // slot of position nn + (NBUF-1)*S (held nn - S)
         const int nl = nn + (NBUF - 1) * S;
         const bool ok = valid_page(P_next);
@@ -481,8 +607,6 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   }
 
   // ---- merge the waves, then write output or the partition partial --------
-  __shared__ float sm_ml[NW][RT][16][2];
-  __shared__ float sm_acc[NW][16][kAccPad];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     float lh = l_run[r];
@@ -554,6 +678,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     }
     __syncthreads();
   }
+  if (a.parts > 1 && a.unit_count) merge_if_last(a, unit, row0, nrows, h, &sm_acc[0][0][0]);
 }
 
 // One workgroup per (row, query head): combine the partitions' (m, l, acc)
@@ -705,7 +830,7 @@ hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool spa
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (merge) {
+  if (merge && !a.unit_count) {
     const int64_t pairs = int64_t(a.rows) * 16 * a.hkv;
     hipLaunchKernelGGL(pa_merge, dim3(uint32_t(pairs)), dim3(256), 0, stream, a);
     e = hipGetLastError();

@@ -48,6 +48,8 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
   if (c.force_parts < 0 || c.force_parts > kMaxParts)
     return fail(err, PA_ERR_INVALID_ARG, "force_parts must be in [0, 256]");
   if (c.max_q_len < 0) return fail(err, PA_ERR_INVALID_ARG, "max_q_len must be >= 0");
+  if (c.merge_mode < PA_MERGE_PLAN || c.merge_mode > PA_MERGE_IN_KERNEL)
+    return fail(err, PA_ERR_INVALID_ARG, "unknown merge_mode " + std::to_string(c.merge_mode));
   // Uniformity is never inferred from divisibility: without cu_seqlens_q the
   // call *declares* every request has rows/batch rows, so rows must divide.
   if (!c.ragged && c.rows % c.batch != 0)
@@ -106,11 +108,25 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
   p.waves = p.rt == 2 ? 8 : 4;
   p.merge = p.parts_launched > 1;
   p.grid = p.units * p.parts_launched;
+  if (!p.sparse && p.groups > 1) {
+    // workgroup id x + 8*(j*groups + gi) carries row group gi of triple
+    // 8j + x: the groups of a triple run back to back on one XCD
+    p.xcd_grouped = true;
+    p.nq = c.batch * hkv * p.parts_launched;
+    p.grid = ceil_div(p.nq, 8) * 8 * p.groups;
+  }
   if (p.merge) {
     // (m, l) pair + 128 accumulators per (partition, row, query head), sized
-    // by the bucket so one reservation serves the whole bucket.
+    // by the bucket so one reservation serves the whole bucket; in front of
+    // them one arrival counter per unit for the in-kernel merge.
     const int64_t per = 2 + kDim;
-    p.scratch_bytes = int64_t(p.parts) * p.rows_bucket * hkv * kGroup * per * int64_t(sizeof(float));
+    // The separate merge kernel is the default: measured on MI355X, the
+    // device-scope fences of the in-kernel merge (each a writeback and
+    // invalidate of the XCD's L2) cost more than the extra launch.
+    p.fused_merge = c.merge_mode == PA_MERGE_IN_KERNEL;
+    p.counter_bytes = (p.units_bucket * 4 + 255) / 256 * 256;
+    p.scratch_bytes = p.counter_bytes +
+                      int64_t(p.parts) * p.rows_bucket * hkv * kGroup * per * int64_t(sizeof(float));
   }
   if (p.scratch_bytes > kMaxScratchBytes)
     return fail(err, PA_ERR_CAPACITY, "split-K scratch for this bucket exceeds 4 GiB");
@@ -131,7 +147,7 @@ void describe(const Plan& p, pa_plan_info* info) {
   info->pages_bucket = p.pages_bucket;
   info->scratch_bytes = p.scratch_bytes;
   info->merge = p.merge ? 1 : 0;
-  info->reserved = 0;
+  info->merge_in_kernel = (p.merge && p.fused_merge) ? 1 : 0;
 }
 
 }  // namespace fp8pa

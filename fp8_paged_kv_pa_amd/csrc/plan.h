@@ -50,6 +50,10 @@ struct Plan {
   bool sparse = false;
   bool bf16kv = false;     // unquantized bf16 cache (32 KiB per page and head)
   bool merge = false;
+  bool fused_merge = false; // the last partition of a unit merges (no merge kernel)
+  int64_t counter_bytes = 0; // arrival counters at the start of the scratch (fused merge)
+  bool xcd_grouped = false;  // dense multi-group grid laid out so row groups share an XCD
+  int64_t nq = 0;          // (request, KV head, partition) triples (xcd_grouped)
   int64_t units = 0;       // dense: batch*Hkv*groups; sparse: rows*Hkv
   int64_t grid = 0;        // main-kernel workgroups (1-D)
   int64_t rows_bucket = 1;

@@ -96,6 +96,19 @@ typedef enum pa_scale_mode {
   PA_SCALE_PER_TOKEN = 2
 } pa_scale_mode;
 
+/* Where split-K partials are combined ([ATOM-2710] review "Must fix" 1
+ * names the partial scratch; the combination is the same log-sum-exp in
+ * either place). */
+typedef enum pa_merge_mode {
+  PA_MERGE_PLAN = 0,       /* the library's choice: the separate kernel       */
+                           /* (measured faster on MI355X: the in-kernel merge */
+                           /* needs device-scope fences, each an L2 writeback */
+                           /* and invalidate on the XCD)                      */
+  PA_MERGE_SEPARATE = 1,   /* a separate merge kernel after the main kernel   */
+  PA_MERGE_IN_KERNEL = 2   /* the last partition of each unit to finish      */
+                           /* merges all of them inside the main kernel       */
+} pa_merge_mode;
+
 /* Return codes.  Every host-checkable problem is reported before anything is
  * launched ([ATOM-2710] review "Should fix" 2; [ATOM-2614] "Change": decline
  * before the low-level launcher aborts).  pa_last_error() has the text. */
@@ -135,6 +148,7 @@ typedef struct pa_decode_opts {
   int32_t workgroup_waves; /* 0 => plan chooses; 4 (a workgroup streams one   */
                            /* page at a time) or 8 (two pages side by side;   */
                            /* two-row calls over a bf16 cache always use 4)   */
+  int32_t merge_mode;      /* pa_merge_mode                                   */
 } pa_decode_opts;
 
 /* Host-side description of a decode call, for capability queries, planning
@@ -154,7 +168,7 @@ typedef struct pa_config {
   int32_t ragged;          /* 1 if cu_seqlens_q is given                     */
   int32_t max_q_len;       /* as pa_decode_opts.max_q_len                    */
   int32_t force_parts;     /* as pa_decode_opts.force_parts                  */
-  int32_t reserved;
+  int32_t merge_mode;      /* as pa_decode_opts.merge_mode                   */
 } pa_config;
 
 /* The launch plan a config maps to (pa_plan_describe). */
@@ -168,8 +182,9 @@ typedef struct pa_plan_info {
   int64_t rows_bucket;     /* capacity bucket of rows (power of two)         */
   int64_t pages_bucket;    /* capacity bucket of pages / topk                */
   int64_t scratch_bytes;   /* split-K scratch this bucket needs (0 if none)  */
-  int32_t merge;           /* 1 if the LSE merge kernel runs                 */
-  int32_t reserved;
+  int32_t merge;           /* 1 if partials are merged (parts > 1)           */
+  int32_t merge_in_kernel; /* 1: merged inside the main kernel; 0: by the    */
+                           /* separate merge kernel (when merge is 1)        */
 } pa_plan_info;
 
 /*
@@ -297,7 +312,9 @@ int pa_plan_describe(const pa_config* cfg, pa_plan_info* info);
  * is per (device, stream): calls on one stream are serialised by the
  * stream; calls on different streams use different scratch.  A captured
  * graph keeps the scratch it was captured with; do not replay two copies of
- * one graph concurrently. */
+ * one graph concurrently.  The scratch starts with one arrival counter per
+ * unit for the in-kernel merge: zeroed when the scratch is allocated, and
+ * put back to zero by every call that uses it. */
 int pa_reserve(const pa_config* cfg, void* stream);
 
 /* pa_release -- free all scratch (synchronises the device first). */

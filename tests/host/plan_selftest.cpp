@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <set>
 #include <string>
+#include <vector>
 
 #include "../../fp8_paged_kv_pa_amd/csrc/plan.h"
 
@@ -38,6 +39,12 @@ static pa_config base() {
   c.max_pages = 72;
   return c;
 }
+
+// the C ABI's struct layouts (the Python binding mirrors them)
+static_assert(sizeof(pa_tensor) == 8 + 4 + 4 + 6 * 8 * 2, "pa_tensor");
+static_assert(sizeof(pa_decode_opts) == 48, "pa_decode_opts");
+static_assert(sizeof(pa_config) == 6 * 4 + 4 * 8 + 4 * 4, "pa_config");
+static_assert(sizeof(pa_plan_info) == 4 * 4 + 6 * 8 + 2 * 4, "pa_plan_info");
 
 int main() {
   std::string err;
@@ -86,6 +93,7 @@ int main() {
               c.max_pages = W;
               c.topk = topk;
               c.force_parts = fp;
+              c.merge_mode = (fp % 3 == 0) ? PA_MERGE_IN_KERNEL : PA_MERGE_PLAN;
               if (c.rows > kMaxRows) continue;
               int rc = make_plan(c, &p, &err);
               if (rc == PA_ERR_CAPACITY && fp > 0) {
@@ -93,7 +101,9 @@ int main() {
                 // largest bucket allows; it must be refused, never truncated
                 const long long pb = next_pow2(topk ? topk : W);
                 const long long parts = std::min<long long>(std::min<long long>(fp, kMaxParts), pb);
-                const long long want = parts * next_pow2(c.rows) * hkv * 16 * 130 * 4;
+                const long long units = topk ? c.rows * hkv : batch * hkv * ((L + 1) / 2);
+                const long long counters = (next_pow2(units) * 4 + 255) / 256 * 256;
+                const long long want = counters + parts * next_pow2(c.rows) * hkv * 16 * 130 * 4;
                 CHECK(want > kMaxScratchBytes, "refused although %lld bytes fit", want);
                 continue;
               }
@@ -110,10 +120,35 @@ int main() {
               CHECK((long long)p.ppp * (p.parts_launched - 1) < npages, "no empty tail partition");
               CHECK(p.merge == (p.parts_launched > 1), "merge flag");
               const long long units = topk ? c.rows * hkv : batch * hkv * p.groups;
-              CHECK(p.units == units && p.grid == units * p.parts_launched, "grid");
+              CHECK(p.units == units, "units");
+              if (!p.xcd_grouped) {
+                CHECK(p.grid == units * p.parts_launched, "grid");
+              } else {
+                // the XCD-grouped layout covers every (triple, row group) once
+                CHECK(!topk && p.groups > 1, "xcd layout only for dense multi-group calls");
+                CHECK(p.nq == batch * hkv * p.parts_launched, "triples");
+                CHECK(p.grid == (p.nq + 7) / 8 * 8 * p.groups, "xcd grid");
+                if (p.grid <= (1 << 20)) {
+                  std::vector<unsigned char> seen(size_t(p.nq * p.groups), 0);
+                  for (long long bid = 0; bid < p.grid; ++bid) {
+                    const long long x = bid & 7, sidx = bid >> 3;
+                    const long long gi = sidx % p.groups, q = (sidx / p.groups) * 8 + x;
+                    if (q >= p.nq) continue;
+                    CHECK(bid % 8 == q % 8, "a triple's groups share an XCD");
+                    seen[size_t(q * p.groups + gi)]++;
+                  }
+                  bool once = true;
+                  for (unsigned char v : seen) once = once && v == 1;
+                  CHECK(once, "every (triple, group) exactly once");
+                }
+              }
               if (p.merge) {
                 const long long need = (long long)p.parts_launched * c.rows * 16 * hkv * 130 * 4;
-                CHECK(p.scratch_bytes >= need, "scratch %lld < %lld", (long long)p.scratch_bytes, need);
+                CHECK(p.scratch_bytes - p.counter_bytes >= need, "scratch %lld < %lld",
+                      (long long)(p.scratch_bytes - p.counter_bytes), need);
+                // one 4-byte arrival counter per unit, 256-byte aligned region
+                CHECK(p.counter_bytes >= p.units * 4 && p.counter_bytes % 256 == 0, "counters");
+                CHECK(p.fused_merge == (c.merge_mode == PA_MERGE_IN_KERNEL), "merge mode");
               } else {
                 CHECK(p.scratch_bytes == 0, "no scratch without merge");
               }

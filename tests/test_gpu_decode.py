@@ -153,3 +153,69 @@ def test_workgroup_widths_match_oracle(kw, waves):
         out = case.decode(out=torch.empty_like(case.out), force_parts=parts, workgroup_waves=waves)
         torch.cuda.synchronize()
         compare(out, oracle_out(w), what=f"{w.name} waves={waves} parts={parts}")
+
+
+@pytest.mark.parametrize("kw", [CASES[0], CASES[2], CASES[4], CASES[6], CASES[7], CASES[8], CASES[9]],
+                         ids=["201", "203", "205", "207", "208", "209", "210"])
+@pytest.mark.parametrize("merge_mode", [pa.MERGE_SEPARATE, pa.MERGE_IN_KERNEL])
+def test_merge_modes_match_oracle(kw, merge_mode):
+    """The separate merge kernel and the in-kernel merge (last partition of
+    a unit merges) both match the oracle, over several partition counts."""
+    w = wl.small_case(**kw)
+    case = GpuCase(w)
+    ref = oracle_out(w)
+    for parts in (2, 3, 8, 40):
+        print("merge mode", merge_mode, w.name, parts, flush=True)
+        out = case.decode(out=torch.empty_like(case.out), force_parts=parts, merge_mode=merge_mode)
+        torch.cuda.synchronize()
+        compare(out, ref, what=f"{w.name} merge_mode={merge_mode} parts={parts}")
+
+
+def test_in_kernel_merge_counters_reset_between_calls():
+    """Arrival counters are left at zero by every call: alternating plans
+    (different unit counts and partition counts) on one stream, repeated,
+    give bit-identical outputs each time."""
+    a = GpuCase(wl.small_case(seed=220, ctx=[2500, 900, 60, 1800], q_lens=[1, 1, 1, 1]))
+    b = GpuCase(wl.small_case(seed=221, ctx=[700, 1300], q_lens=[4, 4], Hkv=2))
+    outs = []
+    for rep in range(3):
+        oa = a.decode(out=torch.empty_like(a.out), force_parts=5, merge_mode=pa.MERGE_IN_KERNEL).clone()
+        ob = b.decode(out=torch.empty_like(b.out), force_parts=3, merge_mode=pa.MERGE_IN_KERNEL).clone()
+        oc = a.decode(out=torch.empty_like(a.out), force_parts=11, merge_mode=pa.MERGE_IN_KERNEL).clone()
+        outs.append((oa, ob, oc))
+    torch.cuda.synchronize()
+    for rep in (1, 2):
+        for x, y in zip(outs[0], outs[rep]):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    compare(outs[0][0], oracle_out(a.w), what="a")
+    compare(outs[0][1], oracle_out(b.w), what="b")
+    compare(outs[0][2], oracle_out(a.w), what="a, 11 parts")
+
+
+@pytest.mark.parametrize("merge_mode", [pa.MERGE_SEPARATE, pa.MERGE_IN_KERNEL])
+def test_graph_replays_match_eager(merge_mode):
+    """A captured decode (scratch reserved first, so nothing allocates under
+    capture) replayed several times, with eager calls and synchronisations
+    between the replays, matches the eager result bit for bit every time."""
+    w = wl.small_case(seed=222, ctx=[3000, 1200, 700], q_lens=[1, 1, 1])
+    case = GpuCase(w)
+    stream = torch.cuda.Stream()
+    cfg = pa.make_config(w.Hkv, w.rows, w.B, w.W, force_parts=6, merge_mode=merge_mode)
+    pa.pa_reserve(cfg, stream)
+    with torch.cuda.stream(stream):
+        eager = case.decode(out=torch.empty_like(case.out), force_parts=6, merge_mode=merge_mode).clone()
+    torch.cuda.synchronize()
+    out = torch.empty_like(case.out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        case.decode(out=out, force_parts=6, merge_mode=merge_mode)
+    for rep in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        with torch.cuda.stream(stream):
+            other = case.decode(out=torch.empty_like(case.out), force_parts=3, merge_mode=merge_mode)
+        torch.cuda.synchronize()
+        compare(other, oracle_out(w), what=f"eager between replays {rep}")
+    compare(eager, oracle_out(w), what="eager")

@@ -38,7 +38,8 @@ def test_struct_sizes_match_header_layout():
     # pa_tensor: ptr + 2 x int32 + 12 x int64
     assert ctypes.sizeof(_lib.PaTensor) == 8 + 8 + 6 * 8 * 2
     assert ctypes.sizeof(_lib.PaConfig) == 6 * 4 + 4 * 8 + 4 * 4
-    assert ctypes.sizeof(_lib.PaDecodeOpts) == 4 + 4 + 4 + 4 + 8 + 8 + 4 + 4
+    assert ctypes.sizeof(_lib.PaDecodeOpts) == 4 + 4 + 4 + 4 + 8 + 8 + 4 + 4 + 4 + 4
+    assert ctypes.sizeof(_lib.PaPlanInfo) == 4 * 4 + 6 * 8 + 2 * 4
 
 
 def cfg(**kw):
@@ -116,6 +117,12 @@ def test_plan_shapes_for_the_workloads():
     assert c5["units"] == 16 and c5["parts"] * c5["pages_per_part"] >= 32
     one = pa.pa_plan_describe(cfg(rows=4, batch=4, max_pages=72, force_parts=1))
     assert one["merge"] == 0 and one["scratch_bytes"] == 0
+    dflt = pa.pa_plan_describe(cfg(rows=4, batch=4, max_pages=72))
+    fused = pa.pa_plan_describe(cfg(rows=4, batch=4, max_pages=72, merge_mode=pa.MERGE_IN_KERNEL))
+    sep = pa.pa_plan_describe(cfg(rows=4, batch=4, max_pages=72, merge_mode=pa.MERGE_SEPARATE))
+    assert fused["merge_in_kernel"] == 1 and sep["merge_in_kernel"] == 0 and dflt["merge_in_kernel"] == 0
+    assert fused["scratch_bytes"] == sep["scratch_bytes"]
+    assert pa.pa_query_support(cfg(merge_mode=3)) == -1
 
 
 def _host_tensor(shape, dtype):

@@ -681,95 +681,126 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   if (a.parts > 1 && a.unit_count) merge_if_last(a, unit, row0, nrows, h, &sm_acc[0][0][0]);
 }
 
-// One workgroup per (row, query head): combine the partitions' (m, l, acc)
-// with log-sum-exp weights and write bf16.  Wave w takes partitions
-// w, w+4, ...; lane owns dims 2*lane, 2*lane+1.  Every load of a batch of
-// partitions is issued before any weight is needed, so the kernel costs
-// about one memory round trip per 64 partitions.
-constexpr int kMergeBatch = 16;  // partitions per wave per batch (64 per workgroup)
+// One wavefront per (row, query head): combine the partitions' (m, l, acc)
+// with log-sum-exp weights and write bf16.  Partitions go in batches of up
+// to 64: lane p holds (m, l) of partition p0 + p, so the batch maximum and
+// weight sum are cross-lane reductions; every lane owns dims 2*lane,
+// 2*lane+1 and takes each partition's weight from its lane.  All loads of a
+// batch -- (m, l) and every accumulator -- are issued together, so a batch
+// costs one memory round trip; no barrier, no LDS.  N: accumulator loads
+// per batch (the partition count rounded up to 8, 16, 32 or 64).
+// Cross-lane max / sum of a wave without LDS: DPP within rows of 16 lanes
+// (swap neighbours, swap pairs, rotate by 4, rotate by 8 -- every lane of a
+// row then holds the row's result), then the four rows through readlane.
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce_dpp(float v) {
+  auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+  int b = __builtin_bit_cast(int, v);
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
+  b = __builtin_bit_cast(int, v);
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
+  b = __builtin_bit_cast(int, v);
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0x124, 0xF, 0xF, false)));  // row_ror 4
+  b = __builtin_bit_cast(int, v);
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0x128, 0xF, 0xF, false)));  // row_ror 8
+  b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return op(op(r0, r1), op(r2, r3));
+}
 
-__global__ __launch_bounds__(256) void pa_merge(DecodeArgs a) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// One wave's share of a (row, query head): partitions [q0, q1), merged into
+// (M, L, ox, oy) relative to its own running maximum M.
+template <int N>
+__device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t base, int q0, int q1, float& M,
+                                            float& L, float& ox, float& oy) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t stride_p = int64_t(a.rows) * (16 * a.hkv);  // between partitions
+  for (int p0 = q0; p0 < q1; p0 += N) {
+    const int cnt = min(N, q1 - p0);
+    float2 v[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int p = p0 + min(j, cnt - 1);
+      v[j] = *reinterpret_cast<const float2*>(a.part_acc + (p * stride_p + base) * 128 + 2 * lane);
+    }
+    float2 ml = {-INFINITY, 0.0f};
+    if (lane < cnt) ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * ((p0 + lane) * stride_p + base));
+    const float Mn = fmaxf(M, wave_reduce_dpp<true>(ml.x));
+    const float keep = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+    const float w = (ml.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml.x - Mn);
+    L = L * keep + wave_reduce_dpp<false>(w * ml.y);
+    ox *= keep;
+    oy *= keep;
+    M = Mn;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const float wj = lane_value(w, j);
+      if (j < cnt && wj != 0.0f) {
+        ox += wj * v[j].x;
+        oy += wj * v[j].y;
+      }
+    }
+  }
+}
+
+// blockDim.x / 64 waves per (row, query head), each merging a contiguous
+// share of the partitions in one memory round trip (up to 16 of them);
+// the waves' results combine through LDS.
+__global__ __launch_bounds__(4 * kWave) void pa_merge(DecodeArgs a) {
+  __shared__ float sm_ml[4][2];
+  __shared__ float2 sm_o[4][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
   const int Hq = 16 * a.hkv;
   const int64_t pair = blockIdx.x;
   const int row = int(pair / Hq);
   const int qh = int(pair - int64_t(row) * Hq);
+  const int64_t base = int64_t(row) * Hq + qh;
+  const int P = a.parts;
+  const int share = (P + nw - 1) / nw;
+  const int q0 = min(P, wave * share), q1 = min(P, q0 + share);
 
   // Every launched partition left a partial; empty ones have m = -inf and
   // weight 0 (their accumulators are never read into the sum).
-  const int P = a.parts;
-
-  __shared__ float sm_w[256];
-  __shared__ float sm_red[2][4];
-  __shared__ float2 sm_acc[4][64];
-  const int64_t stride_p = int64_t(a.rows) * Hq;  // between partitions
-  const int64_t base = int64_t(row) * Hq + qh;
-
-  float ox = 0.0f, oy = 0.0f, Ls = 0.0f;
-  for (int p0 = 0; p0 < P; p0 += 4 * kMergeBatch) {
-    const int cnt = min(4 * kMergeBatch, P - p0);
-    // accumulators of this wave's partitions in the batch (independent loads)
-    float2 v[kMergeBatch];
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const int pj = 4 * j + wave;
-      v[j] = pj < cnt ? *reinterpret_cast<const float2*>(a.part_acc + ((p0 + pj) * stride_p + base) * 128 +
-                                                          2 * lane)
-                      : float2{0.f, 0.f};
+  float M = -INFINITY, L = 0.0f, ox = 0.0f, oy = 0.0f;
+  if (share <= 8) merge_range<8>(a, base, q0, q1, M, L, ox, oy);
+  else if (share <= 16) merge_range<16>(a, base, q0, q1, M, L, ox, oy);
+  else merge_range<32>(a, base, q0, q1, M, L, ox, oy);
+  if (nw > 1) {
+    if (lane == 0) {
+      sm_ml[wave][0] = M;
+      sm_ml[wave][1] = L;
     }
-    // (m, l) of the batch: thread t < cnt holds partition p0 + t
-    const int t = threadIdx.x;
-    float m = -INFINITY, l = 0.0f;
-    if (t < cnt) {
-      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * ((p0 + t) * stride_p + base));
-      m = ml.x;
-      l = ml.y;
+    sm_o[wave][lane] = float2{ox, oy};
+    __syncthreads();
+    if (wave != 0) return;
+    float Mt = -INFINITY;
+    for (int w = 0; w < nw; ++w) Mt = fmaxf(Mt, sm_ml[w][0]);
+    L = 0.0f;
+    ox = oy = 0.0f;
+    for (int w = 0; w < nw; ++w) {
+      const float f = (sm_ml[w][0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sm_ml[w][0] - Mt);
+      if (f != 0.0f) {
+        L += f * sm_ml[w][1];
+        ox += f * sm_o[w][lane].x;
+        oy += f * sm_o[w][lane].y;
+      }
     }
-    float wm = wave_max(m);
-    if (lane == 0) sm_red[0][wave] = wm;
-    __syncthreads();
-    const float Mb = fmaxf(fmaxf(sm_red[0][0], sm_red[0][1]), fmaxf(sm_red[0][2], sm_red[0][3]));
-    // running combination across batches (only one batch unless P > 64)
-    float M = Mb;
-    float scale_old = 1.0f;
-    if (p0 > 0) {
-      M = fmaxf(Mb, sm_red[1][0]);
-      scale_old = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sm_red[1][0] - M);
-    }
-    const float wgt = (M == -INFINITY || t >= cnt) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-    sm_w[t] = wgt;
-    const float lw = wave_sum(wgt * l);
-    __syncthreads();
-    if (lane == 0) sm_red[0][wave] = lw;
-    __syncthreads();
-    Ls = Ls * scale_old + (sm_red[0][0] + sm_red[0][1] + sm_red[0][2] + sm_red[0][3]);
-    ox *= scale_old;
-    oy *= scale_old;
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const float wj = sm_w[4 * j + wave];
-      ox += wj != 0.0f ? wj * v[j].x : 0.0f;
-      oy += wj != 0.0f ? wj * v[j].y : 0.0f;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) sm_red[1][0] = M;
-    __syncthreads();
   }
-  sm_acc[wave][lane] = float2{ox, oy};
-  __syncthreads();
-  if (wave == 0) {
-    float2 s0 = sm_acc[0][lane], s1 = sm_acc[1][lane], s2 = sm_acc[2][lane], s3 = sm_acc[3][lane];
-    const float sx = (s0.x + s1.x) + (s2.x + s3.x);
-    const float sy = (s0.y + s1.y) + (s2.y + s3.y);
-    float v_fold = 1.0f;
-    if (a.scale_mode != PA_SCALE_PER_TOKEN && a.v_scale) v_fold = *a.v_scale;
-    const float inv = Ls > 0.0f ? v_fold / Ls : 0.0f;
-    const uint32_t packed =
-        uint32_t(f32_to_bf16_rne(sx * inv)) | (uint32_t(f32_to_bf16_rne(sy * inv)) << 16);
-    *reinterpret_cast<uint32_t*>(a.out + int64_t(row) * a.out_row_stride +
-                                 int64_t(qh) * a.out_head_stride + 2 * lane) = packed;
-  }
+  float v_fold = 1.0f;
+  if (a.scale_mode != PA_SCALE_PER_TOKEN && a.v_scale) v_fold = *a.v_scale;
+  const float inv = L > 0.0f ? v_fold / L : 0.0f;
+  const uint32_t packed = uint32_t(f32_to_bf16_rne(ox * inv)) | (uint32_t(f32_to_bf16_rne(oy * inv)) << 16);
+  *reinterpret_cast<uint32_t*>(a.out + int64_t(row) * a.out_row_stride + int64_t(qh) * a.out_head_stride +
+                               2 * lane) = packed;
 }
 
 // With events, the dispatch itself records them (start and end of this
@@ -832,7 +863,9 @@ hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool spa
   if (e != hipSuccess) return e;
   if (merge && !a.unit_count) {
     const int64_t pairs = int64_t(a.rows) * 16 * a.hkv;
-    hipLaunchKernelGGL(pa_merge, dim3(uint32_t(pairs)), dim3(256), 0, stream, a);
+    // one wave per 16 partitions, at most four
+    const int waves = a.parts <= 16 ? 1 : (a.parts <= 32 ? 2 : 4);
+    hipLaunchKernelGGL(pa_merge, dim3(uint32_t(pairs)), dim3(kWave * waves), 0, stream, a);
     e = hipGetLastError();
   }
   return e;

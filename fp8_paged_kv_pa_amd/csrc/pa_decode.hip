@@ -278,6 +278,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   const int s0 = n0 + ps;       // this wave's first list position
   int h, b, row0, nrows, lim0;  // row row0+i sees tokens t < lim0 + i
   int first_entry;              // dense: block_table[b][s0]; sparse: sparse_idx[row0][s0] (-1 past the end)
+  int second_entry = -1;        // dense: block_table[b][s0 + S], read with the first
   if constexpr (SPARSE) {
     h = int(unit % a.hkv);
     row0 = int(unit / a.hkv);
@@ -299,6 +300,9 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     h = int(bh % a.hkv);
     b = int(bh / a.hkv);
     first_entry = s0 < a.width ? as_const(a.block_table + int64_t(b) * a.bt_stride)[s0] : -1;
+    // the next position's entry travels with the first: its page's loads
+    // need not wait for a second table round trip after the context length
+    second_entry = s0 + S < a.width ? as_const(a.block_table + int64_t(b) * a.bt_stride)[s0 + S] : -1;
     const int ctx = a.context_lens[b];
     int start, L;
     if (a.cu_seqlens_q) {
@@ -403,7 +407,11 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   // raw physical page of logical page ln (read only if the position is usable)
   auto raw_at = [&](int n, int ln) -> int {
     if (!logical_ok(n, ln)) return -1;
-    return (!SPARSE && n == s0) ? first_entry : bt_c[ln];
+    if constexpr (!SPARSE) {
+      if (n == s0) return first_entry;
+      if (n == s0 + S) return second_entry;
+    }
+    return bt_c[ln];
   };
   auto valid_page = [&](int P) -> bool { return P >= 0 && P < a.num_blocks; };
   auto process = [&](Chunk<BF>& c, int tbase) {

@@ -334,19 +334,19 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   }
   // query operands: B of S^T = K Q^T, lane = (head hr, dims 8g..8g+7 of
   // each 32-dim k-step)
+  // A workgroup with fewer rows than RT (the last group of an odd q_len)
+  // computes its missing row as a copy of its last real row and never writes
+  // it: the per-chunk code then has no per-row branches, so the scheduler
+  // can interleave the rows' MFMA chains.
   static_assert(RT == 1 || RT == 2, "a workgroup carries one or two query rows");
   bf16x8 qop[RT][4];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (r < nrows) {
-        const uint16_t* qp = a.q + int64_t(row0 + r) * a.q_row_stride +
-                             int64_t(16 * h + hr) * a.q_head_stride + 32 * j + 8 * g;
-        qop[r][j] = *reinterpret_cast<const bf16x8*>(qp);
-      } else {
-        qop[r][j] = bf16x8{};
-      }
+      const uint16_t* qp = a.q + int64_t(row0 + min(r, nrows - 1)) * a.q_row_stride +
+                           int64_t(16 * h + hr) * a.q_head_stride + 32 * j + 8 * g;
+      qop[r][j] = *reinterpret_cast<const bf16x8*>(qp);
     }
   }
 
@@ -490,7 +490,6 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       }
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
-        if (r >= nrows) break;
         const bf16x8 qv = qop[r][j];
         st[r][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qv, st[r][0], 0, 0, 0);
         st[r][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qv, st[r][1], 0, 0, 0);
@@ -504,14 +503,13 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     bf16x8 phi[RT], plo[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      if (r >= nrows) break;
       float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         x[e] = st[r][0][e] * kc[e];
         x[4 + e] = st[r][1][e] * kc[4 + e];
       }
-      const int lim_r = min(lim0 + r, cap);
+      const int lim_r = min(lim0 + min(r, nrows - 1), cap);
       if (!full) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -566,7 +564,6 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       else vop = fp8x8_to_bf16x8(c.v[d >> 1][2 * (d & 1)], c.v[d >> 1][2 * (d & 1) + 1]);
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
-        if (r >= nrows) break;
         acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi[r], acc[r][d], 0, 0, 0);
         acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[r], acc[r][d], 0, 0, 0);
       }

@@ -138,21 +138,35 @@ constexpr int kMinBlocks = (NBUF2_NW4 && !(BF && RT == 2)) ? 2 : 1;
 // Threads < 256: (head oh, 8 dims od) as in the wave merge.  sm_w holds
 // 16 x kMaxParts weights (LDS of the finished wave merge).
 constexpr int kMaxMergeParts = 256;
+
+// Partials of the in-kernel merge travel through device-scope (relaxed
+// atomic) 64-bit stores and loads: they are coherent across the XCDs'
+// L2s by themselves, so publishing a partial needs only its stores to be
+// complete -- no L2 writeback or invalidate.
+__device__ __forceinline__ void store_coherent(float* p, float x, float y) {
+  const uint64_t v = uint64_t(__float_as_uint(x)) | (uint64_t(__float_as_uint(y)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_coherent(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return float2{__uint_as_float(uint32_t(v)), __uint_as_float(uint32_t(v >> 32))};
+}
+// s_waitcnt vmcnt(0): every vector memory operation of this wave -- here
+// the coherent partial stores -- has completed.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 constexpr int kMergeChunk = 8;  // partitions whose accumulators are loaded together
 
 __device__ void merge_if_last(const DecodeArgs& a, int64_t unit, int row0, int nrows, int h, float* sm_w) {
   __shared__ int sm_last;
-  // The barrier completes every wave's partial stores; one device-scope
-  // fence by thread 0 then publishes them all (a fence writes back and
-  // invalidates the XCD's L2, so it is issued once per workgroup, not per
-  // wave).
+  // Each wave waits for its coherent partial stores to complete, the
+  // barrier makes that true for the whole workgroup, and only then does
+  // thread 0 count the partition in.
+  wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();  // release
-    const bool last = atomicAdd(a.unit_count + unit, 1u) == uint32_t(a.parts - 1);
-    if (last) __threadfence();  // acquire: every other partition's partial
-    sm_last = last;
-  }
+  if (threadIdx.x == 0)
+    sm_last = __hip_atomic_fetch_add(a.unit_count + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              uint32_t(a.parts - 1);
   __syncthreads();
   if (!sm_last) return;
   const int t = threadIdx.x;
@@ -173,8 +187,7 @@ __device__ void merge_if_last(const DecodeArgs& a, int64_t unit, int row0, int n
 #pragma unroll
       for (int i = 0; i < kMaxMergeParts / 16; ++i) {
         const int p = li + 16 * i;
-        ml[i] = p < P ? *reinterpret_cast<const float2*>(a.part_ml + 2 * (p * stride_p + base))
-                      : float2{-INFINITY, 0.0f};
+        ml[i] = p < P ? load_coherent(a.part_ml + 2 * (p * stride_p + base)) : float2{-INFINITY, 0.0f};
         M = fmaxf(M, ml[i].x);
       }
 #pragma unroll
@@ -197,9 +210,11 @@ __device__ void merge_if_last(const DecodeArgs& a, int64_t unit, int row0, int n
 #pragma unroll
         for (int j = 0; j < kMergeChunk; ++j) {
           const int p = min(p0 + j, P - 1);
-          const f32x4* ap = reinterpret_cast<const f32x4*>(a.part_acc + (p * stride_p + base) * 128 + od);
-          v0[j] = ap[0];
-          v1[j] = ap[1];
+          const float* ap = a.part_acc + (p * stride_p + base) * 128 + od;
+          const float2 x0 = load_coherent(ap), x1 = load_coherent(ap + 2);
+          const float2 x2 = load_coherent(ap + 4), x3 = load_coherent(ap + 6);
+          v0[j] = f32x4{x0.x, x0.y, x1.x, x1.y};
+          v1[j] = f32x4{x2.x, x2.y, x3.x, x3.y};
         }
 #pragma unroll
         for (int j = 0; j < kMergeChunk; ++j) {
@@ -224,7 +239,7 @@ __device__ void merge_if_last(const DecodeArgs& a, int64_t unit, int row0, int n
     }
     __syncthreads();
   }
-  if (t == 0) atomicExch(a.unit_count + unit, 0u);
+  if (t == 0) __hip_atomic_store(a.unit_count + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int RT, bool PER_TOKEN, bool SPARSE, int NBUF, int NW, bool BF>
@@ -367,7 +382,8 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     if (threadIdx.x < 16 * nrows) {
       const int r = threadIdx.x >> 4;
       const int64_t pi = (int64_t(part) * a.rows + row0 + r) * Hq + 16 * h + (threadIdx.x & 15);
-      *reinterpret_cast<float2*>(a.part_ml + 2 * pi) = float2{-INFINITY, 0.0f};
+      if (a.unit_count) store_coherent(a.part_ml + 2 * pi, -INFINITY, 0.0f);
+      else *reinterpret_cast<float2*>(a.part_ml + 2 * pi) = float2{-INFINITY, 0.0f};
     }
     if (a.unit_count) merge_if_last(a, unit, row0, nrows, h, &sm_acc[0][0][0]);
     return;
@@ -672,12 +688,21 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
         *reinterpret_cast<u32x4*>(op) = u32x4{packed[0], packed[1], packed[2], packed[3]};
       } else {
         const int64_t pi = (int64_t(part) * a.rows + row) * Hq + qh;
-        f32x4* ap = reinterpret_cast<f32x4*>(a.part_acc + pi * 128 + od);
-        ap[0] = s0v;
-        ap[1] = s1v;
-        if ((t & 15) == 0) {
-          a.part_ml[2 * pi] = Mo;
-          a.part_ml[2 * pi + 1] = Ls;
+        if (a.unit_count) {
+          float* ap = a.part_acc + pi * 128 + od;
+          store_coherent(ap, s0v[0], s0v[1]);
+          store_coherent(ap + 2, s0v[2], s0v[3]);
+          store_coherent(ap + 4, s1v[0], s1v[1]);
+          store_coherent(ap + 6, s1v[2], s1v[3]);
+          if ((t & 15) == 0) store_coherent(a.part_ml + 2 * pi, Mo, Ls);
+        } else {
+          f32x4* ap = reinterpret_cast<f32x4*>(a.part_acc + pi * 128 + od);
+          ap[0] = s0v;
+          ap[1] = s1v;
+          if ((t & 15) == 0) {
+            a.part_ml[2 * pi] = Mo;
+            a.part_ml[2 * pi + 1] = Ls;
+          }
         }
       }
     }

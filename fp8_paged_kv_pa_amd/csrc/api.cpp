@@ -362,6 +362,7 @@ int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tens
     return fail(PA_ERR_UNSUPPORTED, "a bfloat16 cache is unquantized: scale_mode must be PA_SCALE_NONE");
   if ((rc = check_scales(k_scale, v_scale, scale_mode, nb, hkv))) return rc;
   if (T == 0) return PA_OK;
+  if (T * hkv > kMaxGrid) return fail(PA_ERR_CAPACITY, "too many (token, KV head) pairs for one launch");
 
   WriteArgs a{};
   a.k_new = k_new->data;

@@ -130,6 +130,12 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
   }
   if (p.scratch_bytes > kMaxScratchBytes)
     return fail(err, PA_ERR_CAPACITY, "split-K scratch for this bucket exceeds 4 GiB");
+  // one launch carries at most 2^31 - 1 workgroups; a ragged call whose
+  // max_q_len is unknown plans for rows-long requests and can exceed it
+  if (p.grid > kMaxGrid)
+    return fail(err, PA_ERR_CAPACITY,
+                "the decode grid (" + std::to_string(p.grid) + " workgroups) exceeds one launch" +
+                    (c.ragged && c.max_q_len == 0 ? "; give max_q_len for a ragged call" : ""));
   *out = p;
   if (err) err->clear();
   return PA_OK;

@@ -31,6 +31,7 @@ constexpr int64_t kMaxTopk = 4096;
 constexpr int32_t kMaxKvHeads = 64;
 constexpr int32_t kMaxParts = 256;
 constexpr int64_t kMaxScratchBytes = int64_t(4) << 30;
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // workgroups in one launch
 
 // Workgroups the plan aims for: about one per CU (256 CUs).  Measured on
 // the 128K and 8K decode shapes, one long-running 4-wave workgroup per CU

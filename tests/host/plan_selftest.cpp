@@ -72,6 +72,11 @@ int main() {
     CHECK(make_plan(c, &p, &err) == PA_OK, "121 rows ragged");
     c = base(); c.rows = kMaxRows + 1; c.batch = 1;
     CHECK(make_plan(c, &p, &err) == PA_ERR_CAPACITY, "rows cap");
+    c = base(); c.rows = 65536; c.batch = 65536; c.ragged = 1; c.num_kv_heads = 64; c.max_pages = 1024;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_CAPACITY && err.find("max_q_len") != std::string::npos,
+          "grid beyond one launch");
+    c.max_q_len = 1;
+    CHECK(make_plan(c, &p, &err) == PA_OK && p.grid <= kMaxGrid, "grid with max_q_len");
     c = base(); c.force_parts = 300;
     CHECK(make_plan(c, &p, &err) == PA_ERR_INVALID_ARG, "force parts");
     c = base(); c.batch = 0;
@@ -121,6 +126,7 @@ int main() {
               CHECK(p.merge == (p.parts_launched > 1), "merge flag");
               const long long units = topk ? c.rows * hkv : batch * hkv * p.groups;
               CHECK(p.units == units, "units");
+              CHECK(p.grid >= 1 && p.grid <= kMaxGrid, "grid within one launch");
               if (!p.xcd_grouped) {
                 CHECK(p.grid == units * p.parts_launched, "grid");
               } else {

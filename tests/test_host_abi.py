@@ -92,6 +92,17 @@ def test_capacity_refusals():
     assert pa.pa_query_support(cfg(max_pages=(1 << 20) + 1)) == -6
 
 
+def test_grid_beyond_one_launch_is_refused():
+    """A ragged call with no max_q_len plans every request as rows long; with
+    many requests that needs more than 2^31 - 1 workgroups: refused with a
+    pointer to max_q_len, never truncated."""
+    big = cfg(rows=65536, batch=65536, ragged=True, max_pages=1024, num_kv_heads=64)
+    assert pa.pa_query_support(big) == -6
+    assert "max_q_len" in pa.pa_last_error()
+    assert pa.pa_query_support(cfg(rows=65536, batch=65536, ragged=True, max_pages=1024, num_kv_heads=64,
+                                   max_q_len=1)) == 0
+
+
 def test_plans_and_scratch_depend_only_on_buckets():
     """Every row count inside one power-of-two bucket maps to the same
     partition count and scratch size; the set of scratch sizes is bounded by

@@ -12,7 +12,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -53,17 +52,31 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
   return sign | code;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// Cross-lane max / sum of a wave without LDS: DPP within rows of 16 lanes
+// (swap neighbours, swap pairs, rotate by 4, rotate by 8 -- every lane of a
+// row then holds the row's result), then the four rows through readlane.
+// Every lane gets the result.
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce(float v) {
+  auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+  int b = __builtin_bit_cast(int, v);
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
+  b = __builtin_bit_cast(int, v);
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
+  b = __builtin_bit_cast(int, v);
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0x124, 0xF, 0xF, false)));  // row_ror 4
+  b = __builtin_bit_cast(int, v);
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0x128, 0xF, 0xF, false)));  // row_ror 8
+  b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return op(op(r0, r1), op(r2, r3));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce<true>(v); }
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce<false>(v); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);

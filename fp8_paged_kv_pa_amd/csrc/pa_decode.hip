@@ -719,28 +719,6 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
 // batch -- (m, l) and every accumulator -- are issued together, so a batch
 // costs one memory round trip; no barrier, no LDS.  N: accumulator loads
 // per batch (the partition count rounded up to 8, 16, 32 or 64).
-// Cross-lane max / sum of a wave without LDS: DPP within rows of 16 lanes
-// (swap neighbours, swap pairs, rotate by 4, rotate by 8 -- every lane of a
-// row then holds the row's result), then the four rows through readlane.
-template <bool MAX>
-__device__ __forceinline__ float wave_reduce_dpp(float v) {
-  auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
-  int b = __builtin_bit_cast(int, v);
-  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
-  b = __builtin_bit_cast(int, v);
-  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
-  b = __builtin_bit_cast(int, v);
-  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0x124, 0xF, 0xF, false)));  // row_ror 4
-  b = __builtin_bit_cast(int, v);
-  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0x128, 0xF, 0xF, false)));  // row_ror 8
-  b = __builtin_bit_cast(int, v);
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
-  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
-  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-  return op(op(r0, r1), op(r2, r3));
-}
-
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
@@ -762,10 +740,10 @@ __device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t base, i
     }
     float2 ml = {-INFINITY, 0.0f};
     if (lane < cnt) ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * ((p0 + lane) * stride_p + base));
-    const float Mn = fmaxf(M, wave_reduce_dpp<true>(ml.x));
+    const float Mn = fmaxf(M, wave_max(ml.x));
     const float keep = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
     const float w = (ml.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml.x - Mn);
-    L = L * keep + wave_reduce_dpp<false>(w * ml.y);
+    L = L * keep + wave_sum(w * ml.y);
     ox *= keep;
     oy *= keep;
     M = Mn;

@@ -21,10 +21,13 @@
 // 16*tau + r; k-step j takes dims 32g + 8j .. +7 of that run, and the query
 // operand takes the same dims, so the dot product is over every dim once.
 //
-// index_topk_kernel: one workgroup per row.  A four-pass, 8-bit radix
-// select finds the k-th largest score (scores mapped to order-preserving
-// unsigned keys); a block-wide scan then writes the chosen pages in
-// ascending order, taking ties at the threshold from the lowest page up.
+// index_topk_kernel: one workgroup per row.  Scores are mapped to
+// order-preserving unsigned keys; bytes that all finite keys of the row
+// share are skipped, and an 8-bit radix select over the rest finds the k-th
+// largest (LDS histograms, the digit search by one wave, two barriers per
+// byte); once at most 64 keys share the bytes chosen so far, one wave ranks
+// those few directly.  A block-wide scan then writes the chosen pages in ascending
+// order, taking ties at the threshold from the lowest page up.
 #include "device_common.h"
 #include "launch.h"
 
@@ -33,8 +36,9 @@ namespace fp8pa {
 namespace {
 
 constexpr int kIdxWaves = 4;     // pages per score workgroup (one per wave)
-constexpr int kTopkThreads = 256;  // one thread per radix bin in the digit search
+constexpr int kTopkThreads = 256;  // one histogram entry per thread
 constexpr int kStageKeys = 8192;   // rows with up to this many pages keep their keys in LDS
+constexpr int kLoadBatch = 8;      // key loads a thread issues before using them
 
 typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
 __device__ __forceinline__ const_i32_ptr as_const(const int32_t* p) { return (const_i32_ptr)(p); }
@@ -142,48 +146,92 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Block-wide exclusive scan of one value per thread (kTopkThreads threads);
-// also returns the total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* sm_wave) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += y;
-  }
-  if (lane == kWave - 1) sm_wave[wave] = inc;
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkThreads / kWave; ++w) {
-    const int s = sm_wave[w];
-    if (w < wave) before += s;
-    tot += s;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + inc - v;
+// Unsigned add / max / min over a wave without LDS: DPP within rows of 16
+// lanes (swap neighbours, swap pairs, rotate by 4, rotate by 8), then the
+// four rows through readlane.  Every lane gets the result.
+enum class UOp { ADD, MAX, MIN };
+template <UOp OP>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+  auto op = [](uint32_t x, uint32_t y) { return OP == UOp::ADD ? x + y : (OP == UOp::MAX ? max(x, y) : min(x, y)); };
+  int b = int(v);
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
+  b = int(v);
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(b, b, 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
+  b = int(v);
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(b, b, 0x124, 0xF, 0xF, false)));  // row_ror 4
+  b = int(v);
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(b, b, 0x128, 0xF, 0xF, false)));  // row_ror 8
+  b = int(v);
+  return op(op(uint32_t(__builtin_amdgcn_readlane(b, 0)), uint32_t(__builtin_amdgcn_readlane(b, 16))),
+            op(uint32_t(__builtin_amdgcn_readlane(b, 32)), uint32_t(__builtin_amdgcn_readlane(b, 48))));
+}
+
+// Inclusive prefix sum over a wave by DPP: within rows of 16 lanes (add
+// the lane 1, 2, 4, 8 below; lanes with no such lane in the row add 0),
+// then across rows (lane 15 of rows 0 and 2 into rows 1 and 3, then lane
+// 31 into rows 2 and 3).
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr 1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr 2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr 4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr 8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast 15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast 31
+  return x;
+}
+
+// One histogram increment per active lane with act set.  The lanes that
+// share the first such lane's bin add their count with one atomic (the
+// common case in the leading digits, where a row's keys crowd into a few
+// bins); the others add one each.
+__device__ __forceinline__ void add_to_bin(int* hist, bool act, uint32_t bin) {
+  const uint64_t am = __builtin_amdgcn_ballot_w64(act);
+  if (am == 0) return;
+  const int leader = __builtin_ctzll(am);
+  const uint32_t lb = uint32_t(__builtin_amdgcn_readlane(int(bin), leader));
+  const uint64_t same = __builtin_amdgcn_ballot_w64(act && bin == lb);
+  if (!act) return;
+  if (bin != lb) atomicAdd(&hist[bin], 1);
+  else if (int(threadIdx.x & (kWave - 1)) == leader) atomicAdd(&hist[lb], __builtin_popcountll(same));
 }
 
 __global__ __launch_bounds__(kTopkThreads) void index_topk_kernel(IndexArgs a) {
-  __shared__ int hist[256];
-  __shared__ int sm_wave[kTopkThreads / kWave];
-  __shared__ uint32_t sm_sel[2];  // threshold digit result, remaining count
+  static_assert(kTopkThreads == 4 * kWave, "one histogram entry per thread, digit search by wave 0");
+  __shared__ __align__(16) int hist[2][256];  // double-buffered digit histograms
+  __shared__ uint32_t sm_stat[3][kTopkThreads / kWave];  // per wave: finite count, max key, min finite key
+  __shared__ uint32_t sm_sel[3];              // chosen digit, keys still to take at it, keys with it
+  __shared__ uint32_t sm_cand[kWave];         // the last few candidate keys
+  __shared__ int sm_ncand;
+  __shared__ int sm_scan[2][kTopkThreads / kWave];
   __shared__ uint32_t sm_keys[kStageKeys];
   const int row = blockIdx.x;
   const int t = threadIdx.x;
+  const int lane = t & (kWave - 1), wave = t >> 6;
 
-  // the request of this row and its visible page count
+  const float* srow = a.scores + int64_t(row) * a.score_stride;
+  int32_t* orow = a.out_idx + int64_t(row) * a.out_stride;
+  const int k = a.topk;
+
+  // the first batch of the row's scores, requested before the row's length
+  // is known (every entry below the table width is inside the matrix), so
+  // its latency overlaps the request lookup
+  float first[kLoadBatch];
+#pragma unroll
+  for (int j = 0; j < kLoadBatch; ++j) {
+    const int i = j * kTopkThreads + t;
+    first[j] = i < a.width ? srow[i] : -INFINITY;
+  }
+
+  // the request of this row (with nondecreasing cu_seqlens_q: the number of
+  // request starts after the first at or before the row, counted by each
+  // wave with ballots) and its visible page count
   int b, start, L;
   if (a.cu_seqlens_q) {
-    int lo = 0, hi = a.batch;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.cu_seqlens_q[mid] <= row) lo = mid; else hi = mid;
+    b = 0;
+    for (int base = 1; base < a.batch; base += kWave) {
+      const int j = base + lane;
+      b += __builtin_popcountll(__builtin_amdgcn_ballot_w64(j < a.batch && a.cu_seqlens_q[j] <= row));
     }
-    b = lo;
     start = min(max(a.cu_seqlens_q[b], 0), a.rows);
     L = min(max(a.cu_seqlens_q[b + 1], start), a.rows) - start;
   } else {
@@ -193,87 +241,197 @@ __global__ __launch_bounds__(kTopkThreads) void index_topk_kernel(IndexArgs a) {
   }
   const int lim = max(0, min(a.context_lens[b] - L + (row - start) + 1, a.width * 128));
   const int n = (lim + 127) >> 7;  // pages the row can see
-  const float* srow = a.scores + int64_t(row) * a.score_stride;
-  int32_t* orow = a.out_idx + int64_t(row) * a.out_stride;
-  const int k = a.topk;
 
-  // keys of the row: staged once in LDS (coalesced read) when they fit,
-  // else read from the score matrix on every pass
+  // one coalesced pass over the row: keys staged in LDS when they fit (else
+  // read from the score matrix on every pass), the finite count and the
+  // range of the finite keys
   const bool staged = n <= kStageKeys;
-  if (staged) {
-    for (int i = t; i < n; i += kTopkThreads) sm_keys[i] = score_key(srow[i]);
-    __syncthreads();
-  }
-  auto key_at = [&](int i) -> uint32_t { return staged ? sm_keys[i] : score_key(srow[i]); };
-
-  // this thread's contiguous slice of the row's pages
-  const int chunk = (n + kTopkThreads - 1) / kTopkThreads;
-  const int c0 = min(n, t * chunk), c1 = min(n, c0 + chunk);
-
-  int fin = 0;
-  for (int i = c0; i < c1; ++i) fin += key_at(i) != 0u;
-  int total_fin;
-  block_exclusive_scan(fin, &total_fin, sm_wave);
-
-  uint32_t thr = 1u;  // keys >= thr are candidates; 1 keeps every finite score
-  int need_eq = 0;    // ties at the threshold still to take (lowest pages first)
-  if (total_fin > k) {
-    uint32_t prefix = 0, mask = 0;
-    int rem = k;
-    for (int d = 3; d >= 0; --d) {
-      const int sh = 8 * d;
-      for (int i = t; i < 256; i += kTopkThreads) hist[i] = 0;
-      __syncthreads();
-      for (int i = c0; i < c1; ++i) {
-        const uint32_t key = key_at(i);
-        if (key != 0u && (key & mask) == prefix) atomicAdd(&hist[(key >> sh) & 255u], 1);
+  // fn(i, key) for pages i = from + t, from + t + 256, ...  From LDS one
+  // page at a time; from the score matrix in batches of kLoadBatch loads
+  // issued together (one load latency per batch, not per page), where past
+  // the row's end fn sees key 0, the key of -inf
+  auto for_keys = [&](int from, bool from_lds, auto&& fn) {
+    if (from_lds) {
+      for (int i = from + t; i < n; i += kTopkThreads) fn(i, sm_keys[i]);
+      return;
+    }
+    for (int base = from; base < n; base += kLoadBatch * kTopkThreads) {
+      uint32_t kk[kLoadBatch];
+#pragma unroll
+      for (int j = 0; j < kLoadBatch; ++j) {
+        const int i = base + j * kTopkThreads + t;
+        kk[j] = i < n ? score_key(srow[i]) : 0u;
       }
-      __syncthreads();
-      // the digit D with count(digit > D) < rem <= count(digit >= D): thread
-      // t holds digit 255 - t, an exclusive scan gives count(digit > D)
-      {
-        const int D = 255 - t;
-        const int cnt = hist[D];
-        int tot;
-        const int above = block_exclusive_scan(cnt, &tot, sm_wave);
-        if (above < rem && rem <= above + cnt) {
-          sm_sel[0] = uint32_t(D);
-          sm_sel[1] = uint32_t(rem - above);
+#pragma unroll
+      for (int j = 0; j < kLoadBatch; ++j) fn(base + j * kTopkThreads + t, kk[j]);
+    }
+  };
+  uint32_t fin = 0u, khi = 0u, klo = 0xFFFFFFFFu;
+  auto stage = [&](int i, uint32_t key) {
+    if (staged && i < n) sm_keys[i] = key;
+    fin += key != 0u;
+    khi = max(khi, key);
+    klo = min(klo, key ? key : 0xFFFFFFFFu);
+  };
+#pragma unroll
+  for (int j = 0; j < kLoadBatch; ++j) {
+    const int i = j * kTopkThreads + t;
+    stage(i, i < n ? score_key(first[j]) : 0u);
+  }
+  for_keys(kLoadBatch * kTopkThreads, false, stage);
+  auto key_at = [&](int i) -> uint32_t { return staged ? sm_keys[i] : score_key(srow[i]); };
+  hist[0][t] = 0;
+  hist[1][t] = 0;
+  if (t == 0) sm_ncand = 0;
+  fin = wave_reduce_u32<UOp::ADD>(fin);
+  khi = wave_reduce_u32<UOp::MAX>(khi);
+  klo = wave_reduce_u32<UOp::MIN>(klo);
+  if (lane == 0) {
+    sm_stat[0][wave] = fin;
+    sm_stat[1][wave] = khi;
+    sm_stat[2][wave] = klo;
+  }
+  __syncthreads();
+  int total_fin = 0;
+  khi = 0u;
+  klo = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / kWave; ++w) {
+    total_fin += int(sm_stat[0][w]);
+    khi = max(khi, sm_stat[1][w]);
+    klo = min(klo, sm_stat[2][w]);
+  }
+
+  // the k-th largest key (thr) and how many keys equal to it are taken;
+  // without a selection every finite key is taken
+  const bool select = total_fin > k;
+  uint32_t thr = 1u;
+  int need_eq = 0;
+  if (select) {
+    const uint32_t diff = khi ^ klo;
+    if (diff == 0u) {  // every finite key is the same
+      thr = khi;
+      need_eq = k;
+    } else {
+      // bytes above the highest byte in which the finite keys differ are
+      // the same in all of them, the k-th largest included: take them as
+      // they are, and radix-select the rest a byte at a time
+      int d = (31 - __builtin_clz(diff)) >> 3;
+      uint32_t mask = d == 3 ? 0u : 0xFFFFFFFFu << (8 * (d + 1));
+      uint32_t prefix = khi & mask;
+      int rem = k, buf = 0;
+      for (; d >= 0; --d, buf ^= 1) {
+        const int sh = 8 * d;
+        for_keys(0, staged, [&](int, uint32_t key) {
+          add_to_bin(hist[buf], key != 0u && (key & mask) == prefix, (key >> sh) & 255u);
+        });
+        // the other buffer serves the next digit; its last reader (wave 0's
+        // search of the previous digit) finished before the last barrier
+        hist[buf ^ 1][t] = 0;
+        __syncthreads();
+        if (wave == 0) {
+          // lane l holds digits 255-4l down to 252-4l; the digit D with
+          // count(digit > D) < rem <= count(digit >= D) is unique
+          const int4 c = *reinterpret_cast<const int4*>(&hist[buf][4 * (kWave - 1 - lane)]);
+          const int own = c.x + c.y + c.z + c.w;
+          int acc = wave_inclusive_scan(own) - own;
+          const int cnt[4] = {c.w, c.z, c.y, c.x};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (acc < rem && rem <= acc + cnt[j]) {
+              sm_sel[0] = uint32_t(255 - 4 * lane - j);
+              sm_sel[1] = uint32_t(rem - acc);
+              sm_sel[2] = uint32_t(cnt[j]);
+            }
+            acc += cnt[j];
+          }
+        }
+        __syncthreads();
+        prefix |= sm_sel[0] << sh;
+        mask |= 255u << sh;
+        rem = int(sm_sel[1]);
+        const int few = int(sm_sel[2]);
+        if (d > 0 && few <= kWave) {
+          // at most 64 keys still share the prefix: gather them and let
+          // wave 0 rank them (keys above each, keys equal to it) instead
+          // of resolving the remaining bytes
+          for_keys(0, staged, [&](int, uint32_t key) {
+            if (key != 0u && (key & mask) == prefix) {
+              const int slot = atomicAdd(&sm_ncand, 1);
+              if (slot < kWave) sm_cand[slot] = key;
+            }
+          });
+          __syncthreads();
+          if (wave == 0) {
+            const int m = min(sm_ncand, kWave);
+            const uint32_t c = lane < m ? sm_cand[lane] : 0u;
+            int above = 0, same = 0;
+            for (int j = 0; j < m; ++j) {
+              const uint32_t cj = uint32_t(__builtin_amdgcn_readlane(int(c), j));
+              above += cj > c;
+              same += cj == c;
+            }
+            const bool hit = lane < m && above < rem && rem <= above + same;
+            const uint64_t hm = __builtin_amdgcn_ballot_w64(hit);
+            if (hm != 0 && lane == __builtin_ctzll(hm)) {
+              sm_sel[0] = c;
+              sm_sel[1] = uint32_t(rem - above);
+            }
+          }
+          __syncthreads();
+          prefix = sm_sel[0];
+          rem = int(sm_sel[1]);
+          break;
         }
       }
-      __syncthreads();
-      prefix |= sm_sel[0] << sh;
-      mask |= 255u << sh;
-      rem = int(sm_sel[1]);
-      __syncthreads();
+      thr = prefix;
+      need_eq = rem;
     }
-    thr = prefix;  // the k-th largest key; rem of the keys equal to it are taken
-    need_eq = rem;
   }
 
-  // pass 1: counts; pass 2: write the chosen pages in ascending order
+  // each thread's contiguous slice of the row: counts, one block scan of
+  // (keys above thr, keys at thr), then the chosen pages
+  // in ascending order; ties at thr go to the lowest pages, so the ties
+  // taken before a slice number min(need_eq, ties before it)
+  const int chunk = (n + kTopkThreads - 1) / kTopkThreads;
+  const int c0 = min(n, t * chunk), c1 = min(n, c0 + chunk);
   int gt = 0, eq = 0;
   for (int i = c0; i < c1; ++i) {
     const uint32_t key = key_at(i);
-    if (total_fin > k) {
+    if (select) {
       gt += key > thr;
       eq += key == thr;
     } else {
       gt += key != 0u;
     }
   }
-  int dummy;
-  const int eq_before = block_exclusive_scan(eq, &dummy, sm_wave);
-  const int take_eq = total_fin > k ? min(max(need_eq - eq_before, 0), eq) : 0;
-  int total_sel;
-  int pos = block_exclusive_scan(gt + take_eq, &total_sel, sm_wave);
-  int eq_left = take_eq;
+  const int gt_inc = wave_inclusive_scan(gt), eq_inc = wave_inclusive_scan(eq);
+  if (lane == kWave - 1) {
+    sm_scan[0][wave] = gt_inc;
+    sm_scan[1][wave] = eq_inc;
+  }
+  __syncthreads();
+  int gt_before = gt_inc - gt, eq_before = eq_inc - eq, gt_tot = 0, eq_tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / kWave; ++w) {
+    const int g = sm_scan[0][w], e = sm_scan[1][w];
+    if (w < wave) {
+      gt_before += g;
+      eq_before += e;
+    }
+    gt_tot += g;
+    eq_tot += e;
+  }
+  int pos = gt_before + min(need_eq, eq_before);
+  const int total_sel = gt_tot + min(need_eq, eq_tot);
+  int eq_left = min(max(need_eq - eq_before, 0), eq);
   for (int i = c0; i < c1; ++i) {
     const uint32_t key = key_at(i);
     bool pick;
-    if (total_fin > k) {
-      pick = key > thr || (key == thr && eq_left > 0);
-      if (key == thr && eq_left > 0) --eq_left;
+    if (select) {
+      const bool tie = key == thr && eq_left > 0;
+      pick = key > thr || tie;
+      eq_left -= tie;
     } else {
       pick = key != 0u;
     }

@@ -142,6 +142,7 @@ class Layers:
     prefetch_depth = 0
     workgroup_waves = 0
     merge_mode = 0
+    partition_mode = 0
 
     def step(self, l, ev=None, ev_index=None):
         pa.kv_quant_write(self.step_k, self.step_v, self.step_slots[l], self.kc, self.vc,
@@ -160,6 +161,7 @@ class Layers:
                         max_q_len=self.max_q_len if self.cu is not None else 0,
                         force_parts=self.force_parts, prefetch_depth=self.prefetch_depth,
                         workgroup_waves=self.workgroup_waves, merge_mode=self.merge_mode,
+                        partition_mode=self.partition_mode,
                         main_begin_event=None if ev is None else ev[0],
                         main_end_event=None if ev is None else ev[1])
 
@@ -388,6 +390,8 @@ def main():
     ap.add_argument("--workgroup-waves", type=int, default=0, help="4 or 8 waves per workgroup (0: the plan's)")
     ap.add_argument("--merge-mode", type=int, default=0,
                     help="split-K merge: 0 the plan's, 1 separate kernel, 2 in the main kernel")
+    ap.add_argument("--partition-mode", type=int, default=0,
+                    help="split-K partitions: 0 the plan's, 1 fixed, 2 length-balanced")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -418,11 +422,13 @@ def main():
                          topk=index_topk or (0 if w.sparse is None else w.sparse.shape[1]),
                          ragged=w.cu is not None, max_q_len=int(w.q_lens.max()) if w.cu is not None else 0,
                          scale_mode=w.mode, force_parts=args.force_parts,
-                         kv_dtype=3 if w.kv_dtype == "bf16" else 1, merge_mode=args.merge_mode)
+                         kv_dtype=3 if w.kv_dtype == "bf16" else 1, merge_mode=args.merge_mode,
+                         partition_mode=args.partition_mode)
     layers.force_parts = args.force_parts
     layers.prefetch_depth = args.prefetch_depth
     layers.workgroup_waves = args.workgroup_waves
     layers.merge_mode = args.merge_mode
+    layers.partition_mode = args.partition_mode
     plan = pa.pa_plan_describe(cfg)
     pa.pa_reserve(cfg, stream)
 
@@ -528,7 +534,7 @@ def main():
             "kv_bytes_per_step": int(kv_bytes),
             "plan": {k: int(v) for k, v in plan.items() if k in ("parts", "pages_per_part", "grid_x",
                                                                   "rows_per_group", "merge",
-                                                                  "merge_in_kernel")},
+                                                                  "merge_in_kernel", "balanced")},
         },
         "attended_tokens_per_s": round(tokens_per_s, 1),
         "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),

@@ -10,8 +10,8 @@ stream.
 import ctypes
 
 from ._lib import (  # noqa: F401
-    EXPORTS, MERGE_IN_KERNEL, MERGE_PLAN, MERGE_SEPARATE, PaConfig, PaDecodeOpts, PaError, PaPlanInfo,
-    PaTensor, SCALE_NONE,
+    EXPORTS, MERGE_IN_KERNEL, MERGE_PLAN, MERGE_SEPARATE, PARTITION_BALANCED, PARTITION_FIXED,
+    PARTITION_PLAN, PaConfig, PaDecodeOpts, PaError, PaPlanInfo, PaTensor, SCALE_NONE,
     SCALE_PER_TOKEN, SCALE_SCALAR, STATUS, check, desc, load, ref, stream_handle,
 )
 
@@ -35,7 +35,7 @@ def pa_decode(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
 def pa_decode_ex(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
                  cu_seqlens_q, sparse_page_idx, scale_mode, out, sm_scale=0.0, max_q_len=0,
                  force_parts=0, main_begin_event=None, main_end_event=None, prefetch_depth=0,
-                 workgroup_waves=0, merge_mode=0, stream=None):
+                 workgroup_waves=0, merge_mode=0, partition_mode=0, stream=None):
     """``pa_decode`` with options; events are torch.cuda.Event objects that
     have been recorded once (so they exist)."""
     lib = load()
@@ -46,6 +46,7 @@ def pa_decode_ex(q, k_cache, v_cache, k_scale, v_scale, block_table, context_len
     opts.prefetch_depth = int(prefetch_depth)
     opts.workgroup_waves = int(workgroup_waves)
     opts.merge_mode = int(merge_mode)
+    opts.partition_mode = int(partition_mode)
     opts.main_begin_event = main_begin_event.cuda_event if main_begin_event is not None else None
     opts.main_end_event = main_end_event.cuda_event if main_end_event is not None else None
     d = [desc(t) for t in (q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
@@ -77,13 +78,14 @@ def pa_index_topk(q_idx, index_cache, block_table, context_lens, cu_seqlens_q, s
 
 def make_config(num_kv_heads, rows, batch, max_pages, topk=0, ragged=False, max_q_len=0,
                 scale_mode=SCALE_PER_TOKEN, kv_dtype=1, force_parts=0, group_size=GROUP_SIZE,
-                head_dim=HEAD_DIM, page_size=PAGE_SIZE, merge_mode=0):
+                head_dim=HEAD_DIM, page_size=PAGE_SIZE, merge_mode=0, partition_mode=0):
     c = PaConfig()
     c.num_kv_heads, c.group_size, c.head_dim, c.page_size = num_kv_heads, group_size, head_dim, page_size
     c.kv_dtype, c.scale_mode = kv_dtype, scale_mode
     c.rows, c.batch, c.max_pages, c.topk = rows, batch, max_pages, topk
     c.ragged, c.max_q_len, c.force_parts = int(bool(ragged)), max_q_len, force_parts
     c.merge_mode = merge_mode
+    c.partition_mode = partition_mode
     return c
 
 

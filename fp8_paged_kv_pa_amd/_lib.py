@@ -18,6 +18,7 @@ MAX_DIMS = 6
 DTYPE_U8, DTYPE_F8E4M3, DTYPE_BF16, DTYPE_F32, DTYPE_I32, DTYPE_I64 = 1, 2, 3, 4, 5, 6
 SCALE_NONE, SCALE_SCALAR, SCALE_PER_TOKEN = 0, 1, 2
 MERGE_PLAN, MERGE_SEPARATE, MERGE_IN_KERNEL = 0, 1, 2
+PARTITION_PLAN, PARTITION_FIXED, PARTITION_BALANCED = 0, 1, 2
 
 STATUS = {
     0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_DTYPE", -3: "PA_ERR_SHAPE",
@@ -55,6 +56,7 @@ class PaDecodeOpts(ctypes.Structure):
         ("prefetch_depth", ctypes.c_int32),
         ("workgroup_waves", ctypes.c_int32),
         ("merge_mode", ctypes.c_int32),
+        ("partition_mode", ctypes.c_int32),
     ]
 
 
@@ -74,6 +76,7 @@ class PaConfig(ctypes.Structure):
         ("max_q_len", ctypes.c_int32),
         ("force_parts", ctypes.c_int32),
         ("merge_mode", ctypes.c_int32),
+        ("partition_mode", ctypes.c_int32),
     ]
 
 
@@ -91,6 +94,7 @@ class PaPlanInfo(ctypes.Structure):
         ("scratch_bytes", ctypes.c_int64),
         ("merge", ctypes.c_int32),
         ("merge_in_kernel", ctypes.c_int32),
+        ("balanced", ctypes.c_int32),
     ]
 
 

@@ -236,6 +236,7 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   cfg.max_q_len = opts ? opts->max_q_len : 0;
   cfg.force_parts = opts ? opts->force_parts : 0;
   cfg.merge_mode = opts ? opts->merge_mode : 0;
+  cfg.partition_mode = opts ? opts->partition_mode : 0;
   if (opts && (opts->prefetch_depth < 0 || opts->prefetch_depth > 4))
     return fail(PA_ERR_INVALID_ARG, "prefetch_depth must be in [0, 4]");
   if (opts && opts->workgroup_waves != 0 && opts->workgroup_waves != 4 && opts->workgroup_waves != 8)
@@ -270,7 +271,8 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   a.out_row_stride = out->stride[0];
   a.out_head_stride = out->stride[1];
   if (plan.merge) {
-    const int64_t pairs = int64_t(plan.parts_launched) * rows * Hq;
+    const int64_t pairs = plan.balanced ? int64_t(plan.nslot) * plan.lrows * Hq
+                                        : int64_t(plan.parts_launched) * rows * Hq;
     a.part_ml = static_cast<float*>(scratch);
     a.part_acc = static_cast<float*>(scratch) + 2 * pairs;
     a.unit_count = plan.fused_merge ? counters : nullptr;
@@ -290,6 +292,9 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   a.kv_bf16 = bf16kv ? 1 : 0;
   a.xcd_grouped = plan.xcd_grouped ? 1 : 0;
   a.nq = int32_t(plan.nq);
+  a.balanced = plan.balanced ? 1 : 0;
+  a.nslot = plan.nslot;
+  a.lrows = plan.lrows;
   float sm = (opts && opts->sm_scale != 0.0f) ? opts->sm_scale : 1.0f / std::sqrt(float(kDim));
   a.sm_log2 = sm * 1.4426950408889634f;
 

@@ -78,6 +78,40 @@ __device__ __forceinline__ float wave_reduce(float v) {
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce<true>(v); }
 __device__ __forceinline__ float wave_sum(float v) { return wave_reduce<false>(v); }
 
+// Unsigned add / max / min over a wave without LDS: DPP within rows of 16
+// lanes (swap neighbours, swap pairs, rotate by 4, rotate by 8), then the
+// four rows through readlane.  Every lane gets the result.
+enum class UOp { ADD, MAX, MIN };
+template <UOp OP>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+  auto op = [](uint32_t x, uint32_t y) { return OP == UOp::ADD ? x + y : (OP == UOp::MAX ? max(x, y) : min(x, y)); };
+  int b = int(v);
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
+  b = int(v);
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(b, b, 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
+  b = int(v);
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(b, b, 0x124, 0xF, 0xF, false)));  // row_ror 4
+  b = int(v);
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(b, b, 0x128, 0xF, 0xF, false)));  // row_ror 8
+  b = int(v);
+  return op(op(uint32_t(__builtin_amdgcn_readlane(b, 0)), uint32_t(__builtin_amdgcn_readlane(b, 16))),
+            op(uint32_t(__builtin_amdgcn_readlane(b, 32)), uint32_t(__builtin_amdgcn_readlane(b, 48))));
+}
+
+// Inclusive prefix sum over a wave by DPP: within rows of 16 lanes (add
+// the lane 1, 2, 4, 8 below; lanes with no such lane in the row add 0),
+// then across rows (lane 15 of rows 0 and 2 into rows 1 and 3, then lane
+// 31 into rows 2 and 3).
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr 1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr 2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr 4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr 8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast 15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast 31
+  return x;
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }

@@ -28,8 +28,8 @@ struct DecodeArgs {
   uint16_t* out;              // bf16 [rows, Hq, 128]
   int64_t out_row_stride;
   int64_t out_head_stride;
-  float* part_ml;             // scratch: (m, l) float2 [parts][rows][Hq]
-  float* part_acc;            // scratch: float [parts][rows][Hq][128]
+  float* part_ml;             // scratch: (m, l) float2 [parts][rows][Hq]; balanced: [nslot][lrows][Hq]
+  float* part_acc;            // scratch: float [parts][rows][Hq][128]; balanced: [nslot][lrows][Hq][128]
   uint32_t* unit_count;       // scratch: per-unit arrival counters (in-kernel merge), or null
   int64_t num_blocks;
   int32_t hkv;
@@ -45,7 +45,11 @@ struct DecodeArgs {
   int32_t scale_mode;
   int32_t kv_bf16;            // 1: unquantized bf16 cache (no scales)
   int32_t xcd_grouped;        // 1: dense grid with a (request, head, partition)'s row groups on one XCD
-  int32_t nq;                 // (request, KV head, partition) triples when xcd_grouped
+  int32_t nq;                 // xcd_grouped: (request, KV head, partition) triples, or
+                              // (slot, KV head) pairs when balanced
+  int32_t balanced;           // 1: length-balanced partitions (slots shared by the requests)
+  int32_t nslot;              // balanced: partition slots per (KV head, row group)
+  int32_t lrows;              // balanced: rows per request held by a slot's partials
   float sm_log2;              // sm_scale * log2(e)
 };
 

@@ -79,6 +79,47 @@ __device__ __forceinline__ void request_rows(const DecodeArgs& a, int b, int* st
   *L = e - s;
 }
 
+// Length-balanced partitions (dense calls of at most 64 requests; lane j
+// stands for request j).  Every partition of the call holds ppp pages:
+// the smallest ppp for which the requests' partitions, max(1, ceil(pages_j
+// / ppp)) each, fit the nslot launched slots.  ppp is found by bisection
+// between ceil(total / nslot) and ceil(total / (nslot - batch)); the upper
+// end always fits, since the partitions then number at most total / ppp +
+// batch.  Slots go to the requests in order.  The main and the merge kernel
+// both derive this from the context lengths, so they agree without a pass
+// of their own.
+struct Balanced {
+  int ppp;    // pages per partition
+  int first;  // lane j: first slot of request j
+  int parts;  // lane j: partitions of request j (0 past the batch)
+  int ctx;    // lane j: context length of request j
+};
+
+__device__ __forceinline__ Balanced balanced_layout(const DecodeArgs& a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool live = lane < a.batch;
+  Balanced r;
+  r.ctx = live ? a.context_lens[lane] : 0;
+  const int np = (max(0, min(r.ctx, a.width * 128)) + 127) >> 7;  // pages the request's last row sees
+  const int total = int(wave_reduce_u32<UOp::ADD>(uint32_t(np)));
+  auto parts_at = [&](int ppp) { return live ? max(1, (np + ppp - 1) / ppp) : 0; };
+  int lo = max(1, (total + a.nslot - 1) / a.nslot);
+  int hi = max(lo, (total + a.nslot - a.batch - 1) / (a.nslot - a.batch));
+  // equal lengths that divide evenly fit at the lower end: one count, no search
+  if (hi > lo && int(wave_reduce_u32<UOp::ADD>(uint32_t(parts_at(lo)))) <= a.nslot) hi = lo;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (int(wave_reduce_u32<UOp::ADD>(uint32_t(parts_at(mid)))) <= a.nslot) hi = mid;
+    else lo = mid + 1;
+  }
+  r.ppp = lo;
+  r.parts = parts_at(lo);
+  r.first = wave_inclusive_scan(r.parts) - r.parts;
+  return r;
+}
+
+__device__ __forceinline__ int lane_int(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
 // An empty asm that reads every register of a chunk: forces the compiler to
 // complete the chunk's loads here (used on paths that skip the chunk).
 template <bool PER_TOKEN, bool BF>
@@ -262,8 +303,35 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   const int Hq = 16 * a.hkv;
 
   int part;
-  int64_t unit;
-  if (!SPARSE && a.xcd_grouped) {
+  int64_t unit = 0;
+  int ppp = a.ppp;
+  int bal_slot = 0, bal_b = 0, bal_h = 0, bal_gi = 0, bal_ctx = 0;
+  if (!SPARSE && a.balanced) {
+    // slot (a partition position shared by the requests), KV head, row group
+    uint32_t slot;
+    if (a.xcd_grouped) {
+      // as below: the row groups of one (slot, KV head) on one XCD
+      const uint32_t x = blockIdx.x & 7u, s = blockIdx.x >> 3;
+      bal_gi = int(s % uint32_t(a.groups));
+      const uint32_t q = (s / uint32_t(a.groups)) * 8u + x;
+      if (q >= uint32_t(a.nq)) return;
+      slot = q / uint32_t(a.hkv);
+      bal_h = int(q % uint32_t(a.hkv));
+    } else {
+      slot = blockIdx.x / uint32_t(a.hkv);
+      bal_h = int(blockIdx.x % uint32_t(a.hkv));
+    }
+    const Balanced bl = balanced_layout(a);
+    // the request whose slots hold this one: the requests before it are
+    // those whose slots end at or before it
+    bal_b = __builtin_popcountll(
+        __builtin_amdgcn_ballot_w64(lane < a.batch && bl.first + bl.parts <= int(slot)));
+    if (bal_b >= a.batch) return;  // past the last request's partitions
+    bal_slot = int(slot);
+    part = int(slot) - lane_int(bl.first, bal_b);
+    bal_ctx = lane_int(bl.ctx, bal_b);
+    ppp = bl.ppp;
+  } else if (!SPARSE && a.xcd_grouped) {
     // Row groups of one (request, KV head, partition) read the same pages:
     // give them workgroup ids x + 8s, x + 8(s+1), ... -- consecutive
     // dispatches on the same XCD (ids go round-robin over the 8 XCDs), so
@@ -289,7 +357,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   // The loads that decide the partition's work (context length, row range,
   // the partition's first block-table entry) are issued together, before
   // any branch, so they cost one memory round trip.
-  const int n0 = part * a.ppp;  // < width (dense) or < topk (sparse) by construction of the grid
+  const int n0 = part * ppp;  // < width (dense) or < topk (sparse) by construction of the grid
   const int s0 = n0 + ps;       // this wave's first list position
   int h, b, row0, nrows, lim0;  // row row0+i sees tokens t < lim0 + i
   int first_entry;              // dense: block_table[b][s0]; sparse: sparse_idx[row0][s0] (-1 past the end)
@@ -310,15 +378,22 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     nrows = 1;
     lim0 = a.context_lens[b] - L + (row0 - start) + 1;
   } else {
-    const int gi = int(unit % a.groups);
-    const int64_t bh = unit / a.groups;
-    h = int(bh % a.hkv);
-    b = int(bh / a.hkv);
+    int gi;
+    if (a.balanced) {
+      gi = bal_gi;
+      h = bal_h;
+      b = bal_b;
+    } else {
+      gi = int(unit % a.groups);
+      const int64_t bh = unit / a.groups;
+      h = int(bh % a.hkv);
+      b = int(bh / a.hkv);
+    }
     first_entry = s0 < a.width ? as_const(a.block_table + int64_t(b) * a.bt_stride)[s0] : -1;
     // the next position's entry travels with the first: its page's loads
     // need not wait for a second table round trip after the context length
     second_entry = s0 + S < a.width ? as_const(a.block_table + int64_t(b) * a.bt_stride)[s0 + S] : -1;
-    const int ctx = a.context_lens[b];
+    const int ctx = a.balanced ? bal_ctx : a.context_lens[b];
     int start, L;
     if (a.cu_seqlens_q) {
       request_rows(a, b, &start, &L);
@@ -371,17 +446,21 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
 
   int n1;
   if constexpr (SPARSE) {
-    n1 = min(n0 + a.ppp, a.topk);
+    n1 = min(n0 + ppp, a.topk);
   } else {
     const int npages = (lim_max + 127) >> 7;
-    n1 = min(n0 + a.ppp, npages);
+    n1 = min(n0 + ppp, npages);
   }
-  if (n0 >= n1 && a.parts > 1) {
+  // where this workgroup's rows leave their partials: partition-major over
+  // all rows, or (balanced) slot-major over the rows of one request
+  const bool to_partial = a.balanced || a.parts > 1;
+  const int64_t prow0 = a.balanced ? int64_t(bal_slot) * a.lrows + bal_gi * RT : int64_t(part) * a.rows + row0;
+  if (n0 >= n1 && to_partial) {
     // nothing to attend in this partition: leave an empty partial (weight 0)
     // so the merge can read every partition without knowing the context
     if (threadIdx.x < 16 * nrows) {
       const int r = threadIdx.x >> 4;
-      const int64_t pi = (int64_t(part) * a.rows + row0 + r) * Hq + 16 * h + (threadIdx.x & 15);
+      const int64_t pi = (prow0 + r) * Hq + 16 * h + (threadIdx.x & 15);
       if (a.unit_count) store_coherent(a.part_ml + 2 * pi, -INFINITY, 0.0f);
       else *reinterpret_cast<float2*>(a.part_ml + 2 * pi) = float2{-INFINITY, 0.0f};
     }
@@ -674,7 +753,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       }
       const int row = row0 + r;
       const int qh = 16 * h + oh;
-      if (a.parts == 1) {
+      if (!to_partial) {
         const float inv = Ls > 0.0f ? v_fold / Ls : 0.0f;
         uint32_t packed[4];
 #pragma unroll
@@ -687,7 +766,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
         uint16_t* op = a.out + int64_t(row) * a.out_row_stride + int64_t(qh) * a.out_head_stride + od;
         *reinterpret_cast<u32x4*>(op) = u32x4{packed[0], packed[1], packed[2], packed[3]};
       } else {
-        const int64_t pi = (int64_t(part) * a.rows + row) * Hq + qh;
+        const int64_t pi = (prow0 + r) * Hq + qh;
         if (a.unit_count) {
           float* ap = a.part_acc + pi * 128 + od;
           store_coherent(ap, s0v[0], s0v[1]);
@@ -724,12 +803,12 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
 }
 
 // One wave's share of a (row, query head): partitions [q0, q1), merged into
-// (M, L, ox, oy) relative to its own running maximum M.
+// (M, L, ox, oy) relative to its own running maximum M.  Partition p's
+// partial is entry p * stride_p + base of the (m, l) and accumulator arrays.
 template <int N>
-__device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t base, int q0, int q1, float& M,
-                                            float& L, float& ox, float& oy) {
+__device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t base, int64_t stride_p, int q0, int q1,
+                                            float& M, float& L, float& ox, float& oy) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t stride_p = int64_t(a.rows) * (16 * a.hkv);  // between partitions
   for (int p0 = q0; p0 < q1; p0 += N) {
     const int cnt = min(N, q1 - p0);
     float2 v[N];
@@ -771,17 +850,43 @@ __global__ __launch_bounds__(4 * kWave) void pa_merge(DecodeArgs a) {
   const int64_t pair = blockIdx.x;
   const int row = int(pair / Hq);
   const int qh = int(pair - int64_t(row) * Hq);
-  const int64_t base = int64_t(row) * Hq + qh;
-  const int P = a.parts;
+  uint16_t* op = a.out + int64_t(row) * a.out_row_stride + int64_t(qh) * a.out_head_stride + 2 * lane;
+  int64_t base = int64_t(row) * Hq + qh;
+  int64_t stride_p = int64_t(a.rows) * Hq;  // between partitions
+  int P = a.parts;
+  if (a.balanced) {
+    // the row's request and its place in it (with nondecreasing
+    // cu_seqlens_q: the request starts after the first at or before the
+    // row), then that request's slots
+    const Balanced bl = balanced_layout(a);
+    int b, i;
+    if (a.cu_seqlens_q) {
+      const int cu = lane < a.batch ? a.cu_seqlens_q[lane] : 0;
+      b = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane >= 1 && lane < a.batch && cu <= row));
+      i = row - min(max(lane_int(cu, b), 0), a.rows);
+    } else {
+      b = row / a.uniform_q_len;
+      i = row - b * a.uniform_q_len;
+    }
+    if (i < 0 || i >= a.lrows) {
+      // a row the main kernel has no partial for (more rows in its request
+      // than max_q_len, or a malformed cu_seqlens_q): zeros
+      if (wave == 0) *reinterpret_cast<uint32_t*>(op) = 0u;
+      return;
+    }
+    P = lane_int(bl.parts, b);
+    stride_p = int64_t(a.lrows) * Hq;
+    base = (int64_t(lane_int(bl.first, b)) * a.lrows + i) * Hq + qh;
+  }
   const int share = (P + nw - 1) / nw;
   const int q0 = min(P, wave * share), q1 = min(P, q0 + share);
 
   // Every launched partition left a partial; empty ones have m = -inf and
   // weight 0 (their accumulators are never read into the sum).
   float M = -INFINITY, L = 0.0f, ox = 0.0f, oy = 0.0f;
-  if (share <= 8) merge_range<8>(a, base, q0, q1, M, L, ox, oy);
-  else if (share <= 16) merge_range<16>(a, base, q0, q1, M, L, ox, oy);
-  else merge_range<32>(a, base, q0, q1, M, L, ox, oy);
+  if (share <= 8) merge_range<8>(a, base, stride_p, q0, q1, M, L, ox, oy);
+  else if (share <= 16) merge_range<16>(a, base, stride_p, q0, q1, M, L, ox, oy);
+  else merge_range<32>(a, base, stride_p, q0, q1, M, L, ox, oy);
   if (nw > 1) {
     if (lane == 0) {
       sm_ml[wave][0] = M;
@@ -807,8 +912,7 @@ __global__ __launch_bounds__(4 * kWave) void pa_merge(DecodeArgs a) {
   if (a.scale_mode != PA_SCALE_PER_TOKEN && a.v_scale) v_fold = *a.v_scale;
   const float inv = L > 0.0f ? v_fold / L : 0.0f;
   const uint32_t packed = uint32_t(f32_to_bf16_rne(ox * inv)) | (uint32_t(f32_to_bf16_rne(oy * inv)) << 16);
-  *reinterpret_cast<uint32_t*>(a.out + int64_t(row) * a.out_row_stride + int64_t(qh) * a.out_head_stride +
-                               2 * lane) = packed;
+  *reinterpret_cast<uint32_t*>(op) = packed;
 }
 
 // With events, the dispatch itself records them (start and end of this
@@ -871,8 +975,11 @@ hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool spa
   if (e != hipSuccess) return e;
   if (merge && !a.unit_count) {
     const int64_t pairs = int64_t(a.rows) * 16 * a.hkv;
-    // one wave per 16 partitions, at most four
-    const int waves = a.parts <= 16 ? 1 : (a.parts <= 32 ? 2 : 4);
+    // one wave per 16 partitions, at most four.  Balanced: a request's
+    // partition count is known only on the device and is usually a few, so
+    // one wave, which takes any count in batches of up to 32 (measured at
+    // q_len 4: four waves that each derive the split cost 12 us, one 4.6)
+    const int waves = a.balanced ? 1 : (a.parts <= 16 ? 1 : (a.parts <= 32 ? 2 : 4));
     hipLaunchKernelGGL(pa_merge, dim3(uint32_t(pairs)), dim3(kWave * waves), 0, stream, a);
     e = hipGetLastError();
   }

@@ -50,6 +50,8 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
   if (c.max_q_len < 0) return fail(err, PA_ERR_INVALID_ARG, "max_q_len must be >= 0");
   if (c.merge_mode < PA_MERGE_PLAN || c.merge_mode > PA_MERGE_IN_KERNEL)
     return fail(err, PA_ERR_INVALID_ARG, "unknown merge_mode " + std::to_string(c.merge_mode));
+  if (c.partition_mode < PA_PARTITION_PLAN || c.partition_mode > PA_PARTITION_BALANCED)
+    return fail(err, PA_ERR_INVALID_ARG, "unknown partition_mode " + std::to_string(c.partition_mode));
   // Uniformity is never inferred from divisibility: without cu_seqlens_q the
   // call *declares* every request has rows/batch rows, so rows must divide.
   if (!c.ragged && c.rows % c.batch != 0)
@@ -128,6 +130,40 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
     p.scratch_bytes = p.counter_bytes +
                       int64_t(p.parts) * p.rows_bucket * hkv * kGroup * per * int64_t(sizeof(float));
   }
+
+  // Length-balanced partitions (see pa_partition_mode): nslot slots per (KV
+  // head, row group), handed out request by request on the device, each
+  // request's partials at (slot, row within the request).  At most
+  // nslot - batch slots' worth of pages is spread evenly, so the split
+  // always fits.
+  const bool can_balance = !p.sparse && c.batch <= kMaxBalancedBatch && c.force_parts == 0 &&
+                           c.merge_mode != PA_MERGE_IN_KERNEL && (!c.ragged || c.max_q_len > 0);
+  if (c.partition_mode == PA_PARTITION_BALANCED && !can_balance)
+    return fail(err, PA_ERR_UNSUPPORTED,
+                "balanced partitions serve dense calls of at most 64 requests (ragged ones with max_q_len), "
+                "without force_parts or the in-kernel merge");
+  const bool balanced = can_balance && (c.partition_mode == PA_PARTITION_BALANCED ||
+                                        (c.partition_mode == PA_PARTITION_PLAN && p.ppp >= kBalanceMinPages));
+  if (balanced) {
+    const int64_t per_slot = hkv * p.groups;  // workgroups per slot
+    p.balanced = true;
+    p.nslot = int(std::max<int64_t>(kTargetWorkgroups / per_slot, c.batch + 1));
+    p.lrows = p.groups * p.rt;
+    p.parts = p.parts_launched = p.nslot;
+    p.ppp = 0;
+    p.merge = true;
+    p.fused_merge = false;
+    p.xcd_grouped = p.groups > 1;
+    if (p.xcd_grouped) {
+      p.nq = int64_t(p.nslot) * hkv;
+      p.grid = ceil_div(p.nq, 8) * 8 * p.groups;
+    } else {
+      p.nq = 0;
+      p.grid = int64_t(p.nslot) * hkv;
+    }
+    p.scratch_bytes = p.counter_bytes + next_pow2(p.nslot) * next_pow2(p.lrows) * hkv * kGroup *
+                                            int64_t(2 + kDim) * int64_t(sizeof(float));
+  }
   if (p.scratch_bytes > kMaxScratchBytes)
     return fail(err, PA_ERR_CAPACITY, "split-K scratch for this bucket exceeds 4 GiB");
   // one launch carries at most 2^31 - 1 workgroups; a ragged call whose
@@ -154,6 +190,7 @@ void describe(const Plan& p, pa_plan_info* info) {
   info->scratch_bytes = p.scratch_bytes;
   info->merge = p.merge ? 1 : 0;
   info->merge_in_kernel = (p.merge && p.fused_merge) ? 1 : 0;
+  info->balanced = p.balanced ? 1 : 0;
 }
 
 }  // namespace fp8pa

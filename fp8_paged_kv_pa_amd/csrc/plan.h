@@ -38,6 +38,12 @@ constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // workgroups in one launch
 // streams better than several short ones, and fewer partitions mean less
 // split-K scratch and a cheaper merge.
 constexpr int64_t kTargetWorkgroups = 256;
+// Length-balanced partitions: at most one request per lane of a wave, and
+// chosen by the plan only where the fixed split gives a workgroup at least
+// this many pages (below it the extra memory round trip of the device-side
+// split costs more than the balance gains).
+constexpr int64_t kMaxBalancedBatch = 64;
+constexpr int kBalanceMinPages = 8;
 
 struct Plan {
   int rt = 1;              // query rows per workgroup (1 or 2)
@@ -61,6 +67,9 @@ struct Plan {
   int64_t pages_bucket = 1;
   int64_t units_bucket = 1;
   int64_t scratch_bytes = 0;
+  bool balanced = false;   // length-balanced partitions (partition size chosen on the device)
+  int nslot = 0;           // balanced: partition slots the requests share
+  int lrows = 0;           // balanced: rows per request a slot's partials hold (groups * rt)
 };
 
 inline int64_t next_pow2(int64_t x) {

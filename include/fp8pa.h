@@ -109,6 +109,22 @@ typedef enum pa_merge_mode {
                            /* merges all of them inside the main kernel       */
 } pa_merge_mode;
 
+/* How a dense call's pages are cut into split-K partitions.  Fixed: every
+ * request gets the same partition count and size, set on the host from the
+ * block-table width.  Balanced: one partition size for the whole call,
+ * chosen on the device from the context lengths, and each request gets as
+ * many partitions as its pages need.  Workgroups then stream about the same
+ * number of pages whatever the mix of context lengths.  Balanced serves
+ * dense calls of at most 64 requests (uniform, or ragged with max_q_len)
+ * with the separate merge kernel and no force_parts. */
+typedef enum pa_partition_mode {
+  PA_PARTITION_PLAN = 0,     /* the library's choice: balanced where it is   */
+                             /* served and the fixed split would give a      */
+                             /* workgroup 8 or more pages; fixed otherwise   */
+  PA_PARTITION_FIXED = 1,
+  PA_PARTITION_BALANCED = 2  /* PA_ERR_UNSUPPORTED where it is not served    */
+} pa_partition_mode;
+
 /* Return codes.  Every host-checkable problem is reported before anything is
  * launched ([ATOM-2710] review "Should fix" 2; [ATOM-2614] "Change": decline
  * before the low-level launcher aborts).  pa_last_error() has the text. */
@@ -149,6 +165,7 @@ typedef struct pa_decode_opts {
                            /* page at a time) or 8 (two pages side by side;   */
                            /* two-row calls over a bf16 cache always use 4)   */
   int32_t merge_mode;      /* pa_merge_mode                                   */
+  int32_t partition_mode;  /* pa_partition_mode                               */
 } pa_decode_opts;
 
 /* Host-side description of a decode call, for capability queries, planning
@@ -169,6 +186,7 @@ typedef struct pa_config {
   int32_t max_q_len;       /* as pa_decode_opts.max_q_len                    */
   int32_t force_parts;     /* as pa_decode_opts.force_parts                  */
   int32_t merge_mode;      /* as pa_decode_opts.merge_mode                   */
+  int32_t partition_mode;  /* as pa_decode_opts.partition_mode               */
 } pa_config;
 
 /* The launch plan a config maps to (pa_plan_describe). */
@@ -185,6 +203,9 @@ typedef struct pa_plan_info {
   int32_t merge;           /* 1 if partials are merged (parts > 1)           */
   int32_t merge_in_kernel; /* 1: merged inside the main kernel; 0: by the    */
                            /* separate merge kernel (when merge is 1)        */
+  int32_t balanced;        /* 1: length-balanced partitions; then parts is   */
+                           /* the partition slots the requests share and     */
+                           /* pages_per_part is 0 (chosen on the device)     */
 } pa_plan_info;
 
 /*

@@ -43,8 +43,8 @@ static pa_config base() {
 // the C ABI's struct layouts (the Python binding mirrors them)
 static_assert(sizeof(pa_tensor) == 8 + 4 + 4 + 6 * 8 * 2, "pa_tensor");
 static_assert(sizeof(pa_decode_opts) == 48, "pa_decode_opts");
-static_assert(sizeof(pa_config) == 6 * 4 + 4 * 8 + 4 * 4, "pa_config");
-static_assert(sizeof(pa_plan_info) == 4 * 4 + 6 * 8 + 2 * 4, "pa_plan_info");
+static_assert(sizeof(pa_config) == 6 * 4 + 4 * 8 + 5 * 4 + 4, "pa_config");
+static_assert(sizeof(pa_plan_info) == 4 * 4 + 6 * 8 + 3 * 4 + 4, "pa_plan_info");
 
 int main() {
   std::string err;
@@ -178,10 +178,114 @@ int main() {
     }
     CHECK(sizes.size() == 1, "bucket (%lld, %lld] has %zu scratch sizes", lo, 2 * lo, sizes.size());
   }
+  // length-balanced partitions: when the plan chooses them, what it lays out
+  for (int hkv : {1, 2, 8}) {
+    for (long long batch : {1LL, 3LL, 31LL, 63LL, 64LL, 65LL}) {
+      for (int L : {1, 2, 4, 6}) {
+        for (long long W : {1LL, 5LL, 72LL, 256LL, 1024LL, 3000LL}) {
+          for (int mode : {PA_PARTITION_PLAN, PA_PARTITION_FIXED, PA_PARTITION_BALANCED}) {
+            pa_config c = base();
+            c.num_kv_heads = hkv;
+            c.batch = batch;
+            c.rows = batch * L;
+            c.max_pages = W;
+            c.partition_mode = mode;
+            Plan fixed;
+            pa_config cf = c;
+            cf.partition_mode = PA_PARTITION_FIXED;
+            CHECK(make_plan(cf, &fixed, &err) == PA_OK && !fixed.balanced, "fixed plan");
+            const int rc = make_plan(c, &p, &err);
+            if (mode == PA_PARTITION_BALANCED && batch > kMaxBalancedBatch) {
+              CHECK(rc == PA_ERR_UNSUPPORTED, "balanced beyond 64 requests refused");
+              continue;
+            }
+            CHECK(rc == PA_OK, "balanced plan rc %d (%s)", rc, err.c_str());
+            const bool want = batch <= kMaxBalancedBatch &&
+                              (mode == PA_PARTITION_BALANCED ||
+                               (mode == PA_PARTITION_PLAN && fixed.ppp >= kBalanceMinPages));
+            CHECK(p.balanced == want, "balanced choice batch=%lld W=%lld mode=%d", batch, W, mode);
+            if (!p.balanced) continue;
+            const long long per_slot = hkv * p.groups;
+            CHECK(p.nslot == std::max<long long>(kTargetWorkgroups / per_slot, batch + 1), "slots");
+            CHECK(p.nslot > batch, "more slots than requests");
+            CHECK(p.lrows == p.groups * p.rt && p.lrows >= L, "rows per slot");
+            CHECK(p.merge && !p.fused_merge, "balanced merges in the merge kernel");
+            const long long need = (long long)p.nslot * p.lrows * 16 * hkv * 130 * 4;
+            CHECK(p.scratch_bytes - p.counter_bytes >= need, "balanced scratch");
+            if (p.groups > 1) {
+              CHECK(p.xcd_grouped && p.nq == (long long)p.nslot * hkv, "balanced pairs");
+              CHECK(p.grid == (p.nq + 7) / 8 * 8 * p.groups, "balanced xcd grid");
+            } else {
+              CHECK(!p.xcd_grouped && p.grid == (long long)p.nslot * hkv, "balanced grid");
+            }
+          }
+        }
+      }
+    }
+  }
+  {
+    // refusals of a forced balanced split
+    pa_config c = base();
+    c.partition_mode = PA_PARTITION_BALANCED;
+    c.topk = 8;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_UNSUPPORTED, "balanced sparse");
+    c = base(); c.partition_mode = PA_PARTITION_BALANCED; c.force_parts = 4;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_UNSUPPORTED, "balanced with force_parts");
+    c = base(); c.partition_mode = PA_PARTITION_BALANCED; c.merge_mode = PA_MERGE_IN_KERNEL;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_UNSUPPORTED, "balanced with the in-kernel merge");
+    c = base(); c.partition_mode = PA_PARTITION_BALANCED; c.ragged = 1;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_UNSUPPORTED, "balanced ragged without max_q_len");
+    c.max_q_len = 1;
+    CHECK(make_plan(c, &p, &err) == PA_OK && p.balanced, "balanced ragged with max_q_len");
+    c = base(); c.partition_mode = 3;
+    CHECK(make_plan(c, &p, &err) == PA_ERR_INVALID_ARG, "unknown partition mode");
+  }
+  {
+    // A host model of the device-side split (the bisection for the common
+    // partition size): its upper end always fits, the result is the
+    // smallest size that fits, and every page lands in exactly one slot.
+    unsigned long long rng = 12345;
+    auto next = [&]() { rng = rng * 6364136223846793005ULL + 1442695040888963407ULL; return rng >> 33; };
+    for (int trial = 0; trial < 4000; ++trial) {
+      const int batch = 1 + int(next() % 64);
+      const int nslot = std::max(int(1 + next() % 256), batch + 1);
+      const int width = 1 + int(next() % 2048);
+      std::vector<int> np(batch);
+      long long total = 0;
+      for (int j = 0; j < batch; ++j) {
+        const int kind = int(next() % 4);
+        const long long ctx = kind == 0 ? 0 : (long long)(next() % (kind == 1 ? 300 : width * 128 + 500));
+        np[j] = int((std::max(0LL, std::min(ctx, (long long)width * 128)) + 127) / 128);
+        total += np[j];
+      }
+      auto count = [&](long long ppp) {
+        long long s = 0;
+        for (int v : np) s += std::max(1LL, (v + ppp - 1) / ppp);
+        return s;
+      };
+      long long lo = std::max(1LL, (total + nslot - 1) / nslot);
+      const long long hi0 = std::max(lo, (total + nslot - batch - 1) / (nslot - batch));
+      CHECK(count(hi0) <= nslot, "upper end fits (batch %d, slots %d)", batch, nslot);
+      long long hi = hi0;
+      while (lo < hi) {
+        const long long mid = (lo + hi) / 2;
+        if (count(mid) <= nslot) hi = mid; else lo = mid + 1;
+      }
+      CHECK(count(lo) <= nslot && (lo == 1 || count(lo - 1) > nslot), "smallest fitting size");
+      long long covered = 0, slots = 0;
+      for (int v : np) {
+        const long long parts = std::max(1LL, (v + lo - 1) / lo);
+        for (long long k = 0; k < parts; ++k) covered += std::max(0LL, std::min<long long>(lo, v - k * lo));
+        slots += parts;
+      }
+      CHECK(covered == total && slots <= nslot, "pages covered once");
+    }
+  }
   pa_plan_info info{};
   make_plan(base(), &p, &err);
   describe(p, &info);
-  CHECK(info.parts == p.parts_launched && info.grid_x == p.grid && info.merge == (p.merge ? 1 : 0), "describe");
+  CHECK(info.parts == p.parts_launched && info.grid_x == p.grid && info.merge == (p.merge ? 1 : 0) &&
+            info.balanced == (p.balanced ? 1 : 0), "describe");
   if (failures) {
     std::fprintf(stderr, "%d failures\n", failures);
     return 1;

@@ -37,9 +37,9 @@ def test_library_exports_every_declared_symbol():
 def test_struct_sizes_match_header_layout():
     # pa_tensor: ptr + 2 x int32 + 12 x int64
     assert ctypes.sizeof(_lib.PaTensor) == 8 + 8 + 6 * 8 * 2
-    assert ctypes.sizeof(_lib.PaConfig) == 6 * 4 + 4 * 8 + 4 * 4
+    assert ctypes.sizeof(_lib.PaConfig) == 6 * 4 + 4 * 8 + 5 * 4 + 4  # tail padded to 8
     assert ctypes.sizeof(_lib.PaDecodeOpts) == 4 + 4 + 4 + 4 + 8 + 8 + 4 + 4 + 4 + 4
-    assert ctypes.sizeof(_lib.PaPlanInfo) == 4 * 4 + 6 * 8 + 2 * 4
+    assert ctypes.sizeof(_lib.PaPlanInfo) == 4 * 4 + 6 * 8 + 3 * 4 + 4  # tail padded to 8
 
 
 def cfg(**kw):
@@ -122,8 +122,25 @@ def test_plans_and_scratch_depend_only_on_buckets():
 def test_plan_shapes_for_the_workloads():
     c2 = pa.pa_plan_describe(cfg(rows=4, batch=4, max_pages=72))
     assert c2["merge"] == 1 and c2["pages_per_part"] >= 1 and c2["units"] == 4
+    assert c2["balanced"] == 0  # two pages per partition: the fixed split
+    c3f = pa.pa_plan_describe(cfg(rows=32, batch=32, max_pages=1024, partition_mode=pa.PARTITION_FIXED))
+    assert c3f["parts"] * c3f["pages_per_part"] >= 1024 and c3f["grid_x"] == 32 * c3f["parts"]
+    assert c3f["balanced"] == 0
+    # length-balanced: 256 slots shared by the 32 requests, sizes chosen on the device
     c3 = pa.pa_plan_describe(cfg(rows=32, batch=32, max_pages=1024))
-    assert c3["parts"] * c3["pages_per_part"] >= 1024 and c3["grid_x"] == 32 * c3["parts"]
+    assert c3["balanced"] == 1 and c3["parts"] == 256 and c3["pages_per_part"] == 0
+    assert c3["grid_x"] == 256 and c3["merge"] == 1 and c3["merge_in_kernel"] == 0
+    c4 = pa.pa_plan_describe(cfg(rows=124, batch=31, max_pages=256))
+    assert c4["balanced"] == 1 and c4["groups"] == 2 and c4["parts"] == 128 and c4["grid_x"] == 256
+    c4r = pa.pa_plan_describe(cfg(rows=121, batch=31, max_pages=256, ragged=True))
+    assert c4r["balanced"] == 0  # ragged without max_q_len: fixed
+    c4m = pa.pa_plan_describe(cfg(rows=121, batch=31, max_pages=256, ragged=True, max_q_len=4))
+    assert c4m["balanced"] == 1
+    big = pa.pa_plan_describe(cfg(rows=65, batch=65, max_pages=1024))
+    assert big["balanced"] == 0  # more than 64 requests
+    assert pa.pa_query_support(cfg(rows=65, batch=65, max_pages=1024, partition_mode=pa.PARTITION_BALANCED)) == -5
+    assert pa.pa_query_support(cfg(topk=8, partition_mode=pa.PARTITION_BALANCED)) == -5
+    assert pa.pa_query_support(cfg(partition_mode=3)) == -1
     c5 = pa.pa_plan_describe(cfg(rows=16, batch=16, max_pages=1024, topk=32))
     assert c5["units"] == 16 and c5["parts"] * c5["pages_per_part"] >= 32
     one = pa.pa_plan_describe(cfg(rows=4, batch=4, max_pages=72, force_parts=1))

@@ -129,3 +129,17 @@ def test_balanced_graph_replays_match_eager():
         torch.cuda.synchronize()
         compare(other, oracle_out(w), what=f"eager between replays {rep}")
     compare(eager, oracle_out(w), what="eager")
+
+
+@pytest.mark.parametrize("depth", [3, 4])
+def test_balanced_with_deeper_prefetch_rings(depth):
+    """The single-row, four-wave variants with three- and four-page rings
+    under the balanced layout."""
+    for kw in (CASES[0], CASES[1], CASES[8]):
+        w = wl.small_case(**kw)
+        print("balanced depth", depth, w.name, flush=True)
+        case = GpuCase(w)
+        out = case.decode(out=torch.empty_like(case.out), partition_mode=BAL, prefetch_depth=depth,
+                          workgroup_waves=4)
+        torch.cuda.synchronize()
+        compare(out, oracle_out(w), what=f"{w.name} balanced depth={depth}")

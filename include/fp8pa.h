@@ -154,7 +154,10 @@ typedef struct pa_tensor {
 typedef struct pa_decode_opts {
   float sm_scale;          /* 0 => 1/sqrt(128)                                */
   int32_t max_q_len;       /* ragged only: caller-measured max rows per       */
-                           /* request (0 => unknown, bounded by rows)         */
+                           /* request (0 => unknown, bounded by rows).  Rows  */
+                           /* of a request past it are not computed: with    */
+                           /* balanced partitions they come out as zeros,    */
+                           /* with fixed ones they are left unspecified      */
   int32_t force_parts;     /* 0 => plan chooses; else split-K partitions      */
   void* main_begin_event;  /* hipEvent_t pair recorded by the main kernel's   */
   void* main_end_event;    /* dispatch (its start and end); may be NULL       */

@@ -134,7 +134,7 @@ __device__ __forceinline__ void consume_chunk(const Chunk<BF>& c) {
 // the same number of load instructions is issued on every path (so the
 // compiler's wait counts stay exact across the prefetch ring) at almost no
 // memory traffic.
-template <bool PER_TOKEN, bool BF>
+template <bool PER_TOKEN, bool BF, bool ONCE>
 __device__ __forceinline__ void load_chunk(Chunk<BF>& c, const DecodeArgs& a, int64_t blk, bool valid,
                                            int chunk, int lane) {
   constexpr int64_t kBlockBytes = BF ? 32768 : 16384;  // one (page, head) block
@@ -143,10 +143,22 @@ __device__ __forceinline__ void load_chunk(Chunk<BF>& c, const DecodeArgs& a, in
   const int istep = valid ? 64 : 0;
   const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + base);
   const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_cache + base);
+  // ONCE: these K and V bytes are read once per call (one-row workgroups),
+  // so non-temporal loads keep them from evicting what is reused (tables,
+  // the split-K partials the merge reads next, the pages the writer
+  // touches).  Two-row workgroups read each page once per row group, and
+  // the second group's read should hit the cache.
+  if constexpr (ONCE) {
 #pragma unroll
-  for (int i = 0; i < Chunk<BF>::kRows; ++i) c.k[i] = kp[istep * i];
+    for (int i = 0; i < Chunk<BF>::kRows; ++i) c.k[i] = __builtin_nontemporal_load(&kp[istep * i]);
 #pragma unroll
-  for (int i = 0; i < Chunk<BF>::kRows; ++i) c.v[i] = vp[istep * i];
+    for (int i = 0; i < Chunk<BF>::kRows; ++i) c.v[i] = __builtin_nontemporal_load(&vp[istep * i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < Chunk<BF>::kRows; ++i) c.k[i] = kp[istep * i];
+#pragma unroll
+    for (int i = 0; i < Chunk<BF>::kRows; ++i) c.v[i] = vp[istep * i];
+  }
   if constexpr (PER_TOKEN) {
     const int g = lane >> 4;
     const int64_t sbase = valid ? blk * 128 + chunk * 32 + 4 * g : 0;
@@ -420,7 +432,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     }
     const bool ok0 = P0 >= 0 && P0 < a.num_blocks;
     tb[0] = ok0 ? ln0 * 128 : kNoTokens;
-    load_chunk<PER_TOKEN, BF>(buf[0], a, int64_t(P0) * a.hkv + h, ok0, cw, lane);
+    load_chunk<PER_TOKEN, BF, RT == 1>(buf[0], a, int64_t(P0) * a.hkv + h, ok0, cw, lane);
   }
   // query operands: B of S^T = K Q^T, lane = (head hr, dims 8g..8g+7 of
   // each 32-dim k-step)
@@ -676,7 +688,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       const int P = raw_at(pos, ln);
       const bool ok = valid_page(P);
       tb[k] = ok ? ln * 128 : kNoTokens;
-      load_chunk<PER_TOKEN, BF>(buf[k], a, int64_t(P) * a.hkv + h, ok, cw, lane);
+      load_chunk<PER_TOKEN, BF, RT == 1>(buf[k], a, int64_t(P) * a.hkv + h, ok, cw, lane);
     }
     // raw entry of the next position to load (s0 + (NBUF-1)*S) and the
     // logical page of the one after it
@@ -696,7 +708,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
         const int nl = nn + (NBUF - 1) * S;
         const bool ok = valid_page(P_next);
         tb[ls] = ok ? ln_next * 128 : kNoTokens;
-        load_chunk<PER_TOKEN, BF>(buf[ls], a, int64_t(P_next) * a.hkv + h, ok, cw, lane);
+        load_chunk<PER_TOKEN, BF, RT == 1>(buf[ls], a, int64_t(P_next) * a.hkv + h, ok, cw, lane);
         // table reads for the following steps (checked one step later)
         ln_next = ln_after;
         P_next = raw_at(nl + S, ln_next);

@@ -188,15 +188,22 @@ __global__ __launch_bounds__(kTopkThreads) void index_topk_kernel(IndexArgs a) {
     first[j] = i < a.width ? srow[i] : -INFINITY;
   }
 
-  // the request of this row (with nondecreasing cu_seqlens_q: the number of
-  // request starts after the first at or before the row, counted by each
-  // wave with ballots) and its visible page count
+  // the request of this row (cu_seqlens_q nondecreasing: the last request
+  // starting at or before the row) and its visible page count.  Up to 64
+  // requests one load round trip: each wave counts the later starts at or
+  // before the row with a ballot; beyond that a binary search.
   int b, start, L;
   if (a.cu_seqlens_q) {
-    b = 0;
-    for (int base = 1; base < a.batch; base += kWave) {
-      const int j = base + lane;
-      b += __builtin_popcountll(__builtin_amdgcn_ballot_w64(j < a.batch && a.cu_seqlens_q[j] <= row));
+    if (a.batch <= kWave) {
+      b = __builtin_popcountll(
+          __builtin_amdgcn_ballot_w64(lane >= 1 && lane < a.batch && a.cu_seqlens_q[lane] <= row));
+    } else {
+      int lo = 0, hi = a.batch;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.cu_seqlens_q[mid] <= row) lo = mid; else hi = mid;
+      }
+      b = lo;
     }
     start = min(max(a.cu_seqlens_q[b], 0), a.rows);
     L = min(max(a.cu_seqlens_q[b + 1], start), a.rows) - start;

@@ -179,3 +179,17 @@ def test_rows_too_long_for_lds_staging():
     idx, scores = case.run()
     ref = oidx.block_scores_ref(case.q_np, case.cache_np, w.block_table, w.ctx)
     check(case, idx, scores, ref, "8300-page row")
+
+
+def test_ragged_batch_beyond_one_wave_of_requests():
+    """70 ragged requests: the top-k kernel finds a row's request by binary
+    search over cu_seqlens_q instead of one ballot over a wave."""
+    rng = np.random.default_rng(510)
+    ctx = [int(x) for x in rng.integers(1, 900, size=70)]
+    q_lens = [int(x) for x in rng.integers(1, 4, size=70)]
+    w = wl.small_case(seed=510, ctx=ctx, q_lens=q_lens, ragged=True)
+    print("70 ragged requests", w.rows, flush=True)
+    case = IndexCase(w, 3, max_q_len=3)
+    idx, scores = case.run()
+    ref = oidx.block_scores_ref(case.q_np, case.cache_np, w.block_table, w.ctx, w.cu)
+    check(case, idx, scores, ref, "70 ragged requests")

@@ -6,8 +6,9 @@ step's new tokens (the last q_len tokens of every request), then pa_decode
 The default workload is the 8K serving shape: batch 4, q_len 1, one KV head x
 16 query heads, head_dim 128, 128-token pages, contexts uniform in
 [8192, 9216], per-token e4m3 scales, random block table over a 4096-page
-pool.  Its cache is replicated over 64 layers (64 distinct pools) and steps
-rotate through them, as consecutive attention layers of one model would, so
+pool.  Its cache is replicated over 64 layers (64 distinct cache tensors
+sharing one block table) and steps rotate through them, as consecutive
+attention layers of one model would, so
 every step reads its KV from HBM rather than from the 256 MB Infinity Cache.
 
 Timing: W untimed warmup steps, then exactly K steps replayed from captured
@@ -61,8 +62,10 @@ def log(*a):
 
 
 class Layers:
-    """The workload's cache replicated over `n` layers in one allocation;
-    layer l's block table points at pool pages [l*NB, (l+1)*NB)."""
+    """The workload's cache replicated over `n` layers: one allocation,
+    whose pages [l*NB, (l+1)*NB) are layer l's cache tensor.  Every layer
+    uses the same block table and slot mapping, as a model's layers share a
+    request's block table and each has its own cache."""
 
     def __init__(self, w, n, dev, index_topk=0):
         self.w, self.n, self.dev = w, n, dev
@@ -112,8 +115,16 @@ class Layers:
             self.vs[l * NB:(l + 1) * NB].copy_(self.vs[:NB])
         torch.cuda.synchronize()
         log(f"cache for {w.name} x {n} layers written in {time.time() - t0:.1f}s")
+        # per-layer cache views, one shared block table
+        self.kcl = [self.kc[l * NB:(l + 1) * NB] for l in range(n)]
+        self.vcl = [self.vc[l * NB:(l + 1) * NB] for l in range(n)]
+        if w.mode == wl.PER_TOKEN:
+            self.ksl = [self.ks[l * NB:(l + 1) * NB] for l in range(n)]
+            self.vsl = [self.vs[l * NB:(l + 1) * NB] for l in range(n)]
+        else:
+            self.ksl, self.vsl = [self.ks_arg] * n, [self.vs_arg] * n
         bt = torch.from_numpy(w.block_table).to(dev)
-        self.bt = [torch.where(bt >= 0, bt + l * NB, bt).contiguous() for l in range(n)]
+        self.bt = [bt] * n
         self.ctx = torch.from_numpy(w.ctx).to(dev)
         self.cu = None if w.cu is None else torch.from_numpy(w.cu).to(dev)
         self.sp = None if w.sparse is None else torch.from_numpy(w.sparse).to(dev)
@@ -123,7 +134,7 @@ class Layers:
         k, v, s = w.step_tokens()
         self.step_k = torch.from_numpy(k).to(dev)
         self.step_v = torch.from_numpy(v).to(dev)
-        self.step_slots = [torch.from_numpy(s + np.int64(l * NB * 128)).to(dev) for l in range(n)]
+        self.step_slots = [torch.from_numpy(s).to(dev)] * n
         self.max_q_len = int(w.q_lens.max())
         if index_topk:
             # index cache over the same pages (layer l at pool pages l*NB ...),
@@ -133,6 +144,7 @@ class Layers:
             self.icache[:NB].copy_(torch.from_numpy(w.index_cache().reshape(NB, 128, 128)))
             for l in range(1, n):
                 self.icache[l * NB:(l + 1) * NB].copy_(self.icache[:NB])
+            self.icl = [self.icache[l * NB:(l + 1) * NB] for l in range(n)]
             self.q_idx = torch.from_numpy(w.index_queries()).to(dev).to(torch.bfloat16)
             self.scores = [torch.empty(w.rows, w.W, dtype=torch.float32, device=dev) for _ in range(n)]
             self.lists = [torch.empty(w.rows, index_topk, dtype=torch.int32, device=dev) for _ in range(n)]
@@ -146,18 +158,18 @@ class Layers:
     partition_mode = 0
 
     def step(self, l, ev=None, ev_index=None):
-        pa.kv_quant_write(self.step_k, self.step_v, self.step_slots[l], self.kc, self.vc,
-                          self.ks_arg, self.vs_arg, self.mode)
+        pa.kv_quant_write(self.step_k, self.step_v, self.step_slots[l], self.kcl[l], self.vcl[l],
+                          self.ksl[l], self.vsl[l], self.mode)
         sp = self.sp
         if self.index_topk:
             if ev_index is not None:
                 ev_index[0].record()
-            pa.pa_index_topk(self.q_idx, self.icache, self.bt[l], self.ctx, self.cu, self.lists[l],
+            pa.pa_index_topk(self.q_idx, self.icl[l], self.bt[l], self.ctx, self.cu, self.lists[l],
                              self.scores[l], max_q_len=self.max_q_len if self.cu is not None else 0)
             if ev_index is not None:
                 ev_index[1].record()
             sp = self.lists[l]
-        pa.pa_decode_ex(self.q[l], self.kc, self.vc, self.ks_arg, self.vs_arg, self.bt[l], self.ctx,
+        pa.pa_decode_ex(self.q[l], self.kcl[l], self.vcl[l], self.ksl[l], self.vsl[l], self.bt[l], self.ctx,
                         self.cu, sp, self.mode, self.out[l],
                         max_q_len=self.max_q_len if self.cu is not None else 0,
                         force_parts=self.force_parts, prefetch_depth=self.prefetch_depth,

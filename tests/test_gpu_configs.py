@@ -2,12 +2,14 @@
 times: the cache is written by kv_quant_write; sampled rows are checked
 element by element against the oracle (rebuilt on a compact cache of just
 those requests' pages); every row is checked against properties that hold
-at any size (finite, the default plan agrees with forced partition counts)."""
+at any size (finite, the default plan agrees with forced partition counts
+and with the other partition mode)."""
 
 import numpy as np
 import pytest
 import torch
 
+import fp8_paged_kv_pa_amd as pa
 import workloads as wl
 
 from harness import GpuCase, compact_request_oracle, compare
@@ -36,6 +38,16 @@ def _parts_agree(case, base, parts_list, what):
         compare(o, base.float().cpu().numpy(), atol=4e-3, cos_min=0.99999, what=f"{what} parts={p} vs default")
 
 
+def _modes_agree(w, case, base, what):
+    """Fixed and length-balanced partitions against the default plan (the
+    ragged calls with max_q_len, which balanced partitions need)."""
+    mq = int(w.q_lens.max()) if w.cu is not None else 0
+    for mode in (pa.PARTITION_FIXED, pa.PARTITION_BALANCED):
+        o = case.decode(out=torch.empty_like(case.out), partition_mode=mode, max_q_len=mq)
+        torch.cuda.synchronize()
+        compare(o, base.float().cpu().numpy(), atol=4e-3, cos_min=0.99999, what=f"{what} mode={mode} vs default")
+
+
 def test_c1_tiny():
     w = wl.c1_tiny()
     case = GpuCase(w)
@@ -47,6 +59,7 @@ def test_c2_dense_8k():
     case = GpuCase(w)
     base = _check(w, case, range(4), "c2")
     _parts_agree(case, base, [1, 8, 32], "c2")
+    _modes_agree(w, case, base, "c2")
 
 
 @pytest.mark.parametrize("mode", [wl.PER_TOKEN, wl.SCALAR])
@@ -55,6 +68,7 @@ def test_c3_dense_128k(mode):
     case = GpuCase(w)
     base = _check(w, case, [0, 17, 31], f"c3 mode={mode}")
     _parts_agree(case, base, [8, 16, 32], f"c3 mode={mode}")
+    _modes_agree(w, case, base, f"c3 mode={mode}")
     del case
     torch.cuda.empty_cache()
 
@@ -67,6 +81,7 @@ def test_c4_spec(kind):
     sample = sorted(set([0, w.B - 1] + short[:2]))
     base = _check(w, case, sample, f"c4 {kind}")
     _parts_agree(case, base, [4, 16], f"c4 {kind}")
+    _modes_agree(w, case, base, f"c4 {kind}")
 
 
 @pytest.mark.parametrize("tail", [False, True])

@@ -17,8 +17,9 @@
 //   S^T[token, row] = K[token, d] * Q^T[d, row]   (bf16 MFMA 16x16x32)
 // so the 16 KiB page is read once for all rows of a request (q_len 4 uses
 // 4 of the columns).  Index keys are token-major, so lane (r, g) of token
-// tile tau reads the 32 contiguous bytes of dims 32g..32g+31 of token
-// 16*tau + r; k-step j takes dims 32g + 8j .. +7 of that run, and the query
+// tile tau reads dims 16g..16g+15 and 64+16g..64+16g+15 of token 16*tau + r
+// (each of the two load instructions then covers whole 64-byte runs of the
+// tile); k-step j takes dims 64(j/2) + 16g + 8(j%2) .. +7, and the query
 // operand takes the same dims, so the dot product is over every dim once.
 //
 // index_topk_kernel: one workgroup per row.  Scores are mapped to
@@ -84,20 +85,23 @@ __global__ __launch_bounds__(kWave * kIdxWaves) void index_score_kernel(IndexArg
     return;
   }
 
-  // K: token 16*tau + r, dims 32g .. 32g+31 (two 16-byte loads per tile)
-  const uint8_t* kp = a.index_cache + int64_t(P) * 16384 + r * 128 + 32 * g;
+  // K: token 16*tau + r, dims 16g .. 16g+15 and 64+16g .. 64+16g+15 (two
+  // 16-byte loads per tile; each load instruction covers whole 64-byte
+  // runs, one per token)
+  const uint8_t* kp = a.index_cache + int64_t(P) * 16384 + r * 128 + 16 * g;
   u32x4 kb[8][2];
 #pragma unroll
   for (int tau = 0; tau < 8; ++tau) {
     kb[tau][0] = *reinterpret_cast<const u32x4*>(kp + tau * 2048);
-    kb[tau][1] = *reinterpret_cast<const u32x4*>(kp + tau * 2048 + 16);
+    kb[tau][1] = *reinterpret_cast<const u32x4*>(kp + tau * 2048 + 64);
   }
-  // Q^T operand: column r = row i0 + r, dims 32g + 8j .. +7 for k-step j
+  // Q^T operand: column r = row i0 + r, the same dims as K for each k-step:
+  // k-step j takes dims 64(j/2) + 16g + 8(j%2) .. +7
   bf16x8 qop[4];
   if (r < nrows) {
-    const uint16_t* qp = a.q + int64_t(start + i0 + r) * a.q_row_stride + 32 * g;
+    const uint16_t* qp = a.q + int64_t(start + i0 + r) * a.q_row_stride + 16 * g;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qop[j] = *reinterpret_cast<const bf16x8*>(qp + 8 * j);
+    for (int j = 0; j < 4; ++j) qop[j] = *reinterpret_cast<const bf16x8*>(qp + 64 * (j >> 1) + 8 * (j & 1));
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) qop[j] = bf16x8{};

@@ -410,7 +410,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the library has no "
               f"multi-GPU path; the decode kernel's per-GPU share is what one GPU shows).", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench needs a GPU"

@@ -42,6 +42,11 @@ namespace fp8pa {
 
 namespace {
 
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 constexpr float kLazyMax = 8.0f;  // log2 headroom before the running max moves
 constexpr int kAccPad = 132;      // LDS row pitch (floats) for the wave merge
 constexpr int kNoTokens = 1 << 30;  // token base of a position with nothing to read
@@ -129,44 +134,63 @@ __device__ __forceinline__ void consume_chunk(const Chunk<BF>& c) {
   if constexpr (PER_TOKEN) asm volatile("" ::"v"(c.ks[0]), "v"(c.ks[1]), "v"(c.vs[0]), "v"(c.vs[1]));
 }
 
-// Loads one wave's 32-token chunk of (page, KV head) block `blk`.  When
-// `valid` is false every lane reads the same 16 bytes of block 0 instead:
-// the same number of load instructions is issued on every path (so the
-// compiler's wait counts stay exact across the prefetch ring) at almost no
-// memory traffic.
+// Word 3 of a gfx9 buffer resource: raw (untyped) 32-bit data format, no
+// swizzle, no per-lane index stride.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// A raw buffer over `bytes` bytes at `p` (0: every access is out of range,
+// which returns zeros without touching memory).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), short(0), bytes, kRsrcWord3);
+}
+
+// Per-wave byte offsets of a lane's loads inside a block: the 16-byte
+// piece of its chunk, and the first of its 8 tokens' scales.
+struct LaneOffsets {
+  int kv;     // chunk * chunk_bytes + 16 * lane
+  int scale;  // 4 * (32 * chunk + 4 * (lane / 16))
+};
+template <bool BF>
+__device__ __forceinline__ LaneOffsets lane_offsets(int chunk, int lane) {
+  constexpr int kChunkBytes = BF ? 8192 : 4096;  // one 32-token chunk of a block
+  return LaneOffsets{chunk * kChunkBytes + 16 * lane, 4 * (32 * chunk + 4 * (lane >> 4))};
+}
+
+// Loads one wave's 32-token chunk of (page, KV head) block `blk` through
+// buffer resources whose base is the block: the block address stays in
+// scalar registers, every lane's offset is fixed per wave, and the four
+// (FP8) or eight (bf16) 1 KiB rows are immediate offsets -- no per-load
+// address arithmetic.  When `valid` is false the resources cover 0 bytes:
+// the same loads are issued (so the compiler's wait counts stay exact across
+// the prefetch ring) but they return zeros and touch no memory.
 template <bool PER_TOKEN, bool BF, bool ONCE>
 __device__ __forceinline__ void load_chunk(Chunk<BF>& c, const DecodeArgs& a, int64_t blk, bool valid,
-                                           int chunk, int lane) {
-  constexpr int64_t kBlockBytes = BF ? 32768 : 16384;  // one (page, head) block
-  constexpr int kChunkBytes = BF ? 8192 : 4096;        // one 32-token chunk of it
-  const int64_t base = valid ? blk * kBlockBytes + chunk * kChunkBytes + lane * 16 : 0;
-  const int istep = valid ? 64 : 0;
-  const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + base);
-  const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_cache + base);
+                                           LaneOffsets lo) {
+  constexpr int kBlockBytes = BF ? 32768 : 16384;  // one (page, head) block
+  const int64_t b = valid ? blk : 0;
+  const int nrec = valid ? kBlockBytes : 0;
+  const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.k_cache + b * kBlockBytes, nrec);
+  const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.v_cache + b * kBlockBytes, nrec);
   // ONCE: these K and V bytes are read once per call (one-row workgroups),
   // so non-temporal loads keep them from evicting what is reused (tables,
   // the split-K partials the merge reads next, the pages the writer
   // touches).  Two-row workgroups read each page once per row group, and
   // the second group's read should hit the cache.
-  if constexpr (ONCE) {
+  constexpr int kAux = ONCE ? 2 : 0;  // cache-policy bit 1: non-temporal
 #pragma unroll
-    for (int i = 0; i < Chunk<BF>::kRows; ++i) c.k[i] = __builtin_nontemporal_load(&kp[istep * i]);
+  for (int i = 0; i < Chunk<BF>::kRows; ++i)
+    c.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, lo.kv + 1024 * i, 0, kAux);
 #pragma unroll
-    for (int i = 0; i < Chunk<BF>::kRows; ++i) c.v[i] = __builtin_nontemporal_load(&vp[istep * i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < Chunk<BF>::kRows; ++i) c.k[i] = kp[istep * i];
-#pragma unroll
-    for (int i = 0; i < Chunk<BF>::kRows; ++i) c.v[i] = vp[istep * i];
-  }
+  for (int i = 0; i < Chunk<BF>::kRows; ++i)
+    c.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, lo.kv + 1024 * i, 0, kAux);
   if constexpr (PER_TOKEN) {
-    const int g = lane >> 4;
-    const int64_t sbase = valid ? blk * 128 + chunk * 32 + 4 * g : 0;
-    const int s4 = valid ? 16 : 0;
-    c.ks[0] = *reinterpret_cast<const f32x4*>(a.k_scale + sbase);
-    c.ks[1] = *reinterpret_cast<const f32x4*>(a.k_scale + sbase + s4);
-    c.vs[0] = *reinterpret_cast<const f32x4*>(a.v_scale + sbase);
-    c.vs[1] = *reinterpret_cast<const f32x4*>(a.v_scale + sbase + s4);
+    const int sn = valid ? 512 : 0;  // 128 fp32 scales per block
+    const __amdgpu_buffer_rsrc_t rks = block_rsrc(a.k_scale + b * 128, sn);
+    const __amdgpu_buffer_rsrc_t rvs = block_rsrc(a.v_scale + b * 128, sn);
+    c.ks[0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, lo.scale, 0, 0));
+    c.ks[1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, lo.scale + 64, 0, 0));
+    c.vs[0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, lo.scale, 0, 0));
+    c.vs[1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, lo.scale + 64, 0, 0));
   }
 }
 
@@ -312,6 +336,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   const int ps = wave >> 2;  // page stream: positions n0 + ps, n0 + ps + S, ...
   const int g = lane >> 4;   // lane group: tokens 4g..4g+3 of each 16-token tile
   const int hr = lane & 15;  // query head within the GQA group
+  const LaneOffsets lofs = lane_offsets<BF>(cw, lane);
   const int Hq = 16 * a.hkv;
 
   int part;
@@ -432,7 +457,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     }
     const bool ok0 = P0 >= 0 && P0 < a.num_blocks;
     tb[0] = ok0 ? ln0 * 128 : kNoTokens;
-    load_chunk<PER_TOKEN, BF, RT == 1>(buf[0], a, int64_t(P0) * a.hkv + h, ok0, cw, lane);
+    load_chunk<PER_TOKEN, BF, RT == 1>(buf[0], a, int64_t(P0) * a.hkv + h, ok0, lofs);
   }
   // query operands: B of S^T = K Q^T, lane = (head hr, dims 8g..8g+7 of
   // each 32-dim k-step)
@@ -533,6 +558,17 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
 
     // token of this lane's score slot e: t0 + 16*(e/4) + 4g + e%4
     if (!full) {
+      // One row: V scales of tokens past its cutoff become 0 (in the loaded
+      // registers); their scores are -inf, so p = 0, and p * 0 stays 0
+      // whatever an unwritten slot holds.  (Two rows mask P' per row below:
+      // the first row stops one token before the second, whose newest token
+      // has a written scale that need not be finite.  Without per-token
+      // scales p = 0 alone gives P' = 0.)
+      if constexpr (PER_TOKEN && RT == 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (t0 + 16 * (e >> 2) + 4 * g + (e & 3) >= lim_max) c.vs[e >> 2][e & 3] = 0.0f;
+      }
       // zero V of tokens past the context: those slots were never written
       // (a NaN there would survive a zero weight in the product)
       if constexpr (BF) {
@@ -638,22 +674,23 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
         m_run[r] = mn;
       }
       const float mu = (m_run[r] == -INFINITY) ? 0.0f : m_run[r];
-      float ps = 0.0f;
+      float pe[8];
       uint32_t hb[8];
       float lo[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = __builtin_amdgcn_exp2f(x[e] - mu);
-        ps += p;
+        pe[e] = p;
         float pv = p * vsf[e];
-        if (!full) {
+        if (PER_TOKEN && RT == 2 && !full) {
           const int t = t0 + 16 * (e >> 2) + 4 * g + (e & 3);
           pv = t < lim_r ? pv : 0.0f;
         }
         hb[e] = __float_as_uint(pv) & 0xFFFF0000u;
         lo[e] = pv - __uint_as_float(hb[e]);
       }
-      l_run[r] += ps;
+      // pairwise sum: three dependent adds instead of eight
+      l_run[r] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
       u32x4 hw;
 #pragma unroll
       for (int e = 0; e < 4; ++e) hw[e] = __builtin_amdgcn_perm(hb[2 * e + 1], hb[2 * e], 0x07060302u);
@@ -688,7 +725,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       const int P = raw_at(pos, ln);
       const bool ok = valid_page(P);
       tb[k] = ok ? ln * 128 : kNoTokens;
-      load_chunk<PER_TOKEN, BF, RT == 1>(buf[k], a, int64_t(P) * a.hkv + h, ok, cw, lane);
+      load_chunk<PER_TOKEN, BF, RT == 1>(buf[k], a, int64_t(P) * a.hkv + h, ok, lofs);
     }
     // raw entry of the next position to load (s0 + (NBUF-1)*S) and the
     // logical page of the one after it
@@ -708,7 +745,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
         const int nl = nn + (NBUF - 1) * S;
         const bool ok = valid_page(P_next);
         tb[ls] = ok ? ln_next * 128 : kNoTokens;
-        load_chunk<PER_TOKEN, BF, RT == 1>(buf[ls], a, int64_t(P_next) * a.hkv + h, ok, cw, lane);
+        load_chunk<PER_TOKEN, BF, RT == 1>(buf[ls], a, int64_t(P_next) * a.hkv + h, ok, lofs);
         // table reads for the following steps (checked one step later)
         ln_next = ln_after;
         P_next = raw_at(nl + S, ln_next);

@@ -42,10 +42,11 @@ namespace fp8pa {
 
 namespace {
 
-template <bool B>
-struct Flag {
-  static constexpr bool value = B;
-};
+
+// An empty volatile asm: a block that holds one cannot be speculated, so
+// the compiler keeps a uniform branch around the tail-chunk masks instead of
+// turning them into selects that every full chunk would execute.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
 
 constexpr float kLazyMax = 8.0f;  // log2 headroom before the running max moves
 constexpr int kAccPad = 132;      // LDS row pitch (floats) for the wave merge
@@ -558,6 +559,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
 
     // token of this lane's score slot e: t0 + 16*(e/4) + 4g + e%4
     if (!full) {
+      keep_branch();
       // One row: V scales of tokens past its cutoff become 0 (in the loaded
       // registers); their scores are -inf, so p = 0, and p * 0 stays 0
       // whatever an unwritten slot holds.  (Two rows mask P' per row below:
@@ -654,6 +656,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       }
       const int lim_r = min(lim0 + min(r, nrows - 1), cap);
       if (!full) {
+        keep_branch();
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int t = t0 + 16 * (e >> 2) + 4 * g + (e & 3);
@@ -674,20 +677,26 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
         m_run[r] = mn;
       }
       const float mu = (m_run[r] == -INFINITY) ? 0.0f : m_run[r];
-      float pe[8];
+      float pe[8], pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pe[e] = __builtin_amdgcn_exp2f(x[e] - mu);
+        pv[e] = pe[e] * vsf[e];
+      }
+      if (PER_TOKEN && RT == 2 && !full) {
+        keep_branch();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = t0 + 16 * (e >> 2) + 4 * g + (e & 3);
+          pv[e] = t < lim_r ? pv[e] : 0.0f;
+        }
+      }
       uint32_t hb[8];
       float lo[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(x[e] - mu);
-        pe[e] = p;
-        float pv = p * vsf[e];
-        if (PER_TOKEN && RT == 2 && !full) {
-          const int t = t0 + 16 * (e >> 2) + 4 * g + (e & 3);
-          pv = t < lim_r ? pv : 0.0f;
-        }
-        hb[e] = __float_as_uint(pv) & 0xFFFF0000u;
-        lo[e] = pv - __uint_as_float(hb[e]);
+        hb[e] = __float_as_uint(pv[e]) & 0xFFFF0000u;
+        lo[e] = pv[e] - __uint_as_float(hb[e]);
       }
       // pairwise sum: three dependent adds instead of eight
       l_run[r] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));

@@ -219,3 +219,61 @@ def test_graph_replays_match_eager(merge_mode):
         torch.cuda.synchronize()
         compare(other, oracle_out(w), what=f"eager between replays {rep}")
     compare(eager, oracle_out(w), what="eager")
+
+
+NONFINITE_CASES = [
+    dict(seed=231, ctx=[300, 513, 129], q_lens=[1, 1, 1], Hkv=2),                    # one-row tails
+    dict(seed=232, ctx=[700, 45, 300], q_lens=[2, 2, 2]),                            # two-row groups
+    dict(seed=233, ctx=[600, 301, 250, 90], q_lens=[4, 4, 6, 2], ragged=True),       # ragged
+    dict(seed=234, ctx=[5000, 2100], q_lens=[1, 1], sparse_topk=6),                  # sparse
+]
+
+
+@pytest.mark.parametrize("kw", NONFINITE_CASES, ids=[str(c["seed"]) for c in NONFINITE_CASES])
+@pytest.mark.parametrize("parts", [0, 1, 3])
+def test_nonfinite_scales_past_the_context_never_leak(kw, parts):
+    # The slots of each request's last page past its context were never
+    # written: give them NaN K scales and infinite V scales.  Their scores are
+    # masked and their weights are exactly 0, so the output must stay finite
+    # and equal the oracle's (which never reads those slots).
+    w = wl.small_case(**kw)
+    print("non-finite tail case", w.name, "parts", parts, flush=True)
+    case = GpuCase(w)
+    ks = case.ks.view(-1, w.Hkv, 128)
+    vs = case.vs.view(-1, w.Hkv, 128)
+    for b in range(w.B):
+        c = int(w.ctx[b])
+        if c % 128 == 0:
+            continue
+        n = c // 128
+        if n >= w.W:
+            continue
+        P = int(w.block_table[b, n])
+        ks[P, :, c % 128:] = float("nan")
+        vs[P, :, c % 128:] = float("inf")
+    out = case.decode(force_parts=parts) if parts else case.decode()
+    torch.cuda.synchronize()
+    compare(out, oracle_out(w), what=f"{w.name} non-finite tail scales parts={parts}")
+
+
+@pytest.mark.parametrize("parts", [0, 1, 3])
+def test_two_row_group_first_row_ignores_second_rows_newest_token(parts):
+    # q_len 2: the second row's newest token (position ctx - 1) is not seen by
+    # the first row.  With an infinite V scale on that token, the first row
+    # must still match the oracle exactly; the second row attends it, and its
+    # output is non-finite on both sides.
+    w = wl.small_case(seed=235, ctx=[700, 300], q_lens=[2, 2])
+    print("two-row newest-token case parts", parts, flush=True)
+    case = GpuCase(w)
+    cache = oracle_cache(w)
+    t = int(w.ctx[0]) - 1
+    P = int(w.block_table[0, t // 128])
+    case.vs.view(-1, w.Hkv, 128)[P, 0, t % 128] = float("inf")
+    cache[5][(P * w.Hkv + 0) * 128 + t % 128] = np.inf  # the oracle's per-token V scales
+    out = case.decode(force_parts=parts) if parts else case.decode()
+    torch.cuda.synchronize()
+    ref = oracle_out(w, cache=cache)
+    assert not np.all(np.isfinite(ref[1])), "the second row attends the infinite scale"
+    assert not torch.all(torch.isfinite(out[1])).item(), "GPU: second row should be non-finite"
+    keep = [0, 2, 3]
+    compare(out[keep], ref[keep], what=f"first row beside an infinite newest token parts={parts}")

@@ -765,8 +765,15 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   }
 
   // ---- merge the waves, then write output or the partition partial --------
+  // Per row, every wave leaves its (max, sum) and its unscaled accumulators
+  // in LDS; after one barrier each thread of the first 256 weights the
+  // waves' accumulators of its (head, 8 dims) by 2^(m_w - max) and sums them.
+  const int t = threadIdx.x;
+  const int oh = (t >> 4) & 15;  // output head handled by this thread (threads < 256)
+  const int od = (t & 15) * 8;   // first of its 8 dims
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
+    if (r >= nrows) break;
     float lh = l_run[r];
     lh += __shfl_xor(lh, 16, kWave);
     lh += __shfl_xor(lh, 32, kWave);
@@ -774,40 +781,26 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       sm_ml[wave][r][hr][0] = m_run[r];
       sm_ml[wave][r][hr][1] = lh;
     }
-  }
-  __syncthreads();
-  const int t = threadIdx.x;
-  const int oh = (t >> 4) & 15;  // output head handled by this thread (threads < 256)
-  const int od = (t & 15) * 8;   // first of its 8 dims
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    if (r >= nrows) break;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[w][r][hr][0]);
-    const float f = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[r] - M);
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      f32x4 v = acc[r][d] * f;
-      *reinterpret_cast<f32x4*>(&sm_acc[wave][hr][16 * d + 4 * g]) = v;
-    }
+    for (int d = 0; d < 8; ++d) *reinterpret_cast<f32x4*>(&sm_acc[wave][hr][16 * d + 4 * g]) = acc[r][d];
     __syncthreads();
     if (t < 256) {
+      float mw[NW];
       float Mo = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) Mo = fmaxf(Mo, sm_ml[w][r][oh][0]);
-      float Ls = 0.0f;
-#pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float mw = sm_ml[w][r][oh][0];
-        const float fw = (Mo == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - Mo);
-        Ls += fw * sm_ml[w][r][oh][1];
+        mw[w] = sm_ml[w][r][oh][0];
+        Mo = fmaxf(Mo, mw[w]);
       }
+      float Ls = 0.0f;
       f32x4 s0v = {0.f, 0.f, 0.f, 0.f}, s1v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        s0v += *reinterpret_cast<const f32x4*>(&sm_acc[w][oh][od]);
-        s1v += *reinterpret_cast<const f32x4*>(&sm_acc[w][oh][od + 4]);
+        // a wave that saw no token has m = -inf: weight 0
+        const float fw = (Mo == -INFINITY || mw[w] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - Mo);
+        Ls += fw * sm_ml[w][r][oh][1];
+        s0v += fw * *reinterpret_cast<const f32x4*>(&sm_acc[w][oh][od]);
+        s1v += fw * *reinterpret_cast<const f32x4*>(&sm_acc[w][oh][od + 4]);
       }
       const int row = row0 + r;
       const int qh = 16 * h + oh;

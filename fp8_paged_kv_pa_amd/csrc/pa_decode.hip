@@ -48,6 +48,22 @@ namespace {
 // turning them into selects that every full chunk would execute.
 __device__ __forceinline__ void keep_branch() { asm volatile(""); }
 
+// Maxima of a chunk's scores in 4 instructions for 8 values.  fmaxf lowers
+// to maxnum, for which the compiler first quiets each input with a v_max of
+// the value with itself; the scores are products and selects, never
+// signaling NaNs, so v_max3 / v_max take them as they are (a quiet NaN
+// yields the other operand either way).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 constexpr float kLazyMax = 8.0f;  // log2 headroom before the running max moves
 constexpr int kAccPad = 132;      // LDS row pitch (floats) for the wave merge
 constexpr int kNoTokens = 1 << 30;  // token base of a position with nothing to read
@@ -663,8 +679,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
           x[e] = t < lim_r ? x[e] : -INFINITY;
         }
       }
-      const float lm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      const float lm = max3f(max3f(x[0], x[1], x[2]), max3f(x[3], x[4], x[5]), max2f(x[6], x[7]));
       const bool need = lm > m_run[r] + kLazyMax;
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
         float gm = fmaxf(lm, __shfl_xor(lm, 16, kWave));

@@ -9,6 +9,8 @@ stream.
 
 import ctypes
 
+import torch
+
 from ._lib import (  # noqa: F401
     EXPORTS, MERGE_IN_KERNEL, MERGE_PLAN, MERGE_SEPARATE, PARTITION_BALANCED, PARTITION_FIXED,
     PARTITION_PLAN, PaConfig, PaDecodeOpts, PaError, PaPlanInfo, PaTensor, SCALE_NONE,
@@ -55,6 +57,34 @@ def pa_decode_ex(q, k_cache, v_cache, k_scale, v_scale, block_table, context_len
     check(lib.pa_decode_ex(*[ref(x) for x in d], int(scale_mode), ref(do), ctypes.byref(opts),
                            stream_handle(stream)))
     return out
+
+
+CHECK_KINDS = ("cu_ends", "cu_order", "ctx_short", "table_id", "sparse_id", "sparse_dup", "scale")
+
+
+def pa_check_decode_inputs(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                           cu_seqlens_q, sparse_page_idx, scale_mode, out, report, stream=None):
+    """Device-side check of a ``pa_decode`` call's inputs into ``report``
+    (a device int32 tensor of 16 entries; see ``pa_check_decode_inputs`` in
+    include/fp8pa.h).  Read ``report`` after synchronising the stream."""
+    lib = load()
+    if report.dtype != torch.int32 or report.numel() < 16 or not report.is_cuda:
+        raise ValueError("report must be a device int32 tensor of at least 16 entries")
+    d = [desc(t) for t in (q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                           cu_seqlens_q, sparse_page_idx)]
+    do = desc(out)
+    check(lib.pa_check_decode_inputs(*[ref(x) for x in d], int(scale_mode), ref(do), report.data_ptr(),
+                                     stream_handle(stream)))
+    return report
+
+
+def check_report(report):
+    """The report as a dict: violating items, the kinds found and the
+    smallest offending index of each kind."""
+    r = [int(x) for x in report.cpu().tolist()[:2 + len(CHECK_KINDS)]]
+    return {"count": r[0],
+            "kinds": [k for i, k in enumerate(CHECK_KINDS) if r[1] >> i & 1],
+            "first": {k: r[2 + i] for i, k in enumerate(CHECK_KINDS) if r[1] >> i & 1}}
 
 
 def kv_quant_write(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, scale_mode,

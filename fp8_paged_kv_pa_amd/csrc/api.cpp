@@ -164,8 +164,8 @@ int get_scratch(hipStream_t stream, size_t need_counters, size_t need_partials, 
 // ---------------------------------------------------------------------------
 int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const pa_tensor* ks,
                 const pa_tensor* vs, const pa_tensor* bt, const pa_tensor* ctx, const pa_tensor* cu,
-                const pa_tensor* sp, int mode, pa_tensor* out, const pa_decode_opts* opts,
-                void* stream_ptr) {
+                const pa_tensor* sp, int mode, const pa_tensor* out, const pa_decode_opts* opts,
+                void* stream_ptr, int32_t* check_report = nullptr) {
   g_err.clear();
   int rc;
   if ((rc = check_tensor(q, "q"))) return rc;
@@ -244,9 +244,35 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   Plan plan;
   std::string perr;
   if ((rc = make_plan(cfg, &plan, &perr))) return fail(rc, perr);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  if (check_report) {
+    // the device-side input check: the same host validation, then the check
+    // kernel instead of the decode (no scratch, nothing written but the report)
+    if (!aligned(check_report, 4)) return fail(PA_ERR_LAYOUT, "report must be 4-byte aligned");
+    DecodeArgs c{};
+    c.k_scale = mode == PA_SCALE_NONE ? nullptr : static_cast<const float*>(ks->data);
+    c.v_scale = mode == PA_SCALE_NONE ? nullptr : static_cast<const float*>(vs->data);
+    c.block_table = static_cast<const int32_t*>(bt->data);
+    c.bt_stride = bt->stride[0];
+    c.context_lens = static_cast<const int32_t*>(ctx->data);
+    c.cu_seqlens_q = ragged ? static_cast<const int32_t*>(cu->data) : nullptr;
+    c.sparse_idx = sparse ? static_cast<const int32_t*>(sp->data) : nullptr;
+    c.sp_stride = sparse ? sp->stride[0] : 0;
+    c.num_blocks = nb;
+    c.hkv = int32_t(hkv);
+    c.rows = int32_t(rows);
+    c.batch = int32_t(B);
+    c.width = int32_t(W);
+    c.topk = int32_t(topk);
+    c.uniform_q_len = ragged ? 0 : int32_t(rows / B);
+    c.scale_mode = mode;
+    c.kv_bf16 = bf16kv ? 1 : 0;
+    hipError_t he = launch_check(c, check_report, stream);
+    if (he != hipSuccess) return fail(PA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(he));
+    return PA_OK;
+  }
   if (rows == 0) return PA_OK;
 
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
   uint32_t* counters = nullptr;
   void* scratch = nullptr;
   if ((rc = get_scratch(stream, size_t(plan.counter_bytes), size_t(plan.scratch_bytes - plan.counter_bytes),
@@ -329,6 +355,16 @@ int pa_decode_ex(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* 
                  const pa_decode_opts* opts, void* stream) {
   return decode_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, cu_seqlens_q,
                      sparse_page_idx, scale_mode, out, opts, stream);
+}
+
+int pa_check_decode_inputs(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                           const pa_tensor* k_scale, const pa_tensor* v_scale, const pa_tensor* block_table,
+                           const pa_tensor* context_lens, const pa_tensor* cu_seqlens_q,
+                           const pa_tensor* sparse_page_idx, int scale_mode, const pa_tensor* out,
+                           int32_t* report, void* stream) {
+  if (!report) return fail(PA_ERR_INVALID_ARG, "report must be a device int32[16] buffer");
+  return decode_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, cu_seqlens_q,
+                     sparse_page_idx, scale_mode, out, nullptr, stream, report);
 }
 
 int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,

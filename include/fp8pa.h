@@ -260,6 +260,44 @@ int pa_decode_ex(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* 
                  const pa_tensor* cu_seqlens_q, const pa_tensor* sparse_page_idx,
                  int scale_mode, pa_tensor* out, const pa_decode_opts* opts, void* stream);
 
+/* Device-side check of a pa_decode call's inputs -- the preconditions the
+ * host cannot see without reading device memory.  The pages keep a kernel-side
+ * assert as a backstop for malformed decode metadata (ROCm/ATOM pull request
+ * 2122, section 2: ragged query rows mis-mapped as uniform ones, and the
+ * assert kept beside the fix); here the check is a separate call that
+ * reports instead of trapping, so a caller can run it on suspect batches
+ * (debug builds, tests, input replay) while pa_decode itself stays unchanged.
+ *
+ * Arguments: exactly those of pa_decode (the same host validation runs and
+ * returns the same pa_status), plus
+ *   report   device int32 [16], caller-owned; written on `stream`:
+ *              report[0]      number of violating items found (0 = clean)
+ *              report[1]      bitmask over pa_check_kind
+ *              report[2 + k]  smallest offending index of kind k, or
+ *                             INT32_MAX when kind k did not occur
+ *            Read it after synchronising `stream`.
+ * Nothing is allocated and no output is written; `out` is only validated.
+ * Every read stays inside the tensors the descriptors describe, whatever
+ * their device values.  Returns PA_OK or a pa_status. */
+typedef enum pa_check_kind {
+  PA_CHECK_CU_ENDS = 0,     /* cu_seqlens_q[0] != 0 or cu_seqlens_q[batch] != rows (index 0)    */
+  PA_CHECK_CU_ORDER = 1,    /* cu_seqlens_q[b+1] < cu_seqlens_q[b] (index b)                    */
+  PA_CHECK_CTX_SHORT = 2,   /* context_lens[b] < the request's q_len (index b)                  */
+  PA_CHECK_TABLE_ID = 3,    /* an attended page's block-table id outside [0, num_blocks)
+                               (index b * W + logical page)                                       */
+  PA_CHECK_SPARSE_ID = 4,   /* a list entry neither -1 nor in [0, W) (index row * topk + i)      */
+  PA_CHECK_SPARSE_DUP = 5,  /* a page listed twice in one row (index row)                         */
+  PA_CHECK_SCALE = 6        /* per-token scale of an attended token not finite or negative
+                               (index b * W + logical page); scalar scale not finite or <= 0
+                               (index 0)                                                          */
+} pa_check_kind;
+
+int pa_check_decode_inputs(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                           const pa_tensor* k_scale, const pa_tensor* v_scale,
+                           const pa_tensor* block_table, const pa_tensor* context_lens,
+                           const pa_tensor* cu_seqlens_q, const pa_tensor* sparse_page_idx,
+                           int scale_mode, const pa_tensor* out, int32_t* report, void* stream);
+
 /*
  * kv_quant_write -- the single cache writer ([ATOM-2710] review "Smaller":
  * one shared writer; [ATOM-2614] "Problem": page-shuffled FP8 plus

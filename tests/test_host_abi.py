@@ -290,3 +290,29 @@ def test_index_topk_accepts_a_well_formed_empty_call():
     t = _index_args(q=_host_tensor((0, 128), torch.bfloat16), idx=_host_tensor((0, 32), torch.int32),
                     scores=_host_tensor((0, 3), torch.float32))
     assert _call_index(t) == 0, pa.pa_last_error()
+
+
+def _call_check(t, report):
+    lib = pa.load()
+    d = [_lib.desc(t[k]) for k in ("q", "k", "v", "ks", "vs", "bt", "ctx", "cu", "sp")]
+    do = _lib.desc(t["out"])
+    return lib.pa_check_decode_inputs(*[_lib.ref(x) for x in d], t["mode"], _lib.ref(do), report, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=_host_tensor((4, 16, 128), torch.float32)), -2),
+    (dict(ctx=_host_tensor((3,), torch.int32)), -3),
+    (dict(sp=_host_tensor((3, 4), torch.int32)), -3),
+    (dict(q=_host_tensor((6, 16, 128), torch.bfloat16), out=_host_tensor((6, 16, 128), torch.bfloat16)), -3),
+    (dict(mode=5), -1),
+])
+def test_input_check_runs_the_decode_host_validation_first(over, status):
+    # the same host checks as pa_decode, before anything is launched (the
+    # report pointer is never touched on these paths)
+    assert _call_check(_decode_args(**over), ctypes.c_void_p(0x10000)) == status
+    assert pa.pa_last_error()
+
+
+def test_input_check_needs_a_report_buffer():
+    assert _call_check(_decode_args(), None) == -1
+    assert "report" in pa.pa_last_error()

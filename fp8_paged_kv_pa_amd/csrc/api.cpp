@@ -19,6 +19,7 @@
 #include <utility>
 
 #include "../../include/fp8pa.h"
+#include "check.h"
 #include "launch.h"
 #include "plan.h"
 

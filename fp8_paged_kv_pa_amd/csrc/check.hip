@@ -18,7 +18,7 @@
 #include <climits>
 
 #include "device_common.h"
-#include "launch.h"
+#include "check.h"
 
 namespace fp8pa {
 

@@ -100,8 +100,6 @@ hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool spa
                          hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_index(const IndexArgs& a, int64_t score_grid, hipStream_t stream);
-// Check of a decode call's device-side inputs into `report` (int32[16]).
-hipError_t launch_check(const DecodeArgs& a, int32_t* report, hipStream_t stream);
 // Workgroups of the block-score kernel for `units` (request, 16-row group) pairs.
 int64_t index_score_grid(int64_t units, int32_t width);
 

@@ -664,11 +664,14 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     bf16x8 phi[RT], plo[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
+      // scores relative to the running max (0 before the row has one): the
+      // subtraction rides in the fma, and the lazy test is on x directly
+      const float mu = (m_run[r] == -INFINITY) ? 0.0f : m_run[r];
       float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[e] = st[r][0][e] * kc[e];
-        x[4 + e] = st[r][1][e] * kc[4 + e];
+        x[e] = fmaf(st[r][0][e], kc[e], -mu);
+        x[4 + e] = fmaf(st[r][1][e], kc[4 + e], -mu);
       }
       const int lim_r = min(lim0 + min(r, nrows - 1), cap);
       if (!full) {
@@ -680,22 +683,25 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
         }
       }
       const float lm = max3f(max3f(x[0], x[1], x[2]), max3f(x[3], x[4], x[5]), max2f(x[6], x[7]));
-      const bool need = lm > m_run[r] + kLazyMax;
+      const bool need = lm > (m_run[r] == -INFINITY ? -INFINITY : kLazyMax);
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
         float gm = fmaxf(lm, __shfl_xor(lm, 16, kWave));
         gm = fmaxf(gm, __shfl_xor(gm, 32, kWave));
-        const float mn = fmaxf(m_run[r], gm);
+        const float mn = fmaxf(m_run[r], gm + mu);
         const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[r] - mn);
         l_run[r] *= alpha;
 #pragma unroll
         for (int d = 0; d < 8; ++d) acc[r][d] *= alpha;
         m_run[r] = mn;
+        // re-base the chunk's scores on the new max
+        const float shift = (mn == -INFINITY) ? 0.0f : mn - mu;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] -= shift;
       }
-      const float mu = (m_run[r] == -INFINITY) ? 0.0f : m_run[r];
       float pe[8], pv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pe[e] = __builtin_amdgcn_exp2f(x[e] - mu);
+        pe[e] = __builtin_amdgcn_exp2f(x[e]);
         pv[e] = pe[e] * vsf[e];
       }
       if (PER_TOKEN && RT == 2 && !full) {

@@ -244,7 +244,7 @@ typedef struct pa_plan_info {
  * Device-side preconditions (not checked on the host): cu_seqlens_q
  * monotone with the stated ends, context_len >= q_len, sparse lists free of
  * duplicates, finite scales.  Violations give unspecified output values but
- * no out-of-bounds access.
+ * no out-of-bounds access; pa_check_decode_inputs reports them.
  */
 int pa_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
               const pa_tensor* k_scale, const pa_tensor* v_scale,

@@ -634,6 +634,11 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       }
     }
 
+    // Two-row workgroups run two waves per SIMD.  A wave raises its issue
+    // priority while it issues its MFMA blocks, so the SIMD hands them to it
+    // ahead of the other wave's softmax instructions and the matrix pipe
+    // runs under that wave's VALU work instead of after it.
+    if constexpr (RT == 2) __builtin_amdgcn_s_setprio(1);
     // S^T = K Q^T for every row tile, k-step outer so each converted K
     // operand (exact e4m3 -> bf16, or the bf16 itself) serves all row tiles
     f32x4 st[RT][2];
@@ -656,6 +661,8 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
         st[r][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qv, st[r][1], 0, 0, 0);
       }
     }
+
+    if constexpr (RT == 2) __builtin_amdgcn_s_setprio(0);
 
     // online softmax per row tile; P' = p * v_scale as a bf16 hi + lo pair:
     // hi keeps the top 8 significant bits (truncation), lo = P' - hi is exact
@@ -729,6 +736,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       for (int e = 0; e < 8; ++e) plo[r][e] = (__bf16)lo[e];
     }
 
+    if constexpr (RT == 2) __builtin_amdgcn_s_setprio(1);
     // O^T += V^T P'^T, d-tile outer so each converted V operand serves all
     // row tiles
 #pragma unroll
@@ -742,6 +750,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
         acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[r], acc[r][d], 0, 0, 0);
       }
     }
+    if constexpr (RT == 2) __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- stream the partition's pages: a ring of NBUF chunk buffers, the

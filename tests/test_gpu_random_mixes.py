@@ -76,6 +76,18 @@ def test_random_call_matches_oracle(seed):
     compare(out, oracle_out(w), what=f"random mix {seed} {opts}")
 
 
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", SEEDS[::4])
+def test_random_call_over_a_bf16_cache_matches_oracle(seed):
+    """The same draws over an unquantized bf16 cache (no scales)."""
+    w, opts = draw(seed)
+    w = wl.bf16_kv(w)
+    print("random mix bf16", seed, "q_lens", list(w.q_lens), "ctx", list(w.ctx), "opts", opts, flush=True)
+    out = GpuCase(w).decode(**opts)
+    torch.cuda.synchronize()
+    compare(out, oracle_out(w), what=f"random mix bf16 {seed} {opts}")
+
 def test_draws_cover_every_kind_and_option():
     """The seeds above reach every call kind, scale mode and plan option."""
     kinds, modes, keys, pms = set(), set(), set(), set()

@@ -102,6 +102,39 @@ def test_index_topk_matches_oracle(kw, topk):
     check(case, idx, scores, ref, f"{w.name} topk={topk}")
 
 
+
+def random_index_draw(seed):
+    """A seeded random indexer call: batch, rows per request (uniform or
+    ragged), contexts (empty, next to a page edge, or anywhere) and k."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 7))
+    ragged = bool(rng.random() < 0.5)
+    q_lens = [int(x) for x in rng.integers(1, 9, size=B)] if ragged else [int(rng.integers(1, 6))] * B
+    ctx = []
+    for L in q_lens:
+        u = rng.random()
+        if u < 0.1:
+            c = 0
+        elif u < 0.5:
+            c = 128 * int(rng.integers(1, 24)) + int(rng.integers(-1, 2))
+        else:
+            c = int(rng.integers(1, 3000))
+        ctx.append(c if c == 0 else max(c, L))
+    topk = int(rng.choice([1, 2, 5, 16, 33]))
+    hint = int(max(q_lens)) if ragged and rng.random() < 0.5 else 0
+    return wl.small_case(seed=seed, ctx=ctx, q_lens=q_lens, ragged=ragged), topk, hint
+
+
+@pytest.mark.parametrize("seed", list(range(701, 725)))
+def test_random_index_calls_match_oracle(seed):
+    w, topk, hint = random_index_draw(seed)
+    print("random index call", seed, "q_lens", list(w.q_lens), "ctx", list(w.ctx), "topk", topk, "hint", hint,
+          flush=True)
+    case = IndexCase(w, topk, max_q_len=hint)
+    idx, scores = case.run()
+    ref = oidx.block_scores_ref(case.q_np, case.cache_np, w.block_table, w.ctx, w.cu)
+    check(case, idx, scores, ref, f"random index {seed}")
+
 def test_max_q_len_hint_gives_the_same_result():
     w = wl.small_case(seed=506, ctx=[1500, 600, 300], q_lens=[5, 1, 3], ragged=True)
     a = IndexCase(w, 6).run()

@@ -126,3 +126,58 @@ def test_writer_exhaustive_codes_in_none_mode():
     owr.quant_write_ref(x, x, slots, kc, vc, None, None, wl.NONE, 1)
     assert np.array_equal(kc_g.cpu().numpy().reshape(-1), kc)
     assert np.array_equal(vc_g.cpu().numpy().reshape(-1), vc)
+
+
+@pytest.mark.parametrize("seed", list(range(801, 833)))
+def test_writer_random_calls_bit_exact(seed):
+    """Seeded random writer calls: 1-300 tokens, 1-4 KV heads, fp32 or bf16
+    inputs, every scale mode, per-token magnitudes from 1e-30 to 1e30 with
+    all-zero tokens, and slots that are distinct, skipped (-1) or past the
+    pool; every byte and scale bit against the oracle's writer."""
+    rng = np.random.default_rng(seed)
+    dev = torch.device("cuda:0")
+    T = int(rng.integers(1, 301))
+    Hkv = int(rng.integers(1, 5))
+    nb = int(rng.integers(1, 5))
+    mode = [wl.PER_TOKEN, wl.SCALAR, wl.NONE][int(rng.integers(0, 3))]
+    bf16_in = bool(rng.random() < 0.4)
+    mag = (10.0 ** rng.uniform(-30, 30, size=(T, Hkv, 1))) if mode == wl.PER_TOKEN else \
+        (10.0 ** rng.uniform(-3, 3, size=(T, Hkv, 1)))
+    k = (rng.standard_normal((T, Hkv, 128)) * mag).astype(np.float32)
+    v = (rng.standard_normal((T, Hkv, 128)) * mag).astype(np.float32)
+    k[rng.random(T) < 0.05] = 0.0
+    if bf16_in:
+        k, v = wl.bf16_round(k), wl.bf16_round(v)
+    slots = rng.permutation(nb * 128)[:T].astype(np.int64)
+    if T > nb * 128:
+        slots = np.concatenate([slots, np.full(T - nb * 128, -1, np.int64)])
+    slots[rng.random(T) < 0.1] = -1
+    slots[rng.random(T) < 0.05] = nb * 128 + int(rng.integers(0, 1000))
+    print("writer random", seed, "T", T, "Hkv", Hkv, "nb", nb, "mode", mode, "bf16", bf16_in, flush=True)
+    kc0 = rng.integers(0, 256, size=nb * Hkv * 16384, dtype=np.uint8)
+    vc0 = rng.integers(0, 256, size=nb * Hkv * 16384, dtype=np.uint8)
+    s0 = np.full(nb * Hkv * 128, -3.0, np.float32)
+    kc_g = torch.from_numpy(kc0.copy()).to(dev).view(nb, Hkv, 16384)
+    vc_g = torch.from_numpy(vc0.copy()).to(dev).view(nb, Hkv, 16384)
+    if mode == wl.SCALAR:
+        sk, sv = np.float32(rng.uniform(1e-3, 1)), np.float32(rng.uniform(1e-3, 1))
+        ks_g, vs_g = torch.tensor([sk], device=dev), torch.tensor([sv], device=dev)
+    elif mode == wl.PER_TOKEN:
+        ks_g = torch.from_numpy(s0.copy()).to(dev).view(nb, Hkv, 128)
+        vs_g = torch.from_numpy(s0.copy()).to(dev).view(nb, Hkv, 128)
+    else:
+        ks_g = vs_g = None
+    tin = torch.bfloat16 if bf16_in else torch.float32
+    pa.kv_quant_write(torch.from_numpy(k).to(dev).to(tin), torch.from_numpy(v).to(dev).to(tin),
+                      torch.from_numpy(slots).to(dev), kc_g, vc_g, ks_g, vs_g, mode)
+    torch.cuda.synchronize()
+    kc, vc, ks, vs = kc0.copy(), vc0.copy(), s0.copy(), s0.copy()
+    if mode == wl.SCALAR:
+        owr.quant_write_ref(k, v, slots, kc, vc, np.array([sk]), np.array([sv]), mode, Hkv)
+    else:
+        owr.quant_write_ref(k, v, slots, kc, vc, ks, vs, mode, Hkv)
+    assert np.array_equal(kc_g.cpu().numpy().reshape(-1), kc)
+    assert np.array_equal(vc_g.cpu().numpy().reshape(-1), vc)
+    if mode == wl.PER_TOKEN:
+        assert np.array_equal(ks_g.cpu().numpy().reshape(-1).view(np.uint32), ks.view(np.uint32))
+        assert np.array_equal(vs_g.cpu().numpy().reshape(-1).view(np.uint32), vs.view(np.uint32))

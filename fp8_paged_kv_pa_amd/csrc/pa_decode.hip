@@ -124,7 +124,17 @@ __device__ __forceinline__ Balanced balanced_layout(const DecodeArgs& a) {
   r.ctx = live ? a.context_lens[lane] : 0;
   const int np = (max(0, min(r.ctx, a.width * 128)) + 127) >> 7;  // pages the request's last row sees
   const int total = int(wave_reduce_u32<UOp::ADD>(uint32_t(np)));
-  auto parts_at = [&](int ppp) { return live ? max(1, (np + ppp - 1) / ppp) : 0; };
+  // max(1, ceil(np / ppp)) per request.  np <= 2^20, so the float quotient
+  // (exact operands below 2^24, a reciprocal within 2 ulp) is within one of
+  // floor((np + ppp - 1) / ppp), and one correction each way makes it exact;
+  // this is a third of the instructions of a 32-bit integer division.
+  auto parts_at = [&](int ppp) {
+    const uint32_t n = uint32_t(np + ppp - 1), d = uint32_t(ppp);
+    uint32_t q = uint32_t(float(n) * __builtin_amdgcn_rcpf(float(d)));
+    const int32_t r = int32_t(n - q * d);
+    q = r < 0 ? q - 1 : (uint32_t(r) >= d ? q + 1 : q);
+    return live ? max(1, int(q)) : 0;
+  };
   int lo = max(1, (total + a.nslot - 1) / a.nslot);
   int hi = max(lo, (total + a.nslot - a.batch - 1) / (a.nslot - a.batch));
   // equal lengths that divide evenly fit at the lower end: one count, no search

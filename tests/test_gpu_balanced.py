@@ -78,6 +78,23 @@ def test_sixty_four_requests():
     compare(out, oracle_out(w), what="64 requests balanced")
 
 
+
+def test_one_spare_slot():
+    """64 requests over 4 KV heads: 256 / 4 = 64 slots per head is below
+    batch + 1, so the call gets 65 slots, one more than the requests.  The
+    search for the partition size then spans from ceil(total / 65) up to
+    the whole page count."""
+    rng = np.random.default_rng(616)
+    ctx = [int(x) for x in rng.integers(2, 1500, size=64)]
+    ctx[5], ctx[40] = 6000, 4100
+    w = wl.small_case(seed=616, ctx=ctx, q_lens=[2] * 64, Hkv=4)
+    p = pa.pa_plan_describe(pa.make_config(w.Hkv, w.rows, w.B, w.W, partition_mode=BAL))
+    print("one spare slot", p, flush=True)
+    case = GpuCase(w)
+    out = case.decode(partition_mode=BAL)
+    torch.cuda.synchronize()
+    compare(out, oracle_out(w), what="64 requests x 4 KV heads balanced")
+
 def test_balanced_and_fixed_agree_and_repeat_bitwise():
     w = wl.small_case(seed=615, ctx=[6000, 130, 2500, 900], q_lens=[4, 4, 4, 4], Hkv=2)
     case = GpuCase(w)

@@ -647,8 +647,9 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     // Two-row workgroups run two waves per SIMD.  A wave raises its issue
     // priority while it issues its MFMA blocks, so the SIMD hands them to it
     // ahead of the other wave's softmax instructions and the matrix pipe
-    // runs under that wave's VALU work instead of after it.
-    if constexpr (RT == 2) __builtin_amdgcn_s_setprio(1);
+    // runs under that wave's VALU work instead of after it.  The QK block,
+    // which starts a chunk's dependency chain, goes first (2), then P.V (1).
+    if constexpr (RT == 2) __builtin_amdgcn_s_setprio(2);
     // S^T = K Q^T for every row tile, k-step outer so each converted K
     // operand (exact e4m3 -> bf16, or the bf16 itself) serves all row tiles
     f32x4 st[RT][2];

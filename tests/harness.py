@@ -141,9 +141,11 @@ def oracle_out(w, cache=None, rows_subset=None, sm_scale=None):
                               w.Hkv, sm_scale=sm_scale, rows_subset=rows_subset, kv_dtype=w.kv_dtype)
 
 
-def compact_request_oracle(w, b, rows):
-    """Oracle output for some rows of request b of a large workload, built on
-    a compact cache that holds only request b's written pages."""
+def compact_request_cache(w, b):
+    """The oracle's compact cache of request b of a large workload: its
+    written pages only, logical page n at compact page ``cpage[n]``.
+    Returns (kc, vc, ks, vs, ksa, vsa, bt) with ``bt`` the compact block
+    table [1, W] and ksa/vsa the scale arguments for the oracle's decode."""
     pages = [int(n) for n in w.written[b]]
     nb = len(pages)
     Hkv = w.Hkv
@@ -165,32 +167,86 @@ def compact_request_oracle(w, b, rows):
             owr.quant_write_ref(k, v, slots, kc, vc, ks_in, vs_in, w.mode, Hkv)
         else:
             owr.quant_write_ref(k, v, slots, kc, vc, ks, vs, w.mode, Hkv)
+    ksa, vsa = (ks_in, vs_in) if w.mode == wl.SCALAR else ((None, None) if w.mode == wl.NONE else (ks, vs))
+    return kc, vc, ks, vs, ksa, vsa, bt
+
+
+def compact_request_oracle(w, b, rows, cc=None):
+    """Oracle output for some rows of request b of a large workload, built on
+    a compact cache that holds only request b's written pages."""
+    kc, vc, ks, vs, ksa, vsa, bt = compact_request_cache(w, b) if cc is None else cc
     start = int(w.row_start[b])
     L = int(w.q_lens[b])
     q = w.q[start:start + L]
     cu = None if w.cu is None else np.array([0, L])
     sp = None if w.sparse is None else w.sparse[start:start + L]
-    ksa, vsa = (ks_in, vs_in) if w.mode == wl.SCALAR else ((None, None) if w.mode == wl.NONE else (ks, vs))
     sel = [r - start for r in rows]
-    return oatt.attention_ref(q, kc, vc, ksa, vsa, bt, w.ctx[b:b + 1], cu, sp, w.mode, Hkv,
+    return oatt.attention_ref(q, kc, vc, ksa, vsa, bt, w.ctx[b:b + 1], cu, sp, w.mode, w.Hkv,
                               rows_subset=sel, kv_dtype=w.kv_dtype)
 
 
+def assert_request_bytes(w, b, case, cc):
+    """The GPU cache's bytes of every written slot of request b's pages (and
+    their per-token scale bits) equal the oracle writer's, page by page.
+    Slots a page does not hold (the tail of the last page) are not the
+    writer's output and are skipped."""
+    assert w.kv_dtype == "fp8"
+    kc, vc, ks, vs, _, _, bt = cc
+    pages = [int(n) for n in w.written[b]]
+    phys = torch.as_tensor([int(w.block_table[b, n]) for n in pages], device=case.kc.device)
+    gk = case.kc.view(torch.uint8).index_select(0, phys).cpu().numpy()
+    gv = case.vc.view(torch.uint8).index_select(0, phys).cpu().numpy()
+    Hkv = w.Hkv
+    ok = np.reshape(kc, (-1, Hkv, 16384))
+    ov = np.reshape(vc, (-1, Hkv, 16384))
+    gks = gvs = None
+    if w.mode == wl.PER_TOKEN:
+        gks = case.ks.index_select(0, phys).cpu().numpy().view(np.uint32)
+        gvs = case.vs.index_select(0, phys).cpu().numpy().view(np.uint32)
+        oks = np.reshape(ks, (-1, Hkv, 128)).view(np.uint32)
+        ovs = np.reshape(vs, (-1, Hkv, 128)).view(np.uint32)
+    for i, n in enumerate(pages):
+        ci = int(bt[0, n])
+        cnt = int(min(128, int(w.ctx[b]) - 128 * n))
+        if cnt == 128:
+            kidx = vidx = slice(None)
+        else:
+            o = np.arange(cnt)[:, None]
+            d = np.arange(128)[None, :]
+            kidx = olay.k_offset(o, d).reshape(-1)
+            vidx = olay.v_offset(o, d).reshape(-1)
+        for h in range(Hkv):
+            assert np.array_equal(gk[i, h][kidx], ok[ci, h][kidx]), f"request {b} page {n} head {h}: K bytes"
+            assert np.array_equal(gv[i, h][vidx], ov[ci, h][vidx]), f"request {b} page {n} head {h}: V bytes"
+            if gks is not None:
+                assert np.array_equal(gks[i, h, :cnt], oks[ci, h, :cnt]), f"request {b} page {n}: K scales"
+                assert np.array_equal(gvs[i, h, :cnt], ovs[ci, h, :cnt]), f"request {b} page {n}: V scales"
+
+
 def compare(gpu_bf16, ref64, atol=1e-2, cos_min=0.9999, what=""):
+    """Element-wise parity of a bf16 output with the fp64 oracle: |err| <=
+    atol (1e-2) wherever |ref| < 4, and 2^-7 |ref| where |ref| >= 4 -- there
+    half a bf16 ulp alone is at least 2^-6 = 0.0156 > 1e-2, so no bf16 value
+    can meet the absolute bound; 2^-7 |ref| is one ulp at the bottom of the
+    binade.  Plus cosine >= cos_min over the whole tensor."""
     g = gpu_bf16.float().cpu().numpy().astype(np.float64) if torch.is_tensor(gpu_bf16) else gpu_bf16
     r = np.asarray(ref64, dtype=np.float64)
     assert g.shape == r.shape, (g.shape, r.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
     err = np.abs(g - r)
     maxerr = float(err.max()) if err.size else 0.0
-    # bf16 output: for |out| >= 4 half an ulp alone exceeds 1e-2, so there
-    # the bound is relative (2^-7 |ref|); below |out| = 1.28 it is 1e-2.
-    tol = np.maximum(atol, 2.0 ** -7 * np.abs(r))
+    mag = np.abs(r)
+    relaxed = mag >= 4.0
+    tol = np.where(relaxed, 2.0 ** -7 * mag, atol)
     worst = float((err / tol).max()) if err.size else 0.0
     num = float(np.sum(g * r))
     den = math.sqrt(float(np.sum(g * g)) * float(np.sum(r * r)))
     cos = num / den if den > 0 else (1.0 if float(np.abs(g).max(initial=0)) == 0 else 0.0)
-    assert worst <= 1.0, (f"{what}: max|err| {maxerr:.3e} exceeds max({atol}, 2^-7|ref|) "
-                          f"(max|ref| {np.abs(r).max():.3e}, worst err/tol {worst:.3f})")
+    maxref = float(mag.max()) if mag.size else 0.0
+    abs_err = float(err[~relaxed].max()) if np.any(~relaxed) else 0.0
+    assert worst <= 1.0, (f"{what}: max|err| {maxerr:.3e} (where |ref| < 4: {abs_err:.3e}) exceeds the "
+                          f"bound ({atol} for |ref| < 4, 2^-7|ref| above; max|ref| {maxref:.3e}, "
+                          f"{int(relaxed.sum())} of {r.size} elements at |ref| >= 4, worst err/tol "
+                          f"{worst:.3f})")
     assert cos >= cos_min, f"{what}: cosine {cos:.7f} < {cos_min}"
     return maxerr, cos

@@ -181,3 +181,44 @@ def test_writer_random_calls_bit_exact(seed):
     if mode == wl.PER_TOKEN:
         assert np.array_equal(ks_g.cpu().numpy().reshape(-1).view(np.uint32), ks.view(np.uint32))
         assert np.array_equal(vs_g.cpu().numpy().reshape(-1).view(np.uint32), vs.view(np.uint32))
+
+
+def test_writer_quotient_is_a_division():
+    """The rows of the oracle's division pins (x on an e4m3 midpoint of
+    x / scale, where a reciprocal multiply would round the other way),
+    through the GPU writer: codes and scales equal the exact-rational ones."""
+    from fractions import Fraction
+
+    from exact_rational import quantize_exact
+    from test_oracle_writer import DIVISION_CASES
+    dev = torch.device("cuda:0")
+    T = len(DIVISION_CASES)
+    k = np.zeros((T, 1, 128), np.float32)
+    want = []
+    for t, (m, e, mid) in enumerate(DIVISION_CASES):
+        s = Fraction(m, 512) * Fraction(2) ** e
+        k[t, 0, 0], k[t, 0, 1], k[t, 0, 2] = float(448 * s), float(mid * s), -float(mid * s)
+        want.append((s, quantize_exact(mid * s, 448 * s)[1]))
+    slots = np.arange(T, dtype=np.int64) * 7
+    kc_g = torch.zeros(1, 1, 16384, dtype=torch.uint8, device=dev)
+    vc_g = torch.zeros_like(kc_g)
+    ks_g = torch.zeros(1, 1, 128, dtype=torch.float32, device=dev)
+    vs_g = torch.zeros_like(ks_g)
+    kt = torch.from_numpy(k).to(dev)
+    pa.kv_quant_write(kt, kt, torch.from_numpy(slots).to(dev), kc_g, vc_g, ks_g, vs_g, wl.PER_TOKEN)
+    torch.cuda.synchronize()
+    kc = np.zeros(16384, np.uint8)
+    vc = kc.copy()
+    ks = np.zeros(128, np.float32)
+    vs = ks.copy()
+    owr.quant_write_ref(k, k, slots, kc, vc, ks, vs, wl.PER_TOKEN, 1)
+    assert np.array_equal(kc_g.cpu().numpy().reshape(-1), kc)
+    assert np.array_equal(ks_g.cpu().numpy().reshape(-1).view(np.uint32), ks.view(np.uint32))
+    from oracle import layout as olay
+    got = kc_g.cpu().numpy().reshape(-1)
+    gs = ks_g.cpu().numpy().reshape(-1)
+    for t, (s, code) in enumerate(want):
+        o = int(slots[t])
+        codes = got[olay.k_offset(o, np.arange(128))]
+        assert Fraction(float(gs[o])) == s
+        assert codes[1] == code and codes[2] == (code | 0x80), (t, codes[:3], code)

@@ -110,3 +110,73 @@ def test_scalar_and_none_modes():
     for t in range(8):
         codes = _read_back(vc, 0, 0, int(slots[t]), 1, "v")
         assert np.array_equal(codes, e4m3.encode_bruteforce(v[t, 0]))
+
+
+# ---------------------------------------------------------------------------
+# The per-token quotient is one IEEE fp32 division, not a multiply by a
+# rounded reciprocal.  Each case below puts x exactly on an e4m3 rounding
+# midpoint of x / scale, with scale = amax / 448 exact in fp32 and not a
+# power of two, so the division lands on the tie (rounded to even) while
+# x * fl32(1 / scale) lands one fp32 ulp to the odd side.  The expected codes
+# come from exact rational arithmetic (tests/exact_rational.py); the cases
+# were found by a search over 10-bit scale significands.
+from fractions import Fraction  # noqa: E402
+
+from exact_rational import e4m3_code, quantize_by_reciprocal, quantize_exact, round_f32  # noqa: E402
+
+# (scale significand / 512, power of two, midpoint of x / scale)
+DIVISION_CASES = [
+    (943, -1, Fraction(21, 16)),   # 1.3125: tie -> 1.25 (0x3A); reciprocal lands above -> 0x3B
+    (881, -7, Fraction(21, 16)),
+    (933, -10, Fraction(23, 16)),  # 1.4375: tie -> 1.5 (0x3C); reciprocal lands below -> 0x3B
+    (948, -9, Fraction(23, 16)),
+    (874, -5, Fraction(27, 8)),    # 3.375: tie -> 3.5 (0x46); reciprocal lands below -> 0x45
+]
+
+
+def test_exact_rational_helpers():
+    """The exact models agree with hand-worked values and with torch's own
+    float32 / float8_e4m3fn conversions."""
+    import torch
+    F = Fraction
+    assert e4m3_code(F(17, 16)) == 0x38 and e4m3_code(F(19, 16)) == 0x3A
+    assert e4m3_code(F(1, 1024)) == 0x00 and e4m3_code(F(3, 1024)) == 0x02
+    assert e4m3_code(F(448)) == 0x7E and e4m3_code(F(470)) == 0x7E and e4m3_code(F(-1, 512)) == 0x81
+    assert round_f32(F(1, 3)) == F(11184811, 2 ** 25)
+    assert round_f32(F(2 ** 24 + 1)) == F(2 ** 24)          # tie to even
+    assert round_f32(F(2 ** 24 + 3)) == F(2 ** 24 + 4)
+    rng = np.random.default_rng(11)
+    vals = np.concatenate([rng.standard_normal(400) * 50, rng.standard_normal(100) * 0.01])
+    f32 = vals.astype(np.float32)
+    for v, r in zip(vals.tolist(), f32.tolist()):
+        assert round_f32(F(v)) == F(r)
+    ref = torch.from_numpy(np.clip(f32, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for v, c in zip(f32.tolist(), ref.tolist()):
+        assert e4m3_code(F(v)) == c, v
+
+
+@pytest.mark.parametrize("m,e,mid", DIVISION_CASES)
+def test_per_token_quotient_is_a_division(m, e, mid):
+    s = Fraction(m, 512) * Fraction(2) ** e
+    amax, x = 448 * s, mid * s
+    # every input is an fp32 value, and amax / 448 is exactly s
+    assert round_f32(amax) == amax and round_f32(x) == x
+    s_div, want = quantize_exact(x, amax)
+    s_rec, other = quantize_by_reciprocal(x, amax)
+    assert s_div == s == s_rec
+    assert want != other, "case does not tell division from reciprocal"
+    row = np.zeros((1, 1, 128), dtype=np.float32)
+    row[0, 0, 0] = float(amax)
+    row[0, 0, 1] = float(x)
+    row[0, 0, 2] = -float(x)
+    row[0, 0, 3] = -float(amax)
+    codes, scale = writer.quantize_rows(row, PT)
+    assert Fraction(float(scale[0, 0])) == s
+    assert codes[0, 0, 1] == want and codes[0, 0, 2] == (want | 0x80)
+    assert codes[0, 0, 0] == 0x7E and codes[0, 0, 3] == 0xFE
+    # and through the whole writer (layout and scale store)
+    kc, vc, ks, vs = _fresh(1, 1)
+    writer.quant_write_ref(row, row, np.array([77]), kc, vc, ks, vs, PT, 1)
+    got = _read_back(kc, 0, 0, 77, 1, "k")
+    assert got[1] == want and got[2] == (want | 0x80)
+    assert Fraction(float(ks[layout.scale_index(0, 0, 77, 1)])) == s

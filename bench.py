@@ -3,19 +3,23 @@
 A step is one pass of the hot path over one batch: kv_quant_write of the
 step's new tokens (the last q_len tokens of every request), then pa_decode
 (main kernel, plus the log-sum-exp merge when the plan splits the context).
-The default workload is the 8K serving shape: batch 4, q_len 1, one KV head x
-16 query heads, head_dim 128, 128-token pages, contexts uniform in
-[8192, 9216], per-token e4m3 scales, random block table over a 4096-page
-pool.  Its cache is replicated over 64 layers (64 distinct cache tensors
-sharing one block table) and steps rotate through them, as consecutive
-attention layers of one model would, so
-every step reads its KV from HBM rather than from the 256 MB Infinity Cache.
+The default workload is the long-context shape: batch 32, q_len 1, one KV
+head x 16 query heads, head_dim 128, 128-token pages, context 131072 each
+(1024 pages per request), per-token e4m3 scales, block tables drawn from a
+32768-page pool -- 1.1 GB of KV per step, so every step reads it from HBM.
+Smaller shapes (--config c2: batch 4 at 8K contexts, ...) replicate their
+cache over up to 64 layers (distinct cache tensors sharing one block table)
+and steps rotate through them, as consecutive attention layers of one model
+would, so every step reads its KV from HBM rather than from the 256 MB
+Infinity Cache.
 
 Timing: W untimed warmup steps, then exactly K steps replayed from captured
 HIP graphs, bracketed by torch.cuda.synchronize().  The main decode kernel's
 own duration is measured with HIP events recorded around it on the launch
 stream.  One cold launch (idle GPU, caches evicted first) is reported beside
-the steady state.  Prints one JSON line.
+the steady state.  The CPU oracle is then timed on the host's cores (one
+single-threaded process per core, at most 16) over requests of the same
+workload, and checks the GPU's output on them.  Prints one JSON line.
 """
 
 import argparse
@@ -276,32 +280,48 @@ def hbm_probe(dev, gib=4, same_bytes=None):
     return round(best, 1), best_small
 
 
-def cpu_baseline(w, layers, budget_s=12.0, index_topk=0):
-    """The oracle, as it stands, on one core: the same step -- write the
-    step's new tokens of a request, (with the indexer: score every visible
-    page and take the top-k,) then attend that request's rows over its
-    cache -- for requests of the workload, repeated until about `budget_s`
-    seconds of CPU work.  The oracle's cache for a request is prepared
-    untimed (it is state, as the GPU cache is).  The GPU's layer-0 output for
-    the same rows is checked against the oracle's (and, with the indexer,
-    the GPU's page lists against the oracle's)."""
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_workers():
+    """Worker processes for the oracle leg: the CPUs this process may run
+    on, at most 16 (one GPU's share of a shared 8-GPU host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _oracle_worker(w, reqs, index_topk, budget_s, go, barrier, results, wid):
+    """One worker of the oracle leg, in a process forked before the parent
+    touched the GPU: build the oracle's cache of each of its requests
+    (untimed: it is state, as the GPU cache is), wait until every worker is
+    ready, then repeat request-steps -- write the request's new tokens,
+    (with the indexer: score its visible pages and take the top-k,) attend
+    its rows over its cache -- until about `budget_s` seconds of work.
+    Single-threaded numpy (BLAS limited to one thread)."""
     try:
         from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:  # pragma: no cover
-        threadpool_limits = None
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from harness import compare
+        pass
     from oracle import attention as oatt
     from oracle import indexer as oidx
     from oracle import writer as owr
-
-    lim = threadpool_limits(1) if threadpool_limits else None
     try:
-        out0 = layers.out[0].float().cpu().numpy()
+        go.wait()
         sk, sv, _ = w.step_tokens()
         sc_k = np.array([w.k_scalar], np.float32)
         sc_v = np.array([w.v_scalar], np.float32)
-
         bf = w.kv_dtype == "bf16"
 
         def write(k, v, slots, kc, vc, ka, va):
@@ -311,7 +331,6 @@ def cpu_baseline(w, layers, budget_s=12.0, index_topk=0):
                 owr.quant_write_ref(k, v, slots, kc, vc, ka, va, w.mode, w.Hkv)
 
         def request_state(b):
-            """untimed: the oracle's compact cache of request b (state, like the GPU cache)"""
             pages = [int(x) for x in w.written[b]]
             nb = len(pages) + 1
             kc = np.zeros(nb * w.Hkv * 16384, np.uint16 if bf else np.uint8)
@@ -324,7 +343,7 @@ def cpu_baseline(w, layers, budget_s=12.0, index_topk=0):
                 bt[0, pg] = ci
                 k, v = w.page_kv(b, pg)
                 write(k, v, ci * 128 + np.arange(k.shape[0], dtype=np.int64), kc, vc, ka, va)
-            start, L = int(w.row_start[b]), int(w.q_lens[b])
+            L = int(w.q_lens[b])
             c = int(w.ctx[b])
             new_slots = np.array([bt[0, (c - L + i) // 128] * 128 + (c - L + i) % 128 for i in range(L)],
                                  dtype=np.int64)
@@ -334,12 +353,10 @@ def cpu_baseline(w, layers, budget_s=12.0, index_topk=0):
                 icache = w.index_cache(poison=False, num_blocks=nb, page_map=pm)
             return kc, vc, ka, va, bt, new_slots, icache
 
-        reqs = list(range(min(w.B, 2 if index_topk else 4)))
         state = {b: request_state(b) for b in reqs}
         q_idx = w.index_queries() if index_topk else None
-        gpu_lists = layers.lists[0].cpu().numpy() if index_topk else None
-        lists_equal = True
-        done_bytes, t_used, n, check = 0, 0.0, 0, None
+        barrier.wait()
+        done_bytes, t_used, n, checks = 0, 0.0, 0, []
         while (t_used < budget_s and n < 4096) or n < len(reqs):
             b = reqs[n % len(reqs)]
             kc, vc, ka, va, bt, new_slots, icache = state[b]
@@ -347,47 +364,117 @@ def cpu_baseline(w, layers, budget_s=12.0, index_topk=0):
             rows = list(range(start, start + L))
             sp = None if w.sparse is None else w.sparse[start:start + L]
             cu = None if w.cu is None else np.array([0, L])
-            # timed: the step on the CPU (write the new tokens, [index,] attend the rows)
-            t0 = time.time()
+            t0 = time.perf_counter()
             write(sk[start:start + L], sv[start:start + L], new_slots, kc, vc, ka, va)
             if index_topk:
                 sc = oidx.block_scores_ref(q_idx[start:start + L], icache, bt, w.ctx[b:b + 1], cu)
                 sp = oidx.topk_ref(sc, index_topk)
             ref = oatt.attention_ref(w.q[start:start + L], kc, vc, ka, va, bt, w.ctx[b:b + 1], cu, sp,
                                      w.mode, w.Hkv, kv_dtype=w.kv_dtype)
-            t_used += time.time() - t0
-            if index_topk and n < len(reqs):
-                lists_equal &= bool(np.array_equal(sp, gpu_lists[start:start + L]))
-            if n < len(reqs) and (not index_topk or np.array_equal(sp, gpu_lists[start:start + L])):
-                err, cos = compare(out0[rows], ref, what=f"bench check request {b}")
-                check = (err, cos) if check is None else (max(err, check[0]), min(cos, check[1]))
-            if w.sparse is None:
+            t_used += time.perf_counter() - t0
+            if n < len(reqs):
+                checks.append((b, rows, ref, sp))
+            if w.sparse is None and not index_topk:
                 toks = min(int(w.ctx[b]), w.W * 128)
             else:
-                sel = {int(x) for r in rows for x in w.sparse[r] if 0 <= x < w.W}
+                sel = {int(x) for r in range(L) for x in sp[r] if 0 <= x < w.W}
                 toks = sum(min(128, int(w.ctx[b]) - 128 * x) for x in sel)
             done_bytes += toks * w.Hkv * (512 if bf else 256 + (8 if w.mode == wl.PER_TOKEN else 0))
             if index_topk:
                 done_bytes += min((int(w.ctx[b]) + 127) // 128, w.W) * 128 * 128
             n += 1
-    finally:
-        if lim is not None:
-            lim.__exit__(None, None, None)
-    return {
-        "value": round(done_bytes / t_used / 1e9, 5),
-        "unit": "GB/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"{n} request-steps over the first {len(reqs)} requests of {w.name} (write the "
-                  f"request's new tokens, "
-                  + (f"score its visible pages on the index cache and take the top-{index_topk}, "
-                     if index_topk else "")
-                  + f"decode its attended pages, fp64 softmax attention for its rows), one host thread, "
-                  f"{t_used:.1f} s timed",
-        "check_max_abs_err": None if check is None else round(check[0], 6),
-        **({"check_index_lists_equal": lists_equal} if index_topk else {}),
-        "check_min_cos": None if check is None else round(check[1], 8),
-    }
+        results.put((wid, done_bytes, t_used, n, checks, None))
+    except BaseException as e:  # report, never hang the parent
+        import traceback
+        results.put((wid, 0, 0.0, 0, [], traceback.format_exc() + repr(e)))
+
+
+class OracleLeg:
+    """The oracle timed on the host's cores: one single-threaded worker
+    process per core (at most 16), forked before the parent initialises the
+    GPU, each holding one or more requests of the workload.  `run()` releases
+    them once the GPU measurement is done."""
+
+    def __init__(self, w, index_topk=0, budget_s=12.0):
+        import multiprocessing as mp
+        ctx = mp.get_context("fork")
+        self.w, self.index_topk, self.budget_s = w, index_topk, budget_s
+        self.n = cpu_workers()
+        self.go = ctx.Event()
+        self.barrier = ctx.Barrier(self.n)
+        self.results = ctx.Queue()
+        nreq = min(w.B, self.n)
+        self.reqs = [[i % nreq] for i in range(self.n)]
+        self.procs = [ctx.Process(target=_oracle_worker, daemon=True,
+                                  args=(w, self.reqs[i], index_topk, budget_s, self.go, self.barrier,
+                                        self.results, i))
+                      for i in range(self.n)]
+        for p in self.procs:
+            p.start()
+
+    def stop(self):
+        for p in self.procs:
+            if p.is_alive():
+                p.kill()
+
+    def run(self, layers):
+        """Release the workers, collect their request-steps, check the GPU's
+        layer-0 output (and, with the indexer, its page lists) on the rows
+        the oracle computed, and return the cpu_baseline record."""
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from harness import compare
+        w, index_topk = self.w, self.index_topk
+        out0 = layers.out[0].float().cpu().numpy()
+        gpu_lists = layers.lists[0].cpu().numpy() if index_topk else None
+        t0 = time.perf_counter()
+        self.go.set()
+        got = []
+        for _ in range(self.n):
+            got.append(self.results.get(timeout=600))
+        wall = time.perf_counter() - t0
+        for p in self.procs:
+            p.join(timeout=30)
+        errs = [r[5] for r in got if r[5]]
+        if errs:
+            raise RuntimeError("oracle worker failed:\n" + errs[0])
+        done_bytes = sum(r[1] for r in got)
+        t_max = max(r[2] for r in got)
+        steps = sum(r[3] for r in got)
+        check, lists_equal, checked = None, True, set()
+        for r in got:
+            for b, rows, ref, sp in r[4]:
+                if b in checked:
+                    continue
+                checked.add(b)
+                if index_topk:
+                    same = bool(np.array_equal(sp, gpu_lists[rows[0]:rows[-1] + 1]))
+                    lists_equal &= same
+                    if not same:
+                        continue
+                err, cos = compare(out0[rows], ref, what=f"bench check request {b}")
+                check = (err, cos) if check is None else (max(err, check[0]), min(cos, check[1]))
+        nreq = len({b for r in self.reqs for b in r})
+        return {
+            "value": round(done_bytes / t_max / 1e9, 5),
+            "unit": "GB/s",
+            "cores": self.n,
+            "kind": "oracle",
+            "sample": f"{steps} request-steps over the first {nreq} requests of {w.name} on {self.n} "
+                      f"single-threaded worker processes running together (each: write the request's new "
+                      f"tokens, "
+                      + (f"score its visible pages on the index cache and take the top-{index_topk}, "
+                         if index_topk else "")
+                      + f"decode its attended pages, fp64 softmax attention for its rows), about "
+                      f"{self.budget_s:.0f} s of work each; value = KV bytes of all steps / the longest "
+                      f"worker's timed seconds ({t_max:.1f} s)",
+            "cpu_model": cpu_model(),
+            "host_cpus_visible": os.cpu_count(),
+            "wall_s": round(wall, 1),
+            "check_max_abs_err": None if check is None else round(check[0], 6),
+            **({"check_index_lists_equal": lists_equal} if index_topk else {}),
+            "check_min_cos": None if check is None else round(check[1], 8),
+            "check_requests": sorted(checked),
+        }
 
 
 def main():
@@ -395,7 +482,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3200)
     ap.add_argument("--warmup", type=int, default=128)
-    ap.add_argument("--config", default="c2", choices=sorted(CONFIGS))
+    ap.add_argument("--config", default="c3", choices=sorted(CONFIGS))
     ap.add_argument("--layers", type=int, default=0, help="distinct cache copies to rotate (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--force-parts", type=int, default=0, help="split-K partitions (0: the plan's choice)")
@@ -413,10 +500,6 @@ def main():
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the library has no "
               f"multi-GPU path; the decode kernel's per-GPU share is what one GPU shows).", file=sys.stderr)
         sys.exit(2)
-    assert torch.cuda.is_available(), "bench needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
     w = CONFIGS[args.config]()
     index_topk = INDEX_TOPK.get(args.config, 0)
     idx_bytes = index_bytes(w, index_topk) if index_topk else 0
@@ -428,6 +511,13 @@ def main():
     n_layers = args.layers or max(1, min(64, int(math.ceil(1.0e9 / max(kv_bytes + idx_bytes, 1)))))
     if index_topk:
         w.sparse = None
+    # the oracle's workers are forked now, before this process touches the
+    # GPU; they wait until the GPU measurement is over
+    leg = None if args.no_cpu_baseline else OracleLeg(w, index_topk)
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
     layers = Layers(w, n_layers, dev, index_topk)
 
     stream = torch.cuda.Stream()
@@ -538,7 +628,11 @@ def main():
         torch.cuda.synchronize()
 
     probe, probe_same = hbm_probe(dev, same_bytes=idx_bytes if index_topk else alg_bytes) or (None, None)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, layers, index_topk=index_topk)
+    try:
+        cpu = None if leg is None else leg.run(layers)
+    finally:
+        if leg is not None:
+            leg.stop()
 
     res = {
         "metric": "decode attention KV GB/s & % HBM roofline (attended tokens/s), 1 MI355X",

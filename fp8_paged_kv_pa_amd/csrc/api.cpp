@@ -8,6 +8,8 @@
 // (device, stream), sized by capacity bucket and grown only outside graph
 // capture (ROCm/ATOM pull request 2710 review, "Must fix" 1: bounded plan
 // and scratch shapes, allocated where the memory accounting can see them).
+// A replaced arena stays allocated until pa_release, since a graph captured
+// with it keeps its address.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -17,6 +19,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "../../include/fp8pa.h"
 #include "check.h"
@@ -112,6 +115,11 @@ struct Arena {
 };
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Arena> g_arenas;
+// Arenas replaced by a larger one.  A graph captured while one of them was
+// current still holds its address in its kernel arguments, so they stay
+// allocated until pa_release.  Each growth at least doubles the arena, so
+// the retired ones of a (device, stream) add up to less than the current.
+std::vector<std::pair<int, void*>> g_retired;
 
 int get_scratch(hipStream_t stream, size_t need_counters, size_t need_partials, uint32_t** counters,
                 void** partials) {
@@ -137,24 +145,18 @@ int get_scratch(hipStream_t stream, size_t need_counters, size_t need_partials, 
                     " bytes while the stream is being captured; call pa_reserve before capture");
   size_t sz = 1;
   while (sz < need) sz <<= 1;
-  if (ar.ptr) {
-    // kernels still queued on this stream may use the old arena
-    if (hipStreamSynchronize(stream) != hipSuccess) return fail(PA_ERR_HIP, "hipStreamSynchronize failed");
-    hipFree(ar.ptr);
-    ar.ptr = nullptr;
-    ar.bytes = 0;
-    ar.counter_bytes = 0;
-  }
-  if (hipMalloc(&ar.ptr, sz) != hipSuccess) {
-    ar.ptr = nullptr;
+  void* fresh = nullptr;
+  if (hipMalloc(&fresh, sz) != hipSuccess)
     return fail(PA_ERR_HIP, "hipMalloc of " + std::to_string(sz) + " bytes of split-K scratch failed");
-  }
   // counters must start at zero (never reached under capture: growth is refused there)
-  if (hipMemsetAsync(ar.ptr, 0, cnt, stream) != hipSuccess) {
-    hipFree(ar.ptr);
-    ar.ptr = nullptr;
+  if (hipMemsetAsync(fresh, 0, cnt, stream) != hipSuccess) {
+    hipFree(fresh);
     return fail(PA_ERR_HIP, "clearing the split-K counters failed");
   }
+  // The old arena is retired, not freed: work queued on the stream and any
+  // graph captured with it may still use it (see g_retired).
+  if (ar.ptr) g_retired.emplace_back(dev, ar.ptr);
+  ar.ptr = fresh;
   ar.bytes = sz;
   ar.counter_bytes = cnt;
   *counters = static_cast<uint32_t*>(ar.ptr);
@@ -562,17 +564,20 @@ int pa_reserve(const pa_config* cfg, void* stream) {
 int pa_release(void) {
   g_err.clear();
   std::lock_guard<std::mutex> lk(g_mu);
-  if (g_arenas.empty()) return PA_OK;
+  if (g_arenas.empty() && g_retired.empty()) return PA_OK;
   int cur = 0;
   hipGetDevice(&cur);
   int rc = PA_OK;
-  for (auto& kv : g_arenas) {
-    if (!kv.second.ptr) continue;
-    hipSetDevice(kv.first.first);
+  std::vector<std::pair<int, void*>> all = g_retired;
+  for (auto& kv : g_arenas)
+    if (kv.second.ptr) all.emplace_back(kv.first.first, kv.second.ptr);
+  for (auto& dp : all) {
+    hipSetDevice(dp.first);
     if (hipDeviceSynchronize() != hipSuccess) rc = fail(PA_ERR_HIP, "hipDeviceSynchronize failed");
-    hipFree(kv.second.ptr);
+    hipFree(dp.second);
   }
   g_arenas.clear();
+  g_retired.clear();
   hipSetDevice(cur);
   return rc;
 }

@@ -244,9 +244,8 @@ constexpr int kMinBlocks = (NBUF2_NW4 && !(BF && RT == 2)) ? 2 : 1;
 constexpr int kMaxMergeParts = 256;
 
 // Partials of the in-kernel merge travel through device-scope (relaxed
-// atomic) 64-bit stores and loads: they are coherent across the XCDs'
-// L2s by themselves, so publishing a partial needs only its stores to be
-// complete -- no L2 writeback or invalidate.
+// atomic) 64-bit stores and loads, which are coherent across the XCDs' L2s;
+// the arrival count orders them (acquire-release, see merge_if_last).
 __device__ __forceinline__ void store_coherent(float* p, float x, float y) {
   const uint64_t v = uint64_t(__float_as_uint(x)) | (uint64_t(__float_as_uint(y)) << 32);
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -265,11 +264,15 @@ __device__ void merge_if_last(const DecodeArgs& a, int64_t unit, int row0, int n
   __shared__ int sm_last;
   // Each wave waits for its coherent partial stores to complete, the
   // barrier makes that true for the whole workgroup, and only then does
-  // thread 0 count the partition in.
+  // thread 0 count the partition in.  The count is an acquire-release
+  // read-modify-write at device scope: it publishes this workgroup's
+  // partials (release) and, for the workgroup that sees the last arrival,
+  // orders every other partition's published partials before its reads
+  // (acquire); the barrier after it carries that order to the other waves.
   wait_stores();
   __syncthreads();
   if (threadIdx.x == 0)
-    sm_last = __hip_atomic_fetch_add(a.unit_count + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+    sm_last = __hip_atomic_fetch_add(a.unit_count + unit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
               uint32_t(a.parts - 1);
   __syncthreads();
   if (!sm_last) return;

@@ -122,9 +122,10 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
     // by the bucket so one reservation serves the whole bucket; in front of
     // them one arrival counter per unit for the in-kernel merge.
     const int64_t per = 2 + kDim;
-    // The separate merge kernel is the default: measured on MI355X, the
-    // device-scope fences of the in-kernel merge (each a writeback and
-    // invalidate of the XCD's L2) cost more than the extra launch.
+    // The separate merge kernel is the default: measured on MI355X, merging
+    // inside the main kernel makes the last partition of each unit a serial
+    // tail that pulls every partial through device-coherent loads, which
+    // costs more than the extra launch.
     p.fused_merge = c.merge_mode == PA_MERGE_IN_KERNEL;
     p.counter_bytes = (p.units_bucket * 4 + 255) / 256 * 256;
     p.scratch_bytes = p.counter_bytes +

@@ -101,9 +101,10 @@ typedef enum pa_scale_mode {
  * either place). */
 typedef enum pa_merge_mode {
   PA_MERGE_PLAN = 0,       /* the library's choice: the separate kernel       */
-                           /* (measured faster on MI355X: the in-kernel merge */
-                           /* needs device-scope fences, each an L2 writeback */
-                           /* and invalidate on the XCD)                      */
+                           /* (measured faster on MI355X: in the main kernel  */
+                           /* the merge becomes a serial tail in which one    */
+                           /* workgroup per unit pulls every partial through  */
+                           /* device-coherent loads)                          */
   PA_MERGE_SEPARATE = 1,   /* a separate merge kernel after the main kernel   */
   PA_MERGE_IN_KERNEL = 2   /* the last partition of each unit to finish      */
                            /* merges all of them inside the main kernel       */
@@ -372,14 +373,20 @@ int pa_plan_describe(const pa_config* cfg, pa_plan_info* info);
  * smaller bucket) needs on the current device for calls on `stream`, so
  * later calls (including ones under graph capture) never allocate.  Scratch
  * is per (device, stream): calls on one stream are serialised by the
- * stream; calls on different streams use different scratch.  A captured
- * graph keeps the scratch it was captured with; do not replay two copies of
- * one graph concurrently.  The scratch starts with one arrival counter per
- * unit for the in-kernel merge: zeroed when the scratch is allocated, and
- * put back to zero by every call that uses it. */
+ * stream; calls on different streams use different scratch.  A call outside
+ * capture that needs a larger bucket than the stream's scratch replaces it
+ * with a larger one; the replaced scratch is not freed but kept until
+ * pa_release, so a graph captured with it can still be replayed (it keeps
+ * the scratch it was captured with).  A call under capture that needs more
+ * than is reserved returns PA_ERR_NOT_RESERVED and records nothing.  Do not
+ * replay two copies of one graph concurrently.  The scratch starts with one
+ * arrival counter per unit for the in-kernel merge: zeroed when the scratch
+ * is allocated, and put back to zero by every call that uses it. */
 int pa_reserve(const pa_config* cfg, void* stream);
 
-/* pa_release -- free all scratch (synchronises the device first). */
+/* pa_release -- free all scratch, current and replaced (synchronises each
+ * device first).  Graphs captured before pa_release use freed scratch and
+ * must not be replayed after it; capture them again. */
 int pa_release(void);
 
 /* Text of the last error on the calling thread ("" if none). */

@@ -1,5 +1,7 @@
 """The five workloads at full size, in the launch configuration the bench
-times: the cache is written by kv_quant_write; sampled rows are checked
+times: the cache is written by kv_quant_write, and the sampled requests'
+pages are compared with the oracle writer's byte for byte (codes and scale
+bits); sampled rows are checked
 element by element against the oracle (rebuilt on a compact cache of just
 those requests' pages); every row is checked against properties that hold
 at any size (finite, the default plan agrees with forced partition counts
@@ -12,7 +14,7 @@ import torch
 import fp8_paged_kv_pa_amd as pa
 import workloads as wl
 
-from harness import GpuCase, compact_request_oracle, compare
+from harness import GpuCase, assert_request_bytes, compact_request_cache, compact_request_oracle, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +28,10 @@ def _check(w, case, sample_requests, what):
         start = int(w.row_start[b])
         rows = list(range(start, start + int(w.q_lens[b])))
         print(what, "request", b, "rows", rows, flush=True)
-        ref = compact_request_oracle(w, b, rows)
+        cc = compact_request_cache(w, b)
+        # the cache kv_quant_write wrote for this request: every byte and scale
+        assert_request_bytes(w, b, case, cc)
+        ref = compact_request_oracle(w, b, rows, cc)
         compare(g[rows], ref, what=f"{what} request {b}")
     return out.clone()
 

@@ -34,13 +34,8 @@ def pa_decode(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
     return out
 
 
-def pa_decode_ex(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
-                 cu_seqlens_q, sparse_page_idx, scale_mode, out, sm_scale=0.0, max_q_len=0,
-                 force_parts=0, main_begin_event=None, main_end_event=None, prefetch_depth=0,
-                 workgroup_waves=0, merge_mode=0, partition_mode=0, stream=None):
-    """``pa_decode`` with options; events are torch.cuda.Event objects that
-    have been recorded once (so they exist)."""
-    lib = load()
+def _decode_opts(sm_scale, max_q_len, force_parts, main_begin_event, main_end_event, prefetch_depth,
+                 workgroup_waves, merge_mode, partition_mode):
     opts = PaDecodeOpts()
     opts.sm_scale = float(sm_scale)
     opts.max_q_len = int(max_q_len)
@@ -51,11 +46,41 @@ def pa_decode_ex(q, k_cache, v_cache, k_scale, v_scale, block_table, context_len
     opts.partition_mode = int(partition_mode)
     opts.main_begin_event = main_begin_event.cuda_event if main_begin_event is not None else None
     opts.main_end_event = main_end_event.cuda_event if main_end_event is not None else None
+    return opts
+
+
+def pa_decode_ex(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                 cu_seqlens_q, sparse_page_idx, scale_mode, out, sm_scale=0.0, max_q_len=0,
+                 force_parts=0, main_begin_event=None, main_end_event=None, prefetch_depth=0,
+                 workgroup_waves=0, merge_mode=0, partition_mode=0, stream=None):
+    """``pa_decode`` with options; events are torch.cuda.Event objects that
+    have been recorded once (so they exist)."""
+    lib = load()
+    opts = _decode_opts(sm_scale, max_q_len, force_parts, main_begin_event, main_end_event, prefetch_depth,
+                        workgroup_waves, merge_mode, partition_mode)
     d = [desc(t) for t in (q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
                            cu_seqlens_q, sparse_page_idx)]
     do = desc(out)
     check(lib.pa_decode_ex(*[ref(x) for x in d], int(scale_mode), ref(do), ctypes.byref(opts),
                            stream_handle(stream)))
+    return out
+
+
+def pa_decode_noalloc(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                      cu_seqlens_q, sparse_page_idx, scale_mode, out, sm_scale=0.0, max_q_len=0,
+                      force_parts=0, main_begin_event=None, main_end_event=None, prefetch_depth=0,
+                      workgroup_waves=0, merge_mode=0, partition_mode=0, stream=None):
+    """``pa_decode_ex`` on the library's fixed scratch array: allocates
+    nothing (see ``pa_decode_noalloc`` in include/fp8pa.h for its limit and
+    why calls on one device must not overlap)."""
+    lib = load()
+    opts = _decode_opts(sm_scale, max_q_len, force_parts, main_begin_event, main_end_event, prefetch_depth,
+                        workgroup_waves, merge_mode, partition_mode)
+    d = [desc(t) for t in (q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                           cu_seqlens_q, sparse_page_idx)]
+    do = desc(out)
+    check(lib.pa_decode_noalloc(*[ref(x) for x in d], int(scale_mode), ref(do), ctypes.byref(opts),
+                                stream_handle(stream)))
     return out
 
 

@@ -165,10 +165,17 @@ int get_scratch(hipStream_t stream, size_t need_counters, size_t need_partials, 
 }
 
 // ---------------------------------------------------------------------------
+// Fixed split-K scratch of pa_decode_noalloc (see `scratch` below): its
+// device address on each device, looked up once per device with that
+// device current.  In host code the array's name only stands for the
+// symbol; kernels must be given this address.
+int fixed_scratch(void** out);
+
+// ---------------------------------------------------------------------------
 int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const pa_tensor* ks,
                 const pa_tensor* vs, const pa_tensor* bt, const pa_tensor* ctx, const pa_tensor* cu,
                 const pa_tensor* sp, int mode, const pa_tensor* out, const pa_decode_opts* opts,
-                void* stream_ptr, int32_t* check_report = nullptr) {
+                void* stream_ptr, int32_t* check_report = nullptr, bool no_alloc = false) {
   g_err.clear();
   int rc;
   if ((rc = check_tensor(q, "q"))) return rc;
@@ -277,10 +284,23 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   if (rows == 0) return PA_OK;
 
   uint32_t* counters = nullptr;
-  void* scratch = nullptr;
-  if ((rc = get_scratch(stream, size_t(plan.counter_bytes), size_t(plan.scratch_bytes - plan.counter_bytes),
-                        &counters, &scratch)))
+  void* partials = nullptr;
+  if (no_alloc) {
+    // the library's fixed array instead of an arena: never allocates
+    if (plan.fused_merge)
+      return fail(PA_ERR_UNSUPPORTED,
+                  "pa_decode_noalloc: the in-kernel merge needs per-unit counters; use the separate merge kernel");
+    const int64_t need = plan.merge ? plan.scratch_bytes - plan.counter_bytes : 0;
+    if (need > int64_t(PA_NOALLOC_MAX_SCRATCH_BYTES))
+      return fail(PA_ERR_CAPACITY, "pa_decode_noalloc: this call's split-K scratch bucket needs " +
+                                       std::to_string(need) + " bytes, above the fixed " +
+                                       std::to_string(int64_t(PA_NOALLOC_MAX_SCRATCH_BYTES)) +
+                                       "; use pa_decode with pa_reserve");
+    if (need > 0 && (rc = fixed_scratch(&partials))) return rc;
+  } else if ((rc = get_scratch(stream, size_t(plan.counter_bytes),
+                               size_t(plan.scratch_bytes - plan.counter_bytes), &counters, &partials))) {
     return rc;
+  }
 
   DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q->data);
@@ -302,8 +322,8 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   if (plan.merge) {
     const int64_t pairs = plan.balanced ? int64_t(plan.nslot) * plan.lrows * Hq
                                         : int64_t(plan.parts_launched) * rows * Hq;
-    a.part_ml = static_cast<float*>(scratch);
-    a.part_acc = static_cast<float*>(scratch) + 2 * pairs;
+    a.part_ml = static_cast<float*>(partials);
+    a.part_acc = static_cast<float*>(partials) + 2 * pairs;
     a.unit_count = plan.fused_merge ? counters : nullptr;
   }
   a.num_blocks = nb;
@@ -339,6 +359,38 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
 }  // namespace
 }  // namespace fp8pa
 
+// The split-K scratch of pa_decode_noalloc: a fixed array in every device's
+// memory, held from the library's load until the process ends.  All calls on
+// a device share it (they must not overlap in time), and it keeps the last
+// call's contents; nothing in it needs to start at zero, since every partial
+// a merge reads is written first by the same call's main kernel.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_MAX_SCRATCH_BYTES];
+
+namespace fp8pa {
+namespace {
+
+int fixed_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
+  static std::mutex mu;
+  static std::map<int, void*> addr;  // device -> address of `scratch` there
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(PA_ERR_HIP, std::string("hipGetSymbolAddress of the fixed scratch failed: ") +
+                                  hipGetErrorString(e));
+    it = addr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace fp8pa
+
 using namespace fp8pa;
 
 extern "C" {
@@ -358,6 +410,15 @@ int pa_decode_ex(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* 
                  const pa_decode_opts* opts, void* stream) {
   return decode_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, cu_seqlens_q,
                      sparse_page_idx, scale_mode, out, opts, stream);
+}
+
+int pa_decode_noalloc(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                      const pa_tensor* k_scale, const pa_tensor* v_scale, const pa_tensor* block_table,
+                      const pa_tensor* context_lens, const pa_tensor* cu_seqlens_q,
+                      const pa_tensor* sparse_page_idx, int scale_mode, pa_tensor* out,
+                      const pa_decode_opts* opts, void* stream) {
+  return decode_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, cu_seqlens_q,
+                     sparse_page_idx, scale_mode, out, opts, stream, nullptr, true);
 }
 
 int pa_check_decode_inputs(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,

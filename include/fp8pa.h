@@ -261,6 +261,31 @@ int pa_decode_ex(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* 
                  const pa_tensor* cu_seqlens_q, const pa_tensor* sparse_page_idx,
                  int scale_mode, pa_tensor* out, const pa_decode_opts* opts, void* stream);
 
+/* pa_decode_noalloc -- pa_decode_ex for callers that cannot allocate device
+ * memory: code under HIP graph capture without a prior pa_reserve, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, checks,
+ * kernels and results as pa_decode_ex; the split-K partials go to a fixed
+ * array the library holds in each device's memory for the life of the
+ * process (PA_NOALLOC_MAX_SCRATCH_BYTES per device), so the call allocates
+ * nothing, on the device or through any library.
+ *   Limits: a call whose scratch bucket (pa_plan_info.scratch_bytes, less
+ *   the in-kernel-merge counters) exceeds PA_NOALLOC_MAX_SCRATCH_BYTES
+ *   returns PA_ERR_CAPACITY; merge_mode PA_MERGE_IN_KERNEL returns
+ *   PA_ERR_UNSUPPORTED (it needs counters that start at zero).  Both before
+ *   any launch.
+ *   Sharing: every call on a device uses the same array, which keeps the
+ *   last call's contents.  Calls that overlap in time on one device (on two
+ *   streams, or replays of graphs holding such calls) race on it and give
+ *   wrong results: serialise them.
+ *   The first call on each device looks up the array's address (no stream
+ *   work); make it outside graph capture. */
+#define PA_NOALLOC_MAX_SCRATCH_BYTES (32u << 20)
+int pa_decode_noalloc(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                      const pa_tensor* k_scale, const pa_tensor* v_scale,
+                      const pa_tensor* block_table, const pa_tensor* context_lens,
+                      const pa_tensor* cu_seqlens_q, const pa_tensor* sparse_page_idx,
+                      int scale_mode, pa_tensor* out, const pa_decode_opts* opts, void* stream);
+
 /* Device-side check of a pa_decode call's inputs -- the preconditions the
  * host cannot see without reading device memory.  The pages keep a kernel-side
  * assert as a backstop for malformed decode metadata (ROCm/ATOM pull request

@@ -24,6 +24,9 @@ What it computes is the plain definition, written out slowly and in fp64:
 * ``indexer``   -- the sparse indexer that produces the block-sparse page
                    lists: per-page log2-sum-exp block scores over the fp8
                    index cache, and the per-row top-k rule.
+* ``norm_rope`` -- the writer fused with the key's RMS norm and rotary
+                   embedding: the textbook definitions in fp64, and the
+                   fp32 operation order whose output the cache writer takes.
 
 Sources (web pages about serving MiniMax-M3 with an FP8 KV cache on AMD
 GPUs):
@@ -39,6 +42,9 @@ GPUs):
 * vllm-project/vllm pull request 52060, "[ROCm][Perf] Fold scalar KV scales
   in MiniMax-M3 sparse attention": section "Suggested Fix" gives the scalar
   scale fold; "Test Plan" compares against a dequantized reference.
+* ROCm/ATOM pull request 2710, "Changes" (query/key norm, rotary embedding
+  and cache write fused for prefill) and its review, "Smaller" (the
+  norm-then-rope and rope-only cache-write branches must share one writer).
 """
 
-from . import bf16, e4m3, layout, writer, attention, indexer  # noqa: F401
+from . import bf16, e4m3, layout, writer, attention, indexer, norm_rope  # noqa: F401

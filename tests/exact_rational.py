@@ -82,3 +82,36 @@ def quantize_by_reciprocal(x: Fraction, amax: Fraction):
     s = round_f32(F(amax) / 448)
     r = round_f32(1 / s)
     return s, e4m3_code(round_f32(F(x) * r))
+
+
+def _next_f32(r: Fraction, up: bool) -> Fraction:
+    """The binary32 neighbour of a positive binary32 value r."""
+    e = max(_floor_log2(r), -126)
+    ulp = F(2) ** (e - 23)
+    if up:
+        return r + ulp
+    # stepping down from a power of two halves the spacing
+    if r == F(2) ** e and e > -126:
+        return r - ulp / 2
+    return r - ulp
+
+
+def sqrt_f32(v: Fraction) -> Fraction:
+    """The binary32 value nearest to sqrt(v) for v >= 0, decided exactly:
+    r is nearest when v lies between the squares of the midpoints to its
+    neighbours (a square root never falls on such a midpoint)."""
+    import math
+    v = F(v)
+    if v == 0:
+        return F(0)
+    r = round_f32(F(math.sqrt(v.numerator / v.denominator)))
+    while True:
+        up = _next_f32(r, True)
+        if v >= ((r + up) / 2) ** 2:
+            r = up
+            continue
+        dn = _next_f32(r, False)
+        if v < ((r + dn) / 2) ** 2:
+            r = dn
+            continue
+        return r

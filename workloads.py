@@ -36,6 +36,17 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return b.astype(np.uint32).view(np.float32)
 
 
+def rope_tables(max_pos: int, rot: int, base: float = 10000.0):
+    """Cosine and sine tables [max_pos, rot/2] (fp32) of the usual rotary
+    frequencies: column i turns by base^(-2i/rot) radians per position.
+    Model parameters handed to the fused writer, computed in fp64 and rounded
+    once to fp32."""
+    i = np.arange(rot // 2, dtype=np.float64)
+    inv_freq = base ** (-2.0 * i / rot)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 @dataclass
 class Workload:
     name: str

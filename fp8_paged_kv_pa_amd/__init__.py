@@ -13,7 +13,7 @@ import torch
 
 from ._lib import (  # noqa: F401
     EXPORTS, MERGE_IN_KERNEL, MERGE_PLAN, MERGE_SEPARATE, PARTITION_BALANCED, PARTITION_FIXED,
-    PARTITION_PLAN, PaConfig, PaDecodeOpts, PaError, PaPlanInfo, PaTensor, SCALE_NONE,
+    PARTITION_PLAN, PaConfig, PaDecodeOpts, PaError, PaNormRope, PaPlanInfo, PaTensor, SCALE_NONE,
     SCALE_PER_TOKEN, SCALE_SCALAR, STATUS, check, desc, load, ref, stream_handle,
 )
 
@@ -118,6 +118,27 @@ def kv_quant_write(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scal
     lib = load()
     d = [desc(t) for t in (k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale)]
     check(lib.kv_quant_write(*[ref(x) for x in d], int(scale_mode), stream_handle(stream)))
+
+
+def kv_norm_rope_write(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, scale_mode,
+                       positions, cos=None, sin=None, rotary_dim=0, neox=True, k_norm_weight=None,
+                       q_norm_weight=None, eps=1e-6, weight_offset=0.0, q=None, q_out=None, stream=None):
+    """``kv_quant_write`` fused with the key's RMS norm and rotary embedding,
+    and the same transform of ``q`` into ``q_out`` (see ``kv_norm_rope_write``
+    in include/fp8pa.h)."""
+    lib = load()
+    keep = [desc(t) for t in (positions, cos, sin, k_norm_weight, q_norm_weight)]
+    nr = PaNormRope()
+    nr.positions, nr.cos, nr.sin, nr.k_norm_weight, nr.q_norm_weight = [
+        None if x is None else ctypes.pointer(x) for x in keep]
+    nr.rotary_dim = int(rotary_dim)
+    nr.neox = 1 if neox else 0
+    nr.eps = float(eps)
+    nr.weight_offset = float(weight_offset)
+    d = [desc(t) for t in (q, q_out, k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale)]
+    check(lib.kv_norm_rope_write(*[ref(x) for x in d], int(scale_mode), ctypes.byref(nr),
+                                 stream_handle(stream)))
+    return q_out
 
 
 def pa_index_topk(q_idx, index_cache, block_table, context_lens, cu_seqlens_q, sparse_page_idx,

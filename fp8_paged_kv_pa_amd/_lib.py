@@ -46,6 +46,20 @@ class PaTensor(ctypes.Structure):
     ]
 
 
+class PaNormRope(ctypes.Structure):
+    _fields_ = [
+        ("positions", ctypes.POINTER(PaTensor)),
+        ("cos", ctypes.POINTER(PaTensor)),
+        ("sin", ctypes.POINTER(PaTensor)),
+        ("rotary_dim", ctypes.c_int32),
+        ("neox", ctypes.c_int32),
+        ("k_norm_weight", ctypes.POINTER(PaTensor)),
+        ("q_norm_weight", ctypes.POINTER(PaTensor)),
+        ("eps", ctypes.c_float),
+        ("weight_offset", ctypes.c_float),
+    ]
+
+
 class PaDecodeOpts(ctypes.Structure):
     _fields_ = [
         ("sm_scale", ctypes.c_float),
@@ -98,8 +112,8 @@ class PaPlanInfo(ctypes.Structure):
     ]
 
 
-EXPORTS = ("pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_check_decode_inputs", "kv_quant_write", "pa_index_topk",
-           "pa_query_support", "pa_plan_describe", "pa_reserve", "pa_release", "pa_last_error")
+EXPORTS = ("pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_check_decode_inputs", "kv_quant_write",
+           "kv_norm_rope_write", "pa_index_topk", "pa_query_support", "pa_plan_describe", "pa_reserve", "pa_release", "pa_last_error")
 
 _lib = None
 
@@ -126,6 +140,8 @@ def load():
     lib.pa_check_decode_inputs.restype = ctypes.c_int
     lib.kv_quant_write.argtypes = [T, T, T, T, T, T, T, ctypes.c_int, vp]
     lib.kv_quant_write.restype = ctypes.c_int
+    lib.kv_norm_rope_write.argtypes = [T, T, T, T, T, T, T, T, T, ctypes.c_int, P(PaNormRope), vp]
+    lib.kv_norm_rope_write.restype = ctypes.c_int
     lib.pa_index_topk.argtypes = [T, T, T, T, T, ctypes.c_int, ctypes.c_float, T, T, vp]
     lib.pa_index_topk.restype = ctypes.c_int
     lib.pa_query_support.argtypes = [P(PaConfig)]

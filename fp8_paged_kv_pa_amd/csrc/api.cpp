@@ -356,6 +356,151 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   return PA_OK;
 }
 
+// Checks the fused writer's norm and rotary arguments (and the query pair)
+// and fills the kernel's block.  Every condition is checked before launch.
+int check_norm_rope(const pa_norm_rope* nr, const pa_tensor* q, pa_tensor* q_out, int64_t T, int64_t hkv,
+                    NormRopeArgs* out) {
+  NormRopeArgs n{};
+  n.on = 1;
+  int rc;
+  if ((rc = check_tensor(nr->positions, "positions"))) return rc;
+  if (nr->positions->dtype != PA_DTYPE_I64 || nr->positions->ndim != 1 || nr->positions->shape[0] != T ||
+      (T > 1 && nr->positions->stride[0] != 1))
+    return fail(PA_ERR_SHAPE, "positions must be contiguous int64 [T]");
+  n.positions = static_cast<const int64_t*>(nr->positions->data);
+  if (nr->rotary_dim < 0 || nr->rotary_dim > kDim || nr->rotary_dim % 4 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "rotary_dim must be 0 or a multiple of 4 up to 128");
+  n.rot = nr->rotary_dim;
+  n.neox = nr->neox ? 1 : 0;
+  n.max_pos = 1;
+  if (n.rot > 0) {
+    const pa_tensor* tabs[2] = {nr->cos, nr->sin};
+    const char* names[2] = {"cos", "sin"};
+    for (int i = 0; i < 2; ++i) {
+      if ((rc = check_tensor(tabs[i], names[i]))) return rc;
+      if (tabs[i]->dtype != PA_DTYPE_F32 || tabs[i]->ndim != 2 || tabs[i]->shape[1] != n.rot / 2 ||
+          tabs[i]->shape[0] < 1 || tabs[i]->stride[1] != 1)
+        return fail(PA_ERR_SHAPE, std::string(names[i]) + " must be float32 [max_pos, rotary_dim/2], rows contiguous");
+    }
+    if (nr->cos->shape[0] != nr->sin->shape[0]) return fail(PA_ERR_SHAPE, "cos and sin differ in max_pos");
+    n.cos = static_cast<const float*>(nr->cos->data);
+    n.sin = static_cast<const float*>(nr->sin->data);
+    n.cos_stride = nr->cos->stride[0];
+    n.sin_stride = nr->sin->stride[0];
+    n.max_pos = nr->cos->shape[0];
+  }
+  const pa_tensor* ws[2] = {nr->k_norm_weight, nr->q_norm_weight};
+  const char* wnames[2] = {"k_norm_weight", "q_norm_weight"};
+  const float* wp[2] = {nullptr, nullptr};
+  for (int i = 0; i < 2; ++i) {
+    if (!ws[i] || !ws[i]->data) continue;
+    if ((rc = check_tensor(ws[i], wnames[i]))) return rc;
+    if (ws[i]->dtype != PA_DTYPE_F32 || numel(ws[i]) != kDim || (ws[i]->ndim == 1 && ws[i]->stride[0] != 1))
+      return fail(PA_ERR_SHAPE, std::string(wnames[i]) + " must be contiguous float32 [128]");
+    if (!contiguous(ws[i])) return fail(PA_ERR_LAYOUT, std::string(wnames[i]) + " must be contiguous");
+    wp[i] = static_cast<const float*>(ws[i]->data);
+  }
+  n.k_weight = wp[0];
+  n.q_weight = wp[1];
+  if (!std::isfinite(nr->eps) || nr->eps < 0.0f) return fail(PA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!std::isfinite(nr->weight_offset)) return fail(PA_ERR_INVALID_ARG, "weight_offset must be finite");
+  n.eps = nr->eps;
+  n.offset = nr->weight_offset;
+  const bool has_q = q && q->data;
+  const bool has_qo = q_out && q_out->data;
+  if (has_q != has_qo) return fail(PA_ERR_INVALID_ARG, "q and q_out are given together or not at all");
+  if (has_q) {
+    if ((rc = check_tensor(q, "q"))) return rc;
+    if ((rc = check_tensor(q_out, "q_out"))) return rc;
+    if (q->dtype != PA_DTYPE_F32 && q->dtype != PA_DTYPE_BF16) return fail(PA_ERR_DTYPE, "q must be float32 or bfloat16");
+    if (q_out->dtype != PA_DTYPE_BF16) return fail(PA_ERR_DTYPE, "q_out must be bfloat16");
+    if (q->ndim != 3 || q->shape[0] != T || q->shape[1] != kGroup * hkv || q->shape[2] != kDim)
+      return fail(PA_ERR_SHAPE, "q must be [T, 16*Hkv, 128]");
+    for (int i = 0; i < 3; ++i)
+      if (q_out->ndim != 3 || q_out->shape[i] != q->shape[i]) return fail(PA_ERR_SHAPE, "q_out must have the shape of q");
+    const int64_t qes = q->dtype == PA_DTYPE_F32 ? 4 : 2;
+    if (q->stride[2] != 1 || q->stride[0] % 2 || q->stride[1] % 2 || !aligned(q->data, uintptr_t(2 * qes)))
+      return fail(PA_ERR_LAYOUT, "q: last dim contiguous, even strides, aligned pairs");
+    if (q_out->stride[2] != 1 || q_out->stride[0] % 2 || q_out->stride[1] % 2 || !aligned(q_out->data, 4))
+      return fail(PA_ERR_LAYOUT, "q_out: last dim contiguous, even strides, 4-byte aligned");
+    n.q_in = q->data;
+    n.q_tok_stride = q->stride[0];
+    n.q_head_stride = q->stride[1];
+    n.q_bf16 = q->dtype == PA_DTYPE_BF16 ? 1 : 0;
+    n.hq = int32_t(q->shape[1]);
+    n.q_out = static_cast<uint16_t*>(q_out->data);
+    n.qo_tok_stride = q_out->stride[0];
+    n.qo_head_stride = q_out->stride[1];
+  }
+  *out = n;
+  return PA_OK;
+}
+
+int write_impl(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,
+               pa_tensor* k_cache, pa_tensor* v_cache, pa_tensor* k_scale, pa_tensor* v_scale, int scale_mode,
+               const pa_norm_rope* nr, const pa_tensor* q, pa_tensor* q_out, void* stream) {
+  g_err.clear();
+  int rc;
+
+  if ((rc = check_tensor(k_new, "k_new"))) return rc;
+  if ((rc = check_tensor(v_new, "v_new"))) return rc;
+  if (k_new->dtype != PA_DTYPE_F32 && k_new->dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_DTYPE, "k_new must be float32 or bfloat16");
+  if (v_new->dtype != k_new->dtype) return fail(PA_ERR_DTYPE, "k_new and v_new dtypes differ");
+  if (k_new->ndim != 3 || v_new->ndim != 3) return fail(PA_ERR_SHAPE, "k_new, v_new must be [T, Hkv, 128]");
+  for (int i = 0; i < 3; ++i)
+    if (k_new->shape[i] != v_new->shape[i]) return fail(PA_ERR_SHAPE, "k_new and v_new shapes differ");
+  const int64_t T = k_new->shape[0], hkv_in = k_new->shape[1];
+  if (k_new->shape[2] != kDim) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 128");
+  const int64_t esz = k_new->dtype == PA_DTYPE_F32 ? 4 : 2;
+  for (const pa_tensor* t : {k_new, v_new})
+    if (t->stride[2] != 1 || t->stride[0] % 2 || t->stride[1] % 2 || !aligned(t->data, uintptr_t(2 * esz)))
+      return fail(PA_ERR_LAYOUT, "k_new/v_new: last dim contiguous, even strides, aligned pairs");
+  if ((rc = check_tensor(slot_mapping, "slot_mapping"))) return rc;
+  if (slot_mapping->dtype != PA_DTYPE_I64 || slot_mapping->ndim != 1 || slot_mapping->shape[0] != T ||
+      (T > 1 && slot_mapping->stride[0] != 1))
+    return fail(PA_ERR_SHAPE, "slot_mapping must be contiguous int64 [T]");
+  int64_t nb = 0, hkv = 0, nb2 = 0, hkv2 = 0;
+  if ((rc = check_cache(k_cache, "k_cache", &nb, &hkv))) return rc;
+  if ((rc = check_cache(v_cache, "v_cache", &nb2, &hkv2))) return rc;
+  if (nb2 != nb || hkv2 != hkv) return fail(PA_ERR_SHAPE, "k_cache and v_cache shapes differ");
+  if (hkv != hkv_in) return fail(PA_ERR_SHAPE, "k_new has a different number of KV heads than the cache");
+  if (k_cache->dtype != v_cache->dtype) return fail(PA_ERR_DTYPE, "k_cache and v_cache dtypes differ");
+  if (scale_mode < PA_SCALE_NONE || scale_mode > PA_SCALE_PER_TOKEN)
+    return fail(PA_ERR_INVALID_ARG, "unknown scale_mode");
+  const bool bf16kv = k_cache->dtype == PA_DTYPE_BF16;
+  if (bf16kv && scale_mode != PA_SCALE_NONE)
+    return fail(PA_ERR_UNSUPPORTED, "a bfloat16 cache is unquantized: scale_mode must be PA_SCALE_NONE");
+  if ((rc = check_scales(k_scale, v_scale, scale_mode, nb, hkv))) return rc;
+  NormRopeArgs nra{};
+  if (nr && (rc = check_norm_rope(nr, q, q_out, T, hkv, &nra))) return rc;
+  if (T == 0) return PA_OK;
+  if (T * (hkv + nra.hq) > kMaxGrid) return fail(PA_ERR_CAPACITY, "too many (token, head) pairs for one launch");
+
+  WriteArgs a{};
+  a.k_new = k_new->data;
+  a.v_new = v_new->data;
+  a.k_tok_stride = k_new->stride[0];
+  a.k_head_stride = k_new->stride[1];
+  a.v_tok_stride = v_new->stride[0];
+  a.v_head_stride = v_new->stride[1];
+  a.in_bf16 = k_new->dtype == PA_DTYPE_BF16;
+  a.out_bf16 = bf16kv ? 1 : 0;
+  a.slots = static_cast<const int64_t*>(slot_mapping->data);
+  a.k_cache = static_cast<uint8_t*>(k_cache->data);
+  a.v_cache = static_cast<uint8_t*>(v_cache->data);
+  a.k_scale = scale_mode == PA_SCALE_NONE ? nullptr : static_cast<float*>(k_scale->data);
+  a.v_scale = scale_mode == PA_SCALE_NONE ? nullptr : static_cast<float*>(v_scale->data);
+  a.num_blocks = nb;
+  a.tokens = T;
+  a.hkv = int32_t(hkv);
+  a.scale_mode = scale_mode;
+  a.nr = nra;
+  hipError_t he = launch_write(a, reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return fail(PA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(he));
+  return PA_OK;
+}
+
 }  // namespace
 }  // namespace fp8pa
 
@@ -434,64 +579,18 @@ int pa_check_decode_inputs(const pa_tensor* q, const pa_tensor* k_cache, const p
 int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,
                    pa_tensor* k_cache, pa_tensor* v_cache, pa_tensor* k_scale, pa_tensor* v_scale,
                    int scale_mode, void* stream) {
-  g_err.clear();
-  int rc;
-  if ((rc = check_tensor(k_new, "k_new"))) return rc;
-  if ((rc = check_tensor(v_new, "v_new"))) return rc;
-  if (k_new->dtype != PA_DTYPE_F32 && k_new->dtype != PA_DTYPE_BF16)
-    return fail(PA_ERR_DTYPE, "k_new must be float32 or bfloat16");
-  if (v_new->dtype != k_new->dtype) return fail(PA_ERR_DTYPE, "k_new and v_new dtypes differ");
-  if (k_new->ndim != 3 || v_new->ndim != 3) return fail(PA_ERR_SHAPE, "k_new, v_new must be [T, Hkv, 128]");
-  for (int i = 0; i < 3; ++i)
-    if (k_new->shape[i] != v_new->shape[i]) return fail(PA_ERR_SHAPE, "k_new and v_new shapes differ");
-  const int64_t T = k_new->shape[0], hkv_in = k_new->shape[1];
-  if (k_new->shape[2] != kDim) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 128");
-  const int64_t esz = k_new->dtype == PA_DTYPE_F32 ? 4 : 2;
-  for (const pa_tensor* t : {k_new, v_new})
-    if (t->stride[2] != 1 || t->stride[0] % 2 || t->stride[1] % 2 || !aligned(t->data, uintptr_t(2 * esz)))
-      return fail(PA_ERR_LAYOUT, "k_new/v_new: last dim contiguous, even strides, aligned pairs");
-  if ((rc = check_tensor(slot_mapping, "slot_mapping"))) return rc;
-  if (slot_mapping->dtype != PA_DTYPE_I64 || slot_mapping->ndim != 1 || slot_mapping->shape[0] != T ||
-      (T > 1 && slot_mapping->stride[0] != 1))
-    return fail(PA_ERR_SHAPE, "slot_mapping must be contiguous int64 [T]");
-  int64_t nb = 0, hkv = 0, nb2 = 0, hkv2 = 0;
-  if ((rc = check_cache(k_cache, "k_cache", &nb, &hkv))) return rc;
-  if ((rc = check_cache(v_cache, "v_cache", &nb2, &hkv2))) return rc;
-  if (nb2 != nb || hkv2 != hkv) return fail(PA_ERR_SHAPE, "k_cache and v_cache shapes differ");
-  if (hkv != hkv_in) return fail(PA_ERR_SHAPE, "k_new has a different number of KV heads than the cache");
-  if (k_cache->dtype != v_cache->dtype) return fail(PA_ERR_DTYPE, "k_cache and v_cache dtypes differ");
-  if (scale_mode < PA_SCALE_NONE || scale_mode > PA_SCALE_PER_TOKEN)
-    return fail(PA_ERR_INVALID_ARG, "unknown scale_mode");
-  const bool bf16kv = k_cache->dtype == PA_DTYPE_BF16;
-  if (bf16kv && scale_mode != PA_SCALE_NONE)
-    return fail(PA_ERR_UNSUPPORTED, "a bfloat16 cache is unquantized: scale_mode must be PA_SCALE_NONE");
-  if ((rc = check_scales(k_scale, v_scale, scale_mode, nb, hkv))) return rc;
-  if (T == 0) return PA_OK;
-  if (T * hkv > kMaxGrid) return fail(PA_ERR_CAPACITY, "too many (token, KV head) pairs for one launch");
-
-  WriteArgs a{};
-  a.k_new = k_new->data;
-  a.v_new = v_new->data;
-  a.k_tok_stride = k_new->stride[0];
-  a.k_head_stride = k_new->stride[1];
-  a.v_tok_stride = v_new->stride[0];
-  a.v_head_stride = v_new->stride[1];
-  a.in_bf16 = k_new->dtype == PA_DTYPE_BF16;
-  a.out_bf16 = bf16kv ? 1 : 0;
-  a.slots = static_cast<const int64_t*>(slot_mapping->data);
-  a.k_cache = static_cast<uint8_t*>(k_cache->data);
-  a.v_cache = static_cast<uint8_t*>(v_cache->data);
-  a.k_scale = scale_mode == PA_SCALE_NONE ? nullptr : static_cast<float*>(k_scale->data);
-  a.v_scale = scale_mode == PA_SCALE_NONE ? nullptr : static_cast<float*>(v_scale->data);
-  a.num_blocks = nb;
-  a.tokens = T;
-  a.hkv = int32_t(hkv);
-  a.scale_mode = scale_mode;
-  hipError_t he = launch_write(a, reinterpret_cast<hipStream_t>(stream));
-  if (he != hipSuccess) return fail(PA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(he));
-  return PA_OK;
+  return write_impl(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, scale_mode, nullptr,
+                    nullptr, nullptr, stream);
 }
 
+int kv_norm_rope_write(const pa_tensor* q, pa_tensor* q_out, const pa_tensor* k_new, const pa_tensor* v_new,
+                       const pa_tensor* slot_mapping, pa_tensor* k_cache, pa_tensor* v_cache,
+                       pa_tensor* k_scale, pa_tensor* v_scale, int scale_mode, const pa_norm_rope* nr,
+                       void* stream) {
+  if (!nr) return fail(PA_ERR_INVALID_ARG, "kv_norm_rope_write: nr is NULL");
+  return write_impl(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, scale_mode, nr, q,
+                    q_out, stream);
+}
 int pa_index_topk(const pa_tensor* q_idx, const pa_tensor* index_cache, const pa_tensor* block_table,
                   const pa_tensor* context_lens, const pa_tensor* cu_seqlens_q, int max_q_len, float sm_scale,
                   pa_tensor* sparse_page_idx, pa_tensor* block_scores, void* stream) {

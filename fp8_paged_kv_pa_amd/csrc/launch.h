@@ -53,6 +53,29 @@ struct DecodeArgs {
   float sm_log2;              // sm_scale * log2(e)
 };
 
+// The key norm and rotary embedding the fused writer applies before the
+// cache write (kv_norm_rope_write), and the query it transforms alongside.
+struct NormRopeArgs {
+  int32_t on;                 // 0: the plain writer
+  const int64_t* positions;   // [T]
+  const float* cos;           // [max_pos, rot/2] (rows cos_stride apart)
+  const float* sin;
+  int64_t cos_stride, sin_stride;  // elements
+  int64_t max_pos;
+  int32_t rot;                // 0 or a multiple of 4 up to 128
+  int32_t neox;               // 1: pairs (i, i + rot/2); 0: pairs (2i, 2i + 1)
+  const float* k_weight;      // [128] or null (no norm on K)
+  const float* q_weight;      // [128] or null
+  float eps;
+  float offset;               // 0: x_hat * w, 1: x_hat * (1 + w)
+  const void* q_in;           // f32 or bf16 [T, Hq, 128], or null
+  int64_t q_tok_stride, q_head_stride;
+  int32_t q_bf16;
+  int32_t hq;
+  uint16_t* q_out;            // bf16 [T, Hq, 128]
+  int64_t qo_tok_stride, qo_head_stride;
+};
+
 struct WriteArgs {
   const void* k_new;          // f32 or bf16 [T, Hkv, 128]
   const void* v_new;
@@ -69,6 +92,7 @@ struct WriteArgs {
   int64_t tokens;
   int32_t hkv;
   int32_t scale_mode;
+  NormRopeArgs nr;
 };
 
 // Arguments of the sparse-indexer kernels (block scores, then top-k).

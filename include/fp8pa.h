@@ -349,6 +349,60 @@ int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new,
                    pa_tensor* k_scale, pa_tensor* v_scale, int scale_mode, void* stream);
 
 /*
+ * kv_norm_rope_write -- kv_quant_write fused with the key's RMS norm and
+ * rotary position embedding, and the same transform of the query in the
+ * same launch ([ATOM-2710] "Changes": query/key norm, rotary embedding and
+ * cache write fused for prefill; its review, "Smaller": the norm-then-rope
+ * path and the rope-only path repeated one cache-write branch and drifted,
+ * so both must go through one writer).  K is transformed in registers and
+ * then quantized and stored by exactly the code of kv_quant_write; V is
+ * written as it comes.  The pages give no norm or rotary parameters, so all
+ * are the caller's (pa_norm_rope).
+ *
+ *   Per (token t, head): with x the 128 values (bf16 inputs widened),
+ *     norm (if a weight is given): y_d = x_d / sqrt(mean(x^2) + eps)
+ *       * (weight_offset + w_d)  (weight_offset 0: plain RMS norm, 1: the
+ *       Gemma form 1 + w);
+ *     rotary (rotary_dim > 0): pairs (i, i + rotary_dim/2) when neox, else
+ *       (2i, 2i+1), i < rotary_dim/2; with c = cos[pos_t][i], s =
+ *       sin[pos_t][i], the pair (a, b) becomes (a*c - b*s, b*c + a*s); dims
+ *       from rotary_dim on pass unchanged.
+ *   fp32 order, each step one IEEE operation rounded to nearest even, never
+ *   fused: sq_d = x_d*x_d; S = balanced binary tree over d in order (sq_0 +
+ *   sq_1, sq_2 + sq_3, ..., then adjacent pairs); inv = 1 / sqrt(S/128 +
+ *   eps) (correctly rounded divide and square root); y_d = (x_d*inv) *
+ *   (weight_offset + w_d); rotary products rounded, then their difference
+ *   or sum.
+ *
+ *   q, q_out   optional (both or neither): q f32 or bf16 [T, 16*Hkv, 128]
+ *              (last dim contiguous, even strides), q_out bf16 of the same
+ *              shape: the query after its norm (q_norm_weight) and the same
+ *              rotary embedding, rounded to bf16 (nearest even).
+ *   k_new .. scale_mode, stream   as kv_quant_write.
+ *   nr         the transform's parameters (below).
+ * Positions outside [0, max_pos) are clamped into it (device values are not
+ * checked on the host).  Everything else is checked before launch.
+ * Asynchronous; no allocation.  Returns PA_OK or a pa_status.
+ */
+typedef struct pa_norm_rope {
+  const pa_tensor* positions;      /* int64 [T], contiguous                     */
+  const pa_tensor* cos;            /* float32 [max_pos, rotary_dim/2], rows    */
+  const pa_tensor* sin;            /* contiguous; may be NULL if rotary_dim 0  */
+  int32_t rotary_dim;              /* 0 (no rotary) or a multiple of 4 <= 128  */
+  int32_t neox;                    /* 1: pairs (i, i + rotary_dim/2);          */
+                                   /* 0: pairs (2i, 2i+1)                      */
+  const pa_tensor* k_norm_weight;  /* float32 [128] or NULL (no norm on K)     */
+  const pa_tensor* q_norm_weight;  /* float32 [128] or NULL (no norm on q)     */
+  float eps;                       /* finite, >= 0                             */
+  float weight_offset;             /* finite: 0 plain, 1 Gemma (1 + w)         */
+} pa_norm_rope;
+
+int kv_norm_rope_write(const pa_tensor* q, pa_tensor* q_out, const pa_tensor* k_new,
+                       const pa_tensor* v_new, const pa_tensor* slot_mapping, pa_tensor* k_cache,
+                       pa_tensor* v_cache, pa_tensor* k_scale, pa_tensor* v_scale, int scale_mode,
+                       const pa_norm_rope* nr, void* stream);
+
+/*
  * pa_index_topk -- the sparse indexer that produces sparse_page_idx for the
  * block-sparse pa_decode ([ATOM-2122] section 1: the index cache is
  * float8_e4m3fn (num_blocks, 128, 128) and the block score is the fp32

@@ -57,7 +57,13 @@ CONFIGS = {
     "c5b": lambda: wl.bf16_kv(wl.c5_sparse(False)),
     # the sparse indexer in the step: write, index top-32, block-sparse decode
     "c5i": lambda: wl.index_workload("c5"),
+    # per-token-as-decode prefill of a 16K prompt (one q_len-16384 request)
+    "p16k": lambda: wl.prefill_16k(),
 }
+# shapes whose main kernel is bound by the matrix cores, not HBM: their
+# roofline is algorithmic flops against the dense bf16 MFMA peak
+MFMA_BOUND = {"p16k"}
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 INDEX_TOPK = {"c5i": 32}
 
 
@@ -183,6 +189,24 @@ class Layers:
                         main_end_event=None if ev is None else ev[1])
 
 
+def algorithmic_flops(w):
+    """Flops one decode call must do: for every (query row, query head,
+    attended token) a 128-wide dot product for the score and a 128-wide
+    multiply-add of V (2 flops per multiply-add each)."""
+    rs = w.row_start
+    pairs = 0
+    for b in range(w.B):
+        L, c = int(w.q_lens[b]), min(int(w.ctx[b]), w.W * 128)
+        for i in range(L):
+            lim = max(0, min(int(w.ctx[b]) - L + i + 1, c))
+            if w.sparse is None:
+                pairs += lim
+            else:
+                sel = {int(x) for x in w.sparse[rs[b] + i] if 0 <= x < w.W}
+                pairs += sum(max(0, min(128, lim - 128 * x)) for x in sel)
+    return pairs * w.Hq * 128 * 4
+
+
 def index_bytes(w, topk):
     """Bytes one pa_index_topk call must move: the index keys of every
     visible page once per request (the rows of a request share each read),
@@ -278,6 +302,62 @@ def hbm_probe(dev, gib=4, same_bytes=None):
     del buf
     torch.cuda.empty_cache()
     return round(best, 1), best_small
+
+
+def block_probe(layers, w):
+    """Best rate (GB/s) of the bench probe library's block-read kernel over
+    exactly the (page, head) blocks one decode call reads -- every request's
+    attended pages of layer l, K and V (and their scale pieces in per-token
+    mode) -- with non-temporal 16-byte loads and no arithmetic, 256
+    workgroups, rotating over the layers as the bench's steps do.  FP8
+    caches only; None otherwise."""
+    import ctypes
+    path = os.path.join(ROOT, "fp8_paged_kv_pa_amd", "libhbmprobe.so")
+    if not os.path.exists(path) or w.kv_dtype == "bf16":
+        return None
+    lib = ctypes.CDLL(path)
+    lib.hbm_block_probe.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                                             ctypes.c_void_p]
+    ids = []
+    for b in range(w.B):
+        if w.sparse is None:
+            pages = range(min((int(w.ctx[b]) + 127) // 128, w.W))
+        else:
+            start, L = int(w.row_start[b]), int(w.q_lens[b])
+            pages = sorted({int(x) for r in range(start, start + L) for x in w.sparse[r] if 0 <= x < w.W})
+        for n in pages:
+            P = int(w.block_table[b, n])
+            ids += [P * w.Hkv + h for h in range(w.Hkv)]
+    nblk = w.num_blocks * w.Hkv
+    assert ids and all(0 <= i < nblk for i in ids)
+    wgs = 256
+    per_wg = (len(ids) + wgs - 1) // wgs
+    tab = np.resize(np.asarray(ids, np.int32), per_wg * wgs)
+    dev = layers.q[0].device
+    table = torch.from_numpy(tab).to(dev)
+    sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+    pt = w.mode == wl.PER_TOKEN
+    nbytes = len(tab) * (2 * 16384 + (2 * 512 if pt else 0))
+    stream = torch.cuda.current_stream()
+    best = 0.0
+    for rnd in range(3):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(16)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(5e7))
+        for i, (e0, e1) in enumerate(evs):
+            l = i % layers.n
+            e0.record()
+            rc = lib.hbm_block_probe(layers.kcl[l].data_ptr(), layers.vcl[l].data_ptr(),
+                                     layers.ksl[l].data_ptr() if pt else None,
+                                     layers.vsl[l].data_ptr() if pt else None,
+                                     table.data_ptr(), per_wg, wgs, sink.data_ptr(), stream.cuda_stream)
+            e1.record()
+            if rc != 0:
+                return None
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs[2:])
+        best = max(best, nbytes / (ts[len(ts) // 2] * 1e-3) / 1e9)
+    return round(best, 1)
 
 
 def cpu_model():
@@ -508,7 +588,7 @@ def main():
         # now, recomputed from the lists the indexer produced after warmup
         w.sparse = np.zeros((w.rows, index_topk), np.int32)
     kv_bytes, alg_bytes = algorithmic_bytes(w)
-    n_layers = args.layers or max(1, min(64, int(math.ceil(1.0e9 / max(kv_bytes + idx_bytes, 1)))))
+    n_layers = args.layers or max(1, min(64, int(math.ceil(1.0e9 / max(alg_bytes + idx_bytes, 1)))))
     if index_topk:
         w.sparse = None
     # the oracle's workers are forked now, before this process touches the
@@ -598,6 +678,8 @@ def main():
               f"steps queued behind a spin kernel")
     main_avg_ms = float(np.mean(main_ms))
     achieved = alg_bytes / (main_avg_ms * 1e-3) / 1e9
+    mfma_bound = args.config in MFMA_BOUND
+    flops = algorithmic_flops(w) if mfma_bound else 0
     value = (kv_bytes + idx_bytes) / (ms_per_step * 1e-3) / 1e9
     index_avg_ms = float(np.mean([a.elapsed_time(b) for a, b in evs_idx])) if index_topk else None
     tokens_per_s = w.attended_tokens() * w.Hkv / (ms_per_step * 1e-3)
@@ -628,6 +710,7 @@ def main():
         torch.cuda.synchronize()
 
     probe, probe_same = hbm_probe(dev, same_bytes=idx_bytes if index_topk else alg_bytes) or (None, None)
+    probe_blocks = None if index_topk else block_probe(layers, w)
     try:
         cpu = None if leg is None else leg.run(layers)
     finally:
@@ -678,6 +761,8 @@ def main():
             "frac_of_probe": None if not probe else round(achieved / probe, 4),
             "hbm_read_probe_same_bytes_gbs": probe_same,
             "frac_of_same_bytes_probe": None if not probe_same else round(achieved / probe_same, 4),
+            "block_read_probe_gbs": probe_blocks,
+            "frac_of_block_probe": None if not probe_blocks else round(achieved / probe_blocks, 4),
         },
         "cpu_baseline": cpu,
         "cold_launch": {
@@ -687,6 +772,22 @@ def main():
                     "kernel's dispatch-recorded events, and host wall time from submission to completion",
         },
     }
+    if mfma_bound:
+        # q_len 16384 over a 16384-token context: ~8000 flop per byte moved,
+        # far above the bf16 ridge (~312 flop/B), so the roofline is the MFMA one
+        tf = flops / (main_avg_ms * 1e-3) / 1e12
+        res["decode_main_hbm"] = {k: res["roofline"][k] for k in ("achieved", "frac", "algorithmic_bytes_per_launch")}
+        res["roofline"].update({
+            "bound": "mfma",
+            "achieved": round(tf, 2),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": int(flops),
+            "dtype_note": "bf16 MFMA peak (dense); the kernel runs P.V as a bf16 hi + lo pair, "
+                          "1.5x the algorithmic MFMA work",
+        })
     if index_topk:
         # the indexer reads 16x the decode's bytes here: it is the dominant kernel
         ia = idx_bytes / (index_avg_ms * 1e-3) / 1e9

@@ -349,6 +349,25 @@ __device__ void merge_if_last(const DecodeArgs& a, int64_t unit, int row0, int n
   if (t == 0) __hip_atomic_store(a.unit_count + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Workgroup id -> (unit q, row group gi) of a dense grid with several row
+// groups per unit.  With at least 8 units, id x + 8s carries row group
+// s % groups of unit 8(s / groups) + x: ids go round-robin over the 8 XCDs,
+// so the groups of one unit are consecutive dispatches on one XCD and the
+// second read of each page is an L2 hit.  With fewer than 8 units (long
+// q_len over few requests, e.g. a prompt run as one request) that layout
+// would leave XCDs idle, so the ids run over (row group, unit) with the unit
+// fastest and every XCD gets row groups.
+__device__ __forceinline__ void xcd_group_of(const DecodeArgs& a, uint32_t* q, int* gi) {
+  if (a.nq < 8) {
+    *q = blockIdx.x % uint32_t(a.nq);
+    *gi = int(blockIdx.x / uint32_t(a.nq));
+  } else {
+    const uint32_t x = blockIdx.x & 7u, s = blockIdx.x >> 3;
+    *gi = int(s % uint32_t(a.groups));
+    *q = (s / uint32_t(a.groups)) * 8u + x;
+  }
+}
+
 template <int RT, bool PER_TOKEN, bool SPARSE, int NBUF, int NW, bool BF>
 __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, BF>)) void pa_decode_main(
     DecodeArgs a) {
@@ -378,9 +397,8 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     uint32_t slot;
     if (a.xcd_grouped) {
       // as below: the row groups of one (slot, KV head) on one XCD
-      const uint32_t x = blockIdx.x & 7u, s = blockIdx.x >> 3;
-      bal_gi = int(s % uint32_t(a.groups));
-      const uint32_t q = (s / uint32_t(a.groups)) * 8u + x;
+      uint32_t q;
+      xcd_group_of(a, &q, &bal_gi);
       if (q >= uint32_t(a.nq)) return;
       slot = q / uint32_t(a.hkv);
       bal_h = int(q % uint32_t(a.hkv));
@@ -403,10 +421,10 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     // give them workgroup ids x + 8s, x + 8(s+1), ... -- consecutive
     // dispatches on the same XCD (ids go round-robin over the 8 XCDs), so
     // the second read of each page is an L2 hit.
-    const uint32_t x = blockIdx.x & 7u, s = blockIdx.x >> 3;
-    const uint32_t gi = s % uint32_t(a.groups);
-    const uint32_t q = (s / uint32_t(a.groups)) * 8u + x;  // (partition, request, KV head)
-    if (q >= uint32_t(a.nq)) return;                         // padding of the last XCD round
+    uint32_t q;  // (partition, request, KV head)
+    int gi;
+    xcd_group_of(a, &q, &gi);
+    if (q >= uint32_t(a.nq)) return;  // padding of the last XCD round
     const uint32_t nbh = uint32_t(a.nq / a.parts);
     part = int(q / nbh);
     unit = int64_t(q % nbh) * a.groups + gi;

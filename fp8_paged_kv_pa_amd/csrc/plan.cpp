@@ -12,6 +12,14 @@ int fail(std::string* err, int code, const std::string& msg) {
   return code;
 }
 
+// Workgroups of a dense grid of `nq` units with `groups` row groups each
+// (see the kernel's xcd_group_of): whole rounds of 8 units when there are at
+// least 8, so each unit's groups stay on one XCD; otherwise exactly
+// nq * groups, spread over the XCDs.
+int64_t xcd_grid(int64_t nq, int64_t groups) {
+  return nq >= 8 ? ceil_div(nq, 8) * 8 * groups : nq * groups;
+}
+
 }  // namespace
 
 int make_plan(const pa_config& c, Plan* out, std::string* err) {
@@ -115,7 +123,7 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
     // 8j + x: the groups of a triple run back to back on one XCD
     p.xcd_grouped = true;
     p.nq = c.batch * hkv * p.parts_launched;
-    p.grid = ceil_div(p.nq, 8) * 8 * p.groups;
+    p.grid = xcd_grid(p.nq, p.groups);
   }
   if (p.merge) {
     // (m, l) pair + 128 accumulators per (partition, row, query head), sized
@@ -157,7 +165,7 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
     p.xcd_grouped = p.groups > 1;
     if (p.xcd_grouped) {
       p.nq = int64_t(p.nslot) * hkv;
-      p.grid = ceil_div(p.nq, 8) * 8 * p.groups;
+      p.grid = xcd_grid(p.nq, p.groups);
     } else {
       p.nq = 0;
       p.grid = int64_t(p.nslot) * hkv;

@@ -41,6 +41,42 @@ static pa_config base() {
 }
 
 // the C ABI's struct layouts (the Python binding mirrors them)
+// The dense multi-group grid as the kernel reads it (a restatement written
+// here, not shared with the library): with at least 8 units, id x + 8s is
+// row group s % groups of unit 8(s / groups) + x; with fewer, id is row
+// group id / nq of unit id % nq.
+static long long xcd_grid_ref(long long nq, long long groups) {
+  return nq >= 8 ? (nq + 7) / 8 * 8 * groups : nq * groups;
+}
+
+static void check_xcd_layout(long long nq, long long groups, long long grid) {
+  if (grid > (1 << 20)) return;
+  std::vector<unsigned char> seen(size_t(nq * groups), 0);
+  std::vector<unsigned char> xcd_used(8, 0);
+  for (long long bid = 0; bid < grid; ++bid) {
+    long long q, gi;
+    if (nq >= 8) {
+      const long long x = bid & 7, sidx = bid >> 3;
+      gi = sidx % groups;
+      q = (sidx / groups) * 8 + x;
+      if (q >= nq) continue;
+      CHECK(bid % 8 == q % 8, "a unit's groups share an XCD");
+    } else {
+      q = bid % nq;
+      gi = bid / nq;
+    }
+    CHECK(q < nq && gi < groups, "in range");
+    seen[size_t(q * groups + gi)]++;
+    xcd_used[size_t(bid % 8)] = 1;
+  }
+  bool once = true;
+  for (unsigned char v : seen) once = once && v == 1;
+  CHECK(once, "every (unit, group) exactly once");
+  int used = 0;
+  for (unsigned char v : xcd_used) used += v;
+  CHECK(used == (grid >= 8 ? 8 : int(grid)), "work on every XCD the grid can reach (%d)", used);
+}
+
 static_assert(sizeof(pa_tensor) == 8 + 4 + 4 + 6 * 8 * 2, "pa_tensor");
 static_assert(sizeof(pa_decode_opts) == 48, "pa_decode_opts");
 static_assert(sizeof(pa_config) == 6 * 4 + 4 * 8 + 5 * 4 + 4, "pa_config");
@@ -87,7 +123,7 @@ int main() {
   std::set<long long> scratch_by_bucket[32];
   for (int hkv : {1, 2, 8}) {
     for (long long batch : {1LL, 2LL, 3LL, 4LL, 31LL, 32LL, 33LL, 100LL, 4096LL}) {
-      for (int L : {1, 2, 3, 4, 6}) {
+      for (int L : {1, 2, 3, 4, 6, 300}) {
         for (long long W : {1LL, 2LL, 5LL, 72LL, 256LL, 1024LL, 3000LL}) {
           for (long long topk : {0LL, 1LL, 32LL, 100LL}) {
             for (int fp : {0, 1, 3, 64}) {
@@ -133,20 +169,8 @@ int main() {
                 // the XCD-grouped layout covers every (triple, row group) once
                 CHECK(!topk && p.groups > 1, "xcd layout only for dense multi-group calls");
                 CHECK(p.nq == batch * hkv * p.parts_launched, "triples");
-                CHECK(p.grid == (p.nq + 7) / 8 * 8 * p.groups, "xcd grid");
-                if (p.grid <= (1 << 20)) {
-                  std::vector<unsigned char> seen(size_t(p.nq * p.groups), 0);
-                  for (long long bid = 0; bid < p.grid; ++bid) {
-                    const long long x = bid & 7, sidx = bid >> 3;
-                    const long long gi = sidx % p.groups, q = (sidx / p.groups) * 8 + x;
-                    if (q >= p.nq) continue;
-                    CHECK(bid % 8 == q % 8, "a triple's groups share an XCD");
-                    seen[size_t(q * p.groups + gi)]++;
-                  }
-                  bool once = true;
-                  for (unsigned char v : seen) once = once && v == 1;
-                  CHECK(once, "every (triple, group) exactly once");
-                }
+                CHECK(p.grid == xcd_grid_ref(p.nq, p.groups), "xcd grid");
+                check_xcd_layout(p.nq, p.groups, p.grid);
               }
               if (p.merge) {
                 const long long need = (long long)p.parts_launched * c.rows * 16 * hkv * 130 * 4;
@@ -181,7 +205,7 @@ int main() {
   // length-balanced partitions: when the plan chooses them, what it lays out
   for (int hkv : {1, 2, 8}) {
     for (long long batch : {1LL, 3LL, 31LL, 63LL, 64LL, 65LL}) {
-      for (int L : {1, 2, 4, 6}) {
+      for (int L : {1, 2, 4, 6, 300, 16384}) {
         for (long long W : {1LL, 5LL, 72LL, 256LL, 1024LL, 3000LL}) {
           for (int mode : {PA_PARTITION_PLAN, PA_PARTITION_FIXED, PA_PARTITION_BALANCED}) {
             pa_config c = base();
@@ -190,6 +214,7 @@ int main() {
             c.rows = batch * L;
             c.max_pages = W;
             c.partition_mode = mode;
+            if (c.rows > kMaxRows) continue;
             Plan fixed;
             pa_config cf = c;
             cf.partition_mode = PA_PARTITION_FIXED;
@@ -197,6 +222,14 @@ int main() {
             const int rc = make_plan(c, &p, &err);
             if (mode == PA_PARTITION_BALANCED && batch > kMaxBalancedBatch) {
               CHECK(rc == PA_ERR_UNSUPPORTED, "balanced beyond 64 requests refused");
+              continue;
+            }
+            if (rc == PA_ERR_CAPACITY) {
+              // a balanced split whose bucketed scratch exceeds the largest bucket
+              const long long groups = (L + 1) / 2, rt = L > 1 ? 2 : 1;
+              const long long nslot = std::max<long long>(kTargetWorkgroups / (hkv * groups), batch + 1);
+              const long long want = next_pow2(nslot) * next_pow2(groups * rt) * hkv * 16 * 130 * 4;
+              CHECK(want > kMaxScratchBytes, "balanced refused although %lld bytes fit", want);
               continue;
             }
             CHECK(rc == PA_OK, "balanced plan rc %d (%s)", rc, err.c_str());
@@ -214,7 +247,8 @@ int main() {
             CHECK(p.scratch_bytes - p.counter_bytes >= need, "balanced scratch");
             if (p.groups > 1) {
               CHECK(p.xcd_grouped && p.nq == (long long)p.nslot * hkv, "balanced pairs");
-              CHECK(p.grid == (p.nq + 7) / 8 * 8 * p.groups, "balanced xcd grid");
+              CHECK(p.grid == xcd_grid_ref(p.nq, p.groups), "balanced xcd grid");
+              check_xcd_layout(p.nq, p.groups, p.grid);
             } else {
               CHECK(!p.xcd_grouped && p.grid == (long long)p.nslot * hkv, "balanced grid");
             }

@@ -290,6 +290,14 @@ def c5_sparse(tail=False):
                  [1] * 16, 1, 16384, False, sparse_topk=32)
 
 
+def prefill_16k(Hkv=1):
+    """Per-token-as-decode prefill of a 16384-token prompt: one request whose
+    q_len is the whole prompt (ragged form, cu_seqlens_q given), context
+    16384 (128 pages), per-token e4m3 scales; 16384 x 16 query heads of
+    bf16 output per KV head (64 MiB)."""
+    return _make("prefill_16k", 20268, [16384], [16384], Hkv, 160, True)
+
+
 def small_case(seed, ctx, q_lens, Hkv=1, ragged=False, mode=PER_TOKEN, sparse_topk=0,
                pool=None, W=None):
     """A parity case sized for the oracle: any contexts, q_lens and heads."""

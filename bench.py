@@ -309,8 +309,9 @@ def block_probe(layers, w):
     exactly the (page, head) blocks one decode call reads -- every request's
     attended pages of layer l, K and V (and their scale pieces in per-token
     mode) -- with non-temporal 16-byte loads and no arithmetic, 256
-    workgroups, rotating over the layers as the bench's steps do.  FP8
-    caches only; None otherwise."""
+    workgroups, rotating over the layers as the bench's steps do; and, in
+    per-token mode, the same over the K/V blocks alone.  FP8 caches only;
+    None otherwise."""
     import ctypes
     path = os.path.join(ROOT, "fp8_paged_kv_pa_amd", "libhbmprobe.so")
     if not os.path.exists(path) or w.kv_dtype == "bf16":
@@ -336,28 +337,34 @@ def block_probe(layers, w):
     dev = layers.q[0].device
     table = torch.from_numpy(tab).to(dev)
     sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
-    pt = w.mode == wl.PER_TOKEN
-    nbytes = len(tab) * (2 * 16384 + (2 * 512 if pt else 0))
     stream = torch.cuda.current_stream()
-    best = 0.0
-    for rnd in range(3):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(16)]
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(5e7))
-        for i, (e0, e1) in enumerate(evs):
-            l = i % layers.n
-            e0.record()
-            rc = lib.hbm_block_probe(layers.kcl[l].data_ptr(), layers.vcl[l].data_ptr(),
-                                     layers.ksl[l].data_ptr() if pt else None,
-                                     layers.vsl[l].data_ptr() if pt else None,
-                                     table.data_ptr(), per_wg, wgs, sink.data_ptr(), stream.cuda_stream)
-            e1.record()
-            if rc != 0:
-                return None
-        torch.cuda.synchronize()
-        ts = sorted(a.elapsed_time(b) for a, b in evs[2:])
-        best = max(best, nbytes / (ts[len(ts) // 2] * 1e-3) / 1e9)
-    return round(best, 1)
+
+    def rate(scales):
+        nbytes = len(tab) * (2 * 16384 + (2 * 512 if scales else 0))
+        best = 0.0
+        for rnd in range(3):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(16)]
+            torch.cuda.synchronize()
+            torch.cuda._sleep(int(5e7))
+            for i, (e0, e1) in enumerate(evs):
+                l = i % layers.n
+                e0.record()
+                rc = lib.hbm_block_probe(layers.kcl[l].data_ptr(), layers.vcl[l].data_ptr(),
+                                         layers.ksl[l].data_ptr() if scales else None,
+                                         layers.vsl[l].data_ptr() if scales else None,
+                                         table.data_ptr(), per_wg, wgs, sink.data_ptr(), stream.cuda_stream)
+                e1.record()
+                if rc != 0:
+                    return None
+            torch.cuda.synchronize()
+            ts = sorted(a.elapsed_time(b) for a, b in evs[2:])
+            best = max(best, nbytes / (ts[len(ts) // 2] * 1e-3) / 1e9)
+        return round(best, 1)
+
+    # with the scale pieces when the call reads them, and the K/V blocks alone
+    pt = w.mode == wl.PER_TOKEN
+    return rate(pt), (rate(False) if pt else None)
 
 
 def cpu_model():
@@ -710,7 +717,7 @@ def main():
         torch.cuda.synchronize()
 
     probe, probe_same = hbm_probe(dev, same_bytes=idx_bytes if index_topk else alg_bytes) or (None, None)
-    probe_blocks = None if index_topk else block_probe(layers, w)
+    probe_blocks, probe_blocks_kv = (None, None) if index_topk else (block_probe(layers, w) or (None, None))
     try:
         cpu = None if leg is None else leg.run(layers)
     finally:
@@ -762,6 +769,7 @@ def main():
             "hbm_read_probe_same_bytes_gbs": probe_same,
             "frac_of_same_bytes_probe": None if not probe_same else round(achieved / probe_same, 4),
             "block_read_probe_gbs": probe_blocks,
+            "block_read_probe_kv_only_gbs": probe_blocks_kv,
             "frac_of_block_probe": None if not probe_blocks else round(achieved / probe_blocks, 4),
         },
         "cpu_baseline": cpu,

@@ -316,3 +316,89 @@ def test_input_check_runs_the_decode_host_validation_first(over, status):
 def test_input_check_needs_a_report_buffer():
     assert _call_check(_decode_args(), None) == -1
     assert "report" in pa.pa_last_error()
+
+
+def _call_noalloc(t, **opts):
+    lib = pa.load()
+    d = [_lib.desc(t[k]) for k in ("q", "k", "v", "ks", "vs", "bt", "ctx", "cu", "sp")]
+    do = _lib.desc(t["out"])
+    o = _lib.PaDecodeOpts()
+    for k, v in opts.items():
+        setattr(o, k, v)
+    return lib.pa_decode_noalloc(*[_lib.ref(x) for x in d], t["mode"], _lib.ref(do), ctypes.byref(o), None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=_host_tensor((4, 16, 128), torch.float32)), -2),
+    (dict(k=_host_tensor((8, 1, 8192), torch.uint8)), -3),
+    (dict(ctx=_host_tensor((3,), torch.int32)), -3),
+    (dict(mode=5), -1),
+])
+def test_noalloc_runs_the_decode_host_validation(over, status):
+    assert _call_noalloc(_decode_args(**over)) == status
+    assert pa.pa_last_error()
+
+
+def test_noalloc_refusals_before_any_device_call():
+    # the in-kernel merge needs zeroed counters the fixed array does not keep
+    assert _call_noalloc(_decode_args(), force_parts=4, merge_mode=pa.MERGE_IN_KERNEL) == -5
+    assert "in-kernel merge" in pa.pa_last_error()
+    # 16384 one-row requests at 8 partitions: a scratch bucket above the 32 MiB array
+    T = 16384
+    t = _decode_args(q=_host_tensor((T, 16, 128), torch.bfloat16), out=_host_tensor((T, 16, 128), torch.bfloat16),
+                     bt=_host_tensor((T, 2), torch.int32), ctx=_host_tensor((T,), torch.int32))
+    assert _call_noalloc(t, force_parts=2) == -6
+    assert "pa_decode_noalloc" in pa.pa_last_error()
+    # a well-formed empty call passes every check and launches nothing
+    e = _decode_args(q=_host_tensor((0, 16, 128), torch.bfloat16), out=_host_tensor((0, 16, 128), torch.bfloat16))
+    assert _call_noalloc(e) == 0, pa.pa_last_error()
+
+
+def _norm_rope_call(T=3, with_q=True, **over):
+    lib = pa.load()
+    t = dict(
+        q=_host_tensor((T, 16, 128), torch.float32) if with_q else None,
+        q_out=_host_tensor((T, 16, 128), torch.bfloat16) if with_q else None,
+        k=_host_tensor((T, 1, 128), torch.float32), v=_host_tensor((T, 1, 128), torch.float32),
+        slots=_host_tensor((T,), torch.int64),
+        kc=_host_tensor((2, 1, 16384), torch.uint8), vc=_host_tensor((2, 1, 16384), torch.uint8),
+        ks=_host_tensor((2, 1, 128), torch.float32), vs=_host_tensor((2, 1, 128), torch.float32),
+        pos=_host_tensor((T,), torch.int64), cos=_host_tensor((64, 32), torch.float32),
+        sin=_host_tensor((64, 32), torch.float32), kw=_host_tensor((128,), torch.float32), qw=None,
+        rot=64, neox=1, eps=1e-6, off=1.0, nr=True)
+    t.update(over)
+    keep = [_lib.desc(t[k]) for k in ("pos", "cos", "sin", "kw", "qw")]
+    nr = _lib.PaNormRope()
+    nr.positions, nr.cos, nr.sin, nr.k_norm_weight, nr.q_norm_weight = [
+        None if x is None else ctypes.pointer(x) for x in keep]
+    nr.rotary_dim, nr.neox, nr.eps, nr.weight_offset = t["rot"], t["neox"], t["eps"], t["off"]
+    d = [_lib.desc(t[k]) for k in ("q", "q_out", "k", "v", "slots", "kc", "vc", "ks", "vs")]
+    return lib.kv_norm_rope_write(*[_lib.ref(x) for x in d], 2, ctypes.byref(nr) if t["nr"] else None, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(rot=6), -5),
+    (dict(rot=132), -5),
+    (dict(cos=_host_tensor((64, 16), torch.float32)), -3),
+    (dict(sin=_host_tensor((32, 32), torch.float32)), -3),
+    (dict(pos=_host_tensor((3,), torch.int32)), -3),
+    (dict(pos=_host_tensor((4,), torch.int64)), -3),
+    (dict(kw=_host_tensor((64,), torch.float32)), -3),
+    (dict(qw=_host_tensor((128,), torch.bfloat16)), -3),
+    (dict(eps=-1.0), -1),
+    (dict(eps=float("inf")), -1),
+    (dict(off=float("nan")), -1),
+    (dict(q_out=None), -1),
+    (dict(q=_host_tensor((3, 8, 128), torch.float32), q_out=_host_tensor((3, 8, 128), torch.bfloat16)), -3),
+    (dict(q_out=_host_tensor((3, 16, 128), torch.float32)), -2),
+    (dict(nr=False), -1),
+])
+def test_fused_writer_refuses_bad_arguments_before_launch(over, status):
+    assert _norm_rope_call(**over) == status
+    assert pa.pa_last_error()
+
+
+def test_fused_writer_accepts_well_formed_empty_calls():
+    assert _norm_rope_call(T=0) == 0, pa.pa_last_error()
+    # no rotation: the tables may be absent
+    assert _norm_rope_call(T=0, with_q=False, rot=0, cos=None, sin=None, kw=None) == 0, pa.pa_last_error()

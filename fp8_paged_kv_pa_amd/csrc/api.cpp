@@ -150,7 +150,7 @@ int get_scratch(hipStream_t stream, size_t need_counters, size_t need_partials, 
     return fail(PA_ERR_HIP, "hipMalloc of " + std::to_string(sz) + " bytes of split-K scratch failed");
   // counters must start at zero (never reached under capture: growth is refused there)
   if (hipMemsetAsync(fresh, 0, cnt, stream) != hipSuccess) {
-    hipFree(fresh);
+    (void)hipFree(fresh);
     return fail(PA_ERR_HIP, "clearing the split-K counters failed");
   }
   // The old arena is retired, not freed: work queued on the stream and any
@@ -726,19 +726,19 @@ int pa_release(void) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (g_arenas.empty() && g_retired.empty()) return PA_OK;
   int cur = 0;
-  hipGetDevice(&cur);
+  (void)hipGetDevice(&cur);
   int rc = PA_OK;
   std::vector<std::pair<int, void*>> all = g_retired;
   for (auto& kv : g_arenas)
     if (kv.second.ptr) all.emplace_back(kv.first.first, kv.second.ptr);
   for (auto& dp : all) {
-    hipSetDevice(dp.first);
+    (void)hipSetDevice(dp.first);
     if (hipDeviceSynchronize() != hipSuccess) rc = fail(PA_ERR_HIP, "hipDeviceSynchronize failed");
-    hipFree(dp.second);
+    (void)hipFree(dp.second);
   }
   g_arenas.clear();
   g_retired.clear();
-  hipSetDevice(cur);
+  (void)hipSetDevice(cur);
   return rc;
 }
 

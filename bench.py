@@ -1,8 +1,13 @@
 """Decode-attention benchmark on one MI355X.
 
-A step is one pass of the hot path over one batch: kv_quant_write of the
-step's new tokens (the last q_len tokens of every request), then pa_decode
-(main kernel, plus the log-sum-exp merge when the plan splits the context).
+A step is one pass of the hot path over one batch: the step's new tokens
+(the last q_len tokens of every request) are quantized and stored, and the
+decode attends the cache they were written to.  By default the step is one
+pa_decode_write call: the decode's main kernel writes the new tokens with
+kv_quant_write's code and attends them, plus the log-sum-exp merge kernel
+when the plan splits the context.  Block-sparse configs (their lists come
+from the indexer) and --separate-write run kv_quant_write, then
+pa_decode_ex (main kernel and merge).
 The default workload is the long-context shape: batch 32, q_len 1, one KV
 head x 16 query heads, head_dim 128, 128-token pages, context 131072 each
 (1024 pages per request), per-token e4m3 scales, block tables drawn from a
@@ -166,8 +171,21 @@ class Layers:
     workgroup_waves = 0
     merge_mode = 0
     partition_mode = 0
+    separate_write = False
 
     def step(self, l, ev=None, ev_index=None):
+        mq = self.max_q_len if self.cu is not None else 0
+        if self.sp is None and not self.index_topk and not self.separate_write:
+            # one decode step through pa_decode_write: the new tokens are
+            # written inside the decode launch where the library can
+            pa.pa_decode_write(self.q[l], self.step_k, self.step_v, self.step_slots[l], self.kcl[l],
+                               self.vcl[l], self.ksl[l], self.vsl[l], self.bt[l], self.ctx, self.cu, self.mode,
+                               self.out[l], max_q_len=mq, force_parts=self.force_parts,
+                               prefetch_depth=self.prefetch_depth, workgroup_waves=self.workgroup_waves,
+                               merge_mode=self.merge_mode, partition_mode=self.partition_mode,
+                               main_begin_event=None if ev is None else ev[0],
+                               main_end_event=None if ev is None else ev[1])
+            return
         pa.kv_quant_write(self.step_k, self.step_v, self.step_slots[l], self.kcl[l], self.vcl[l],
                           self.ksl[l], self.vsl[l], self.mode)
         sp = self.sp
@@ -229,7 +247,15 @@ def algorithmic_bytes(w):
 
 
 KERNEL_SOURCES = ("fp8_paged_kv_pa_amd/csrc/pa_decode.hip", "fp8_paged_kv_pa_amd/csrc/device_common.h",
-                  "fp8_paged_kv_pa_amd/csrc/launch.h")
+                  "fp8_paged_kv_pa_amd/csrc/launch.h", "fp8_paged_kv_pa_amd/csrc/writer_common.h")
+
+
+def write_in_decode(w, separate_write, index_topk):
+    """Whether a step's cache write runs inside the decode launch: dense FP8
+    calls through pa_decode_write with at most PA_FUSED_WRITE_MAX_Q_LEN
+    rows per request (16) and the default two-page ring."""
+    return (not separate_write and w.sparse is None and not index_topk and w.kv_dtype == "fp8"
+            and int(w.q_lens.max()) <= 16)
 
 
 def recorded_traffic(workload):
@@ -579,6 +605,8 @@ def main():
                     help="split-K merge: 0 the plan's, 1 separate kernel, 2 in the main kernel")
     ap.add_argument("--partition-mode", type=int, default=0,
                     help="split-K partitions: 0 the plan's, 1 fixed, 2 length-balanced")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="write the step's new tokens with kv_quant_write, then decode (two launches)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -619,6 +647,7 @@ def main():
     layers.workgroup_waves = args.workgroup_waves
     layers.merge_mode = args.merge_mode
     layers.partition_mode = args.partition_mode
+    layers.separate_write = args.separate_write
     plan = pa.pa_plan_describe(cfg)
     pa.pa_reserve(cfg, stream)
 
@@ -745,6 +774,8 @@ def main():
             "kv_dtype": w.kv_dtype,
             "scale_mode": ["none", "scalar", "per_token"][w.mode],
             "sparse_topk": 0 if w.sparse is None else int(w.sparse.shape[1]),
+            "write": "in_decode" if write_in_decode(w, args.separate_write, index_topk) and args.prefetch_depth <= 2
+                     else "separate",
             "layers_rotated": n_layers,
             "kv_bytes_per_step": int(kv_bytes),
             "plan": {k: int(v) for k, v in plan.items() if k in ("parts", "pages_per_part", "grid_x",

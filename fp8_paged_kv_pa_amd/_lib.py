@@ -112,7 +112,7 @@ class PaPlanInfo(ctypes.Structure):
     ]
 
 
-EXPORTS = ("pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_check_decode_inputs", "kv_quant_write",
+EXPORTS = ("pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_decode_write", "pa_check_decode_inputs", "kv_quant_write",
            "kv_norm_rope_write", "pa_index_topk", "pa_query_support", "pa_plan_describe", "pa_reserve", "pa_release", "pa_last_error")
 
 _lib = None
@@ -136,6 +136,8 @@ def load():
     lib.pa_decode_ex.restype = ctypes.c_int
     lib.pa_decode_noalloc.argtypes = [T, T, T, T, T, T, T, T, T, ctypes.c_int, T, P(PaDecodeOpts), vp]
     lib.pa_decode_noalloc.restype = ctypes.c_int
+    lib.pa_decode_write.argtypes = [T, T, T, T, T, T, T, T, T, T, T, ctypes.c_int, T, P(PaDecodeOpts), vp]
+    lib.pa_decode_write.restype = ctypes.c_int
     lib.pa_check_decode_inputs.argtypes = [T, T, T, T, T, T, T, T, T, ctypes.c_int, T, vp, vp]
     lib.pa_check_decode_inputs.restype = ctypes.c_int
     lib.kv_quant_write.argtypes = [T, T, T, T, T, T, T, ctypes.c_int, vp]

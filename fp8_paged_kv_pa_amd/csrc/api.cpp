@@ -175,8 +175,9 @@ int fixed_scratch(void** out);
 int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const pa_tensor* ks,
                 const pa_tensor* vs, const pa_tensor* bt, const pa_tensor* ctx, const pa_tensor* cu,
                 const pa_tensor* sp, int mode, const pa_tensor* out, const pa_decode_opts* opts,
-                void* stream_ptr, int32_t* check_report = nullptr, bool no_alloc = false) {
-  g_err.clear();
+                void* stream_ptr, int32_t* check_report = nullptr, bool no_alloc = false,
+                const WriteArgs* fuse = nullptr) {
+  if (!fuse) g_err.clear();
   int rc;
   if ((rc = check_tensor(q, "q"))) return rc;
   if (q->dtype != PA_DTYPE_BF16) return fail(PA_ERR_DTYPE, "q must be bfloat16");
@@ -255,6 +256,20 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   std::string perr;
   if ((rc = make_plan(cfg, &plan, &perr))) return fail(rc, perr);
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  // pa_decode_write: the new tokens are the query rows.  Dense FP8 calls
+  // with short requests write them inside the decode launch; the rest run
+  // the writer first.
+  bool fused = false;
+  if (fuse) {
+    if (fuse->tokens != rows)
+      return fail(PA_ERR_SHAPE, "k_new holds " + std::to_string(fuse->tokens) + " tokens but q holds " +
+                                    std::to_string(rows) + " rows: the new tokens are the query rows");
+    if (fuse->hkv != hkv) return fail(PA_ERR_SHAPE, "k_new and the cache differ in KV heads");
+    const int64_t lmax = ragged ? (opts ? opts->max_q_len : 0) : (B > 0 ? rows / B : 0);
+    // (the fused kernels take the two-page ring; a forced deeper ring runs unfused)
+    fused = !sparse && !bf16kv && lmax >= 1 && lmax <= PA_FUSED_WRITE_MAX_Q_LEN &&
+            !(opts && opts->prefetch_depth > 2);
+  }
   if (check_report) {
     // the device-side input check: the same host validation, then the check
     // kernel instead of the decode (no scratch, nothing written but the report)
@@ -346,11 +361,30 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   a.lrows = plan.lrows;
   float sm = (opts && opts->sm_scale != 0.0f) ? opts->sm_scale : 1.0f / std::sqrt(float(kDim));
   a.sm_log2 = sm * 1.4426950408889634f;
+  if (fused) {
+    a.fused = 1;
+    a.kn_bf16 = fuse->in_bf16;
+    a.k_new = fuse->k_new;
+    a.v_new = fuse->v_new;
+    a.kn_tok_stride = fuse->k_tok_stride;
+    a.kn_head_stride = fuse->k_head_stride;
+    a.vn_tok_stride = fuse->v_tok_stride;
+    a.vn_head_stride = fuse->v_head_stride;
+    a.slots = fuse->slots;
+    a.k_cache_w = fuse->k_cache;
+    a.v_cache_w = fuse->v_cache;
+    a.k_scale_w = fuse->k_scale;
+    a.v_scale_w = fuse->v_scale;
+  }
 
   hipEvent_t e0 = opts ? reinterpret_cast<hipEvent_t>(opts->main_begin_event) : nullptr;
   hipEvent_t e1 = opts ? reinterpret_cast<hipEvent_t>(opts->main_end_event) : nullptr;
   const int depth = (opts && opts->prefetch_depth > 0) ? opts->prefetch_depth : plan.depth;
   const int waves = (opts && opts->workgroup_waves > 0) ? opts->workgroup_waves : plan.waves;
+  if (fuse && !fused) {
+    hipError_t he = launch_write(*fuse, stream);
+    if (he != hipSuccess) return fail(PA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(he));
+  }
   hipError_t he = launch_decode(a, plan.grid, plan.merge, plan.sparse, depth, waves, e0, e1, stream);
   if (he != hipSuccess) return fail(PA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(he));
   return PA_OK;
@@ -436,10 +470,10 @@ int check_norm_rope(const pa_norm_rope* nr, const pa_tensor* q, pa_tensor* q_out
   return PA_OK;
 }
 
-int write_impl(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,
-               pa_tensor* k_cache, pa_tensor* v_cache, pa_tensor* k_scale, pa_tensor* v_scale, int scale_mode,
-               const pa_norm_rope* nr, const pa_tensor* q, pa_tensor* q_out, void* stream) {
-  g_err.clear();
+// Validates a writer call and fills its kernel block (nothing launched).
+int prepare_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,
+                  pa_tensor* k_cache, pa_tensor* v_cache, pa_tensor* k_scale, pa_tensor* v_scale, int scale_mode,
+                  const pa_norm_rope* nr, const pa_tensor* q, pa_tensor* q_out, WriteArgs* out) {
   int rc;
 
   if ((rc = check_tensor(k_new, "k_new"))) return rc;
@@ -474,10 +508,10 @@ int write_impl(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* 
   if ((rc = check_scales(k_scale, v_scale, scale_mode, nb, hkv))) return rc;
   NormRopeArgs nra{};
   if (nr && (rc = check_norm_rope(nr, q, q_out, T, hkv, &nra))) return rc;
-  if (T == 0) return PA_OK;
   if (T * (hkv + nra.hq) > kMaxGrid) return fail(PA_ERR_CAPACITY, "too many (token, head) pairs for one launch");
 
-  WriteArgs a{};
+  WriteArgs& a = *out;
+  a = WriteArgs{};
   a.k_new = k_new->data;
   a.v_new = v_new->data;
   a.k_tok_stride = k_new->stride[0];
@@ -496,6 +530,19 @@ int write_impl(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* 
   a.hkv = int32_t(hkv);
   a.scale_mode = scale_mode;
   a.nr = nra;
+  return PA_OK;
+}
+
+int write_impl(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,
+               pa_tensor* k_cache, pa_tensor* v_cache, pa_tensor* k_scale, pa_tensor* v_scale, int scale_mode,
+               const pa_norm_rope* nr, const pa_tensor* q, pa_tensor* q_out, void* stream) {
+  g_err.clear();
+  WriteArgs a;
+  int rc;
+  if ((rc = prepare_write(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, scale_mode, nr, q, q_out,
+                          &a)))
+    return rc;
+  if (a.tokens == 0) return PA_OK;
   hipError_t he = launch_write(a, reinterpret_cast<hipStream_t>(stream));
   if (he != hipSuccess) return fail(PA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(he));
   return PA_OK;
@@ -574,6 +621,21 @@ int pa_check_decode_inputs(const pa_tensor* q, const pa_tensor* k_cache, const p
   if (!report) return fail(PA_ERR_INVALID_ARG, "report must be a device int32[16] buffer");
   return decode_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, cu_seqlens_q,
                      sparse_page_idx, scale_mode, out, nullptr, stream, report);
+}
+
+int pa_decode_write(const pa_tensor* q, const pa_tensor* k_new, const pa_tensor* v_new,
+                    const pa_tensor* slot_mapping, pa_tensor* k_cache, pa_tensor* v_cache, pa_tensor* k_scale,
+                    pa_tensor* v_scale, const pa_tensor* block_table, const pa_tensor* context_lens,
+                    const pa_tensor* cu_seqlens_q, int scale_mode, pa_tensor* out, const pa_decode_opts* opts,
+                    void* stream) {
+  g_err.clear();
+  WriteArgs w;
+  int rc;
+  if ((rc = prepare_write(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, scale_mode, nullptr,
+                          nullptr, nullptr, &w)))
+    return rc;
+  return decode_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, cu_seqlens_q, nullptr,
+                     scale_mode, out, opts, stream, nullptr, false, &w);
 }
 
 int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,

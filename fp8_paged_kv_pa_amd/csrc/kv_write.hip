@@ -9,7 +9,9 @@
 // the scale modes of vllm-project/vllm pull request 52060 ("Suggested
 // Fix").  It is the only cache writer of the library (ROCm/ATOM pull request
 // 2710 review, "Smaller": one shared writer so the FP8 and non-FP8 branches
-// cannot drift), so the unquantized bf16 cache is written here too.
+// cannot drift), so the unquantized bf16 cache is written here too.  Its
+// per-token load, quantization and FP8 store live in writer_common.h, which
+// the decode kernel's fused write (pa_decode_write) calls as well.
 //
 // The fused variant (kv_norm_rope_write) applies the key's RMS norm and
 // rotary embedding to K in registers before the same quantize-and-store
@@ -22,49 +24,13 @@
 // scales it writes are reproducible bit for bit.
 #include "device_common.h"
 #include "launch.h"
+#include "writer_common.h"
 
 namespace fp8pa {
 
 namespace {
 
 constexpr int kWriteWaves = 4;
-
-__device__ __forceinline__ void load_pair(const void* base, int64_t off, int bf16, float* x0,
-                                          float* x1) {
-  if (bf16) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(
-        reinterpret_cast<const uint16_t*>(base) + off);
-    *x0 = __uint_as_float(w << 16);
-    *x1 = __uint_as_float(w & 0xFFFF0000u);
-  } else {
-    const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(base) + off);
-    *x0 = v.x;
-    *x1 = v.y;
-  }
-}
-
-// Quantize this lane's two values of one 128-wide row.  Returns the two
-// codes (low byte = even dim) and, through *scale_out, the stored scale.
-__device__ __forceinline__ uint32_t quantize_pair(float x0, float x1, int mode, const float* scalar,
-                                                  float* scale_out) {
-  float s = 1.0f;
-  bool divide = false;
-  if (mode == PA_SCALE_PER_TOKEN) {
-    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-    s = amax / 448.0f;  // IEEE fp32 division
-    divide = s != 0.0f;
-  } else if (mode == PA_SCALE_SCALAR) {
-    s = *scalar;
-    divide = true;
-  }
-  float y0 = x0, y1 = x1;
-  if (divide) {
-    y0 = x0 / s;
-    y1 = x1 / s;
-  }
-  *scale_out = s;
-  return f32_to_e4m3(y0) | (f32_to_e4m3(y1) << 8);
-}
 
 // fp32 -> bf16 bits: round to nearest, ties to even, on the 16 dropped
 // bits; NaN stays NaN (quiet bit set, sign kept).  Integer work, so the
@@ -221,32 +187,7 @@ __global__ __launch_bounds__(kWave * kWriteWaves) void kv_write_kernel(WriteArgs
   const uint32_t kc = quantize_pair(k0, k1, a.scale_mode, a.k_scale, &ks);
   const uint32_t vc = quantize_pair(v0, v1, a.scale_mode, a.v_scale, &vs);
 
-  const int64_t blk = (page * a.hkv + h) * int64_t(16384);
-  const int c = o >> 5, tau = (o >> 4) & 1;
-
-  // K: dims d = 2*lane, 2*lane+1 share one 8-byte run (u even, u+1).
-  {
-    const int d = 2 * lane;
-    const int j = d >> 5, g = (d >> 3) & 3, u = d & 7, r = o & 15;
-    const int off = 4096 * c + 1024 * (2 * tau + (j >> 1)) + 16 * (16 * g + r) + 8 * (j & 1) + u;
-    *reinterpret_cast<uint16_t*>(a.k_cache + blk + off) = uint16_t(kc);
-  }
-  // V: each dim goes to a different 16-byte piece.
-  {
-    const int w = o & 15, g = w >> 2, e = 4 * tau + (w & 3);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int d = 2 * lane + s;
-      const int delta = d >> 4, r = d & 15;
-      const int off = 4096 * c + 1024 * (delta >> 1) + 16 * (16 * g + r) + 8 * (delta & 1) + e;
-      a.v_cache[blk + off] = uint8_t(vc >> (8 * s));
-    }
-  }
-  if (a.scale_mode == PA_SCALE_PER_TOKEN && lane == 0) {
-    const int64_t si = (page * a.hkv + h) * 128 + o;
-    a.k_scale[si] = ks;
-    a.v_scale[si] = vs;
-  }
+  store_token_fp8(a.k_cache, a.v_cache, a.k_scale, a.v_scale, a.hkv, a.scale_mode, slot, h, lane, kc, vc, ks, vs);
 }
 
 }  // namespace

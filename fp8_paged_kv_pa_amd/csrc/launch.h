@@ -51,6 +51,23 @@ struct DecodeArgs {
   int32_t nslot;              // balanced: partition slots per (KV head, row group)
   int32_t lrows;              // balanced: rows per request held by a slot's partials
   float sm_log2;              // sm_scale * log2(e)
+  // Fused write (pa_decode_write): query row t's own new token k_new[t],
+  // v_new[t] sits at position ctx - L + i of its request (i = t - start).
+  // The main loop attends only the older positions; the workgroups of the
+  // partition holding the request's last position quantize the new tokens
+  // with the writer's code, attend them from registers, and (row group 0)
+  // store them at slots[t].
+  int32_t fused;
+  int32_t kn_bf16;            // 1: k_new/v_new are bf16, 0: f32
+  const void* k_new;          // [rows, Hkv, 128]
+  const void* v_new;
+  int64_t kn_tok_stride, kn_head_stride;  // elements
+  int64_t vn_tok_stride, vn_head_stride;
+  const int64_t* slots;       // [rows]
+  uint8_t* k_cache_w;         // the same caches and scales, written
+  uint8_t* v_cache_w;
+  float* k_scale_w;
+  float* v_scale_w;
 };
 
 // The key norm and rotary embedding the fused writer applies before the

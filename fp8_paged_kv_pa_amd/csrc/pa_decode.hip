@@ -36,6 +36,7 @@
 #include <hip/hip_ext.h>
 
 #include "device_common.h"
+#include "writer_common.h"
 #include "launch.h"
 
 namespace fp8pa {
@@ -368,10 +369,11 @@ __device__ __forceinline__ void xcd_group_of(const DecodeArgs& a, uint32_t* q, i
   }
 }
 
-template <int RT, bool PER_TOKEN, bool SPARSE, int NBUF, int NW, bool BF>
+template <int RT, bool PER_TOKEN, bool SPARSE, int NBUF, int NW, bool BF, bool FW>
 __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, BF>)) void pa_decode_main(
     DecodeArgs a) {
   static_assert(!(BF && PER_TOKEN), "a bf16 cache carries no scales");
+  static_assert(!FW || (!SPARSE && !BF), "the fused write serves dense FP8 calls");
   static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
   static_assert(NW * 16 * kAccPad >= 16 * kMaxMergeParts, "merge weights reuse the wave-merge LDS");
   __shared__ float sm_ml[NW][RT][16][2];
@@ -444,7 +446,8 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   // any branch, so they cost one memory round trip.
   const int n0 = part * ppp;  // < width (dense) or < topk (sparse) by construction of the grid
   const int s0 = n0 + ps;       // this wave's first list position
-  int h, b, row0, nrows, lim0;  // row row0+i sees tokens t < lim0 + i
+  int h, b, row0, nrows, lim0;  // row row0+i sees tokens t < lim0 + i (fused write: t < lim0)
+  int fz_start = 0, fz_L = 0, fz_ctx = 0, fz_i0 = 0;  // request rows, length, context; group's first row
   int first_entry;              // dense: block_table[b][s0]; sparse: sparse_idx[row0][s0] (-1 past the end)
   int second_entry = -1;        // dense: block_table[b][s0 + S], read with the first
   if constexpr (SPARSE) {
@@ -490,8 +493,34 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     if (i0 >= L) return;  // this request has no rows in this group
     nrows = min(RT, L - i0);
     row0 = start + i0;
-    lim0 = ctx - L + i0 + 1;
+    // with the fused write every row of the main loop sees only the older
+    // positions; the request's new tokens are attended separately
+    lim0 = FW ? ctx - L : ctx - L + i0 + 1;
+    fz_start = start;
+    fz_L = L;
+    fz_ctx = ctx;
+    fz_i0 = i0;
   }
+  // Fused write: the partition holding the request's last attended position
+  // takes the new tokens.  Each wave's first new token is loaded ahead of
+  // the page stream, so it has arrived by the time the wave handles it,
+  // under the first pages' latency.
+  bool fz_last = false;
+  float fk0 = 0.f, fk1 = 0.f, fv0 = 0.f, fv1 = 0.f;
+  int64_t fslot = -1;
+  if constexpr (FW) {
+    const int ctx_cap = min(fz_ctx, a.width * 128);
+    const int pl = (ctx_cap - 1) >> 7;
+    fz_last = ctx_cap > 0 && n0 <= pl && pl < n0 + ppp;
+    if (fz_last && wave < fz_L) {
+      const int64_t t = fz_start + wave;
+      load_pair(a.k_new, t * a.kn_tok_stride + h * a.kn_head_stride + 2 * lane, a.kn_bf16, &fk0, &fk1);
+      load_pair(a.v_new, t * a.vn_tok_stride + h * a.vn_head_stride + 2 * lane, a.kn_bf16, &fv0, &fv1);
+      fslot = a.slots[t];
+    }
+  }
+  const bool fz_pend = fz_last && wave < fz_L;  // this wave has a first new token
+
   // The partition's first chunk and the query operands do not depend on the
   // context length: issue their loads now, so they travel together with the
   // context-length read instead of after it (masking handles the rest).
@@ -526,8 +555,9 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   }
 
   const int cap = a.width * 128;
+  const int rstep = FW ? 0 : 1;  // cutoff step from one row to the next
   const int lim_min = max(0, min(lim0, cap));
-  const int lim_max = max(0, min(lim0 + nrows - 1, cap));
+  const int lim_max = max(0, min(lim0 + (nrows - 1) * rstep, cap));
 
   int n1;
   if constexpr (SPARSE) {
@@ -540,7 +570,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   // all rows, or (balanced) slot-major over the rows of one request
   const bool to_partial = a.balanced || a.parts > 1;
   const int64_t prow0 = a.balanced ? int64_t(bal_slot) * a.lrows + bal_gi * RT : int64_t(part) * a.rows + row0;
-  if (n0 >= n1 && to_partial) {
+  if (n0 >= n1 && to_partial && !fz_last) {
     // nothing to attend in this partition: leave an empty partial (weight 0)
     // so the merge can read every partition without knowing the context
     if (threadIdx.x < 16 * nrows) {
@@ -712,7 +742,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
         x[e] = fmaf(st[r][0][e], kc[e], -mu);
         x[4 + e] = fmaf(st[r][1][e], kc[4 + e], -mu);
       }
-      const int lim_r = min(lim0 + min(r, nrows - 1), cap);
+      const int lim_r = min(lim0 + min(r, nrows - 1) * rstep, cap);
       if (!full) {
         keep_branch();
 #pragma unroll
@@ -785,6 +815,84 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     if constexpr (RT == 2) __builtin_amdgcn_s_setprio(0);
   };
 
+  // ---- the request's new tokens (fused write) -------------------------------
+  // Wave w takes new tokens w, w + NW, ...: it quantizes the token's K and V
+  // rows exactly as kv_quant_write does (writer_common.h), stores them when
+  // this is row group 0 (one store per token), and folds the token into its
+  // own (max, sum, accumulators) for the rows that see it -- row i of the
+  // request sees new tokens 0..i.  The dequantized codes go through this
+  // wave's LDS rows (untouched until the epilogue) from the writer's layout
+  // (two dims per lane) to the score layout (the query operand's dims) and
+  // the accumulator layout, a few values at a time.  Scores and weights are
+  // fp32: the token's K scale multiplies its score, its V scale its weight,
+  // as in the page stream.  It runs after the page stream: inside its first
+  // step (under that step's loads) the one-row kernel measured 11-14 us
+  // slower at 128K, and the two-row kernel has no registers to spare there.
+  auto new_token = [&](int j, float k0, float k1, float v0, float v1, int64_t slot) {
+    if constexpr (FW) {
+      float* lds = &sm_acc[wave][0][0];  // 256 floats: the K codes' values, then V's
+      float ks_t, vs_t;
+      const uint32_t kcode = quantize_pair(k0, k1, a.scale_mode, a.k_scale, &ks_t);
+      const uint32_t vcode = quantize_pair(v0, v1, a.scale_mode, a.v_scale, &vs_t);
+      if (fz_i0 == 0 && slot >= 0 && slot < a.num_blocks * 128)
+        store_token_fp8(a.k_cache_w, a.v_cache_w, a.k_scale_w, a.v_scale_w, a.hkv, a.scale_mode, slot, h, lane,
+                        kcode, vcode, ks_t, vs_t);
+      const int pos = fz_ctx - fz_L + j;
+      if (pos < 0 || pos >= cap) return;  // not attended (uniform)
+      const bf16x2 kb = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kcode, 1.0f, false);
+      const bf16x2 vb = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vcode, 1.0f, false);
+      // the previous token's reads of these rows are done before they change
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      *reinterpret_cast<float2*>(lds + 2 * lane) = float2{float(kb[0]), float(kb[1])};
+      *reinterpret_cast<float2*>(lds + 128 + 2 * lane) = float2{float(vb[0]), float(vb[1])};
+      // the wave's LDS writes complete before any lane reads another's
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const float kcf = PER_TOKEN ? ks_t * k_fold : k_fold;
+      const float vsf = PER_TOKEN ? vs_t : 1.0f;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        if (r >= nrows || j > fz_i0 + r) continue;  // uniform: this row does not see token j
+        float s = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 lo4 = *reinterpret_cast<const f32x4*>(lds + 32 * jj + 8 * g);
+          const f32x4 hi4 = *reinterpret_cast<const f32x4*>(lds + 32 * jj + 8 * g + 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            s = fmaf(float(qop[r][jj][i]), lo4[i], s);
+            s = fmaf(float(qop[r][jj][4 + i]), hi4[i], s);
+          }
+        }
+        s += __shfl_xor(s, 16, kWave);  // the head's four lane groups hold its 128 dims
+        s += __shfl_xor(s, 32, kWave);
+        const float sc = s * kcf;  // log2-domain score, equal in the head's four lanes
+        // raise the running max as the page stream does: lazily, so p <= 2^8
+        const bool raise = m_run[r] == -INFINITY || sc - m_run[r] > kLazyMax;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+          const float mn = raise ? fmaxf(m_run[r], sc) : m_run[r];
+          const float alpha = (m_run[r] == -INFINITY || !raise) ? 1.0f : __builtin_amdgcn_exp2f(m_run[r] - mn);
+          l_run[r] *= alpha;
+#pragma unroll
+          for (int d = 0; d < 8; ++d) acc[r][d] *= alpha;
+          m_run[r] = mn;
+        }
+        const float p = __builtin_amdgcn_exp2f(sc - m_run[r]);
+        if (g == 0) l_run[r] += p;  // the epilogue sums l over the four lane groups
+        const float pw = p * vsf;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const f32x4 v4 = *reinterpret_cast<const f32x4*>(lds + 128 + 16 * d + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[r][d][e] = fmaf(pw, v4[e], acc[r][d][e]);
+        }
+      }
+    }
+  };
+
   // ---- stream the partition's pages: a ring of NBUF chunk buffers, the
   // loads of the next NBUF-1 pages in flight while one is processed.  Table
   // entries are read one step ahead of their use. -------------------------
@@ -822,6 +930,19 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
         P_next = raw_at(nl + S, ln_next);
         ln_after = logical_at(nl + 2 * S);
         process(buf[k], tb[k]);
+      }
+    }
+  }
+
+  if constexpr (FW) {
+    if (fz_pend) new_token(wave, fk0, fk1, fv0, fv1, fslot);
+    if (fz_last) {
+      for (int j = wave + NW; j < fz_L; j += NW) {
+        const int64_t t = fz_start + j;
+        float k0, k1, v0, v1;
+        load_pair(a.k_new, t * a.kn_tok_stride + h * a.kn_head_stride + 2 * lane, a.kn_bf16, &k0, &k1);
+        load_pair(a.v_new, t * a.vn_tok_stride + h * a.vn_head_stride + 2 * lane, a.kn_bf16, &v0, &v1);
+        new_token(j, k0, k1, v0, v1, a.slots[t]);
       }
     }
   }
@@ -1030,13 +1151,13 @@ __global__ __launch_bounds__(4 * kWave) void pa_merge(DecodeArgs a) {
 
 // With events, the dispatch itself records them (start and end of this
 // kernel), so the measured time is the kernel's own, without marker packets.
-template <int RT, bool PT, bool SP, int NB, int NW, bool BF>
+template <int RT, bool PT, bool SP, int NB, int NW, bool BF, bool FW = false>
 void launch_main_t(const DecodeArgs& a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (e0 || e1)
-    hipExtLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB, NW, BF>), dim3(uint32_t(grid)), dim3(kWave * NW),
+    hipExtLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB, NW, BF, FW>), dim3(uint32_t(grid)), dim3(kWave * NW),
                           0, s, e0, e1, 0, a);
   else
-    hipLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB, NW, BF>), dim3(uint32_t(grid)), dim3(kWave * NW), 0,
+    hipLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB, NW, BF, FW>), dim3(uint32_t(grid)), dim3(kWave * NW), 0,
                        s, a);
 }
 
@@ -1047,6 +1168,13 @@ void launch_main_t(const DecodeArgs& a, int64_t grid, hipStream_t s, hipEvent_t 
 template <int RT, bool PT, bool SP, bool BF = false>
 void launch_shape(const DecodeArgs& a, int depth, int waves, int64_t grid, hipStream_t s, hipEvent_t e0,
                   hipEvent_t e1) {
+  if constexpr (!SP && !BF) {
+    // the fused write: the two-page ring at either width
+    if (a.fused) {
+      if (waves == 8) return launch_main_t<RT, PT, SP, 2, 8, BF, true>(a, grid, s, e0, e1);
+      return launch_main_t<RT, PT, SP, 2, 4, BF, true>(a, grid, s, e0, e1);
+    }
+  }
   if constexpr (BF && RT == 2) {
     launch_main_t<RT, PT, SP, 2, 4, BF>(a, grid, s, e0, e1);
   } else {

@@ -349,6 +349,44 @@ int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new,
                    pa_tensor* k_scale, pa_tensor* v_scale, int scale_mode, void* stream);
 
 /*
+ * pa_decode_write -- one decode step: kv_quant_write of the step's new
+ * tokens followed by pa_decode_ex over the cache they were written to, with
+ * the write done inside the decode launch (one launch fewer per step).  The
+ * cache write is the writer's own code ([ATOM-2710] review "Smaller": one
+ * shared writer), so the bytes and scales stored are exactly those of
+ * kv_quant_write; the attention is that of the decode contract over the
+ * written cache ([ATOM-2614] "Change"), within the decode's tolerance.
+ *
+ * Arguments: those of pa_decode_ex without sparse_page_idx, plus k_new,
+ * v_new, slot_mapping as in kv_quant_write, with T == rows:
+ *   token t is query row t's own token; row i of request b (rows
+ *   cu[b] .. cu[b+1]-1, or the uniform split) sits at position
+ *   context_lens[b] - L_b + i, and slot_mapping[t] must be the cache slot
+ *   of that position through block_table (block_table[b][pos/128]*128 +
+ *   pos%128, >= 0).  context_lens counts the new tokens.
+ *   k_cache, v_cache, k_scale, v_scale are written (as kv_quant_write) and
+ *   read (as pa_decode).
+ * Behaviour: dense FP8 calls (PER_TOKEN, SCALAR or NONE) whose requests hold
+ * at most PA_FUSED_WRITE_MAX_Q_LEN rows (uniform split, or max_q_len given
+ * in opts for a ragged call) run as one decode launch (plus the merge when
+ * split): the workgroups of each request's last partition quantize its new
+ * tokens, row group 0 stores them, and every row attends them from
+ * registers while the page stream covers the older positions.  Every other
+ * call (a bf16 cache, longer or unknown q_len) runs kv_quant_write and then
+ * pa_decode_ex, with the same results.  Errors: everything the two calls
+ * check, plus T != rows (PA_ERR_SHAPE), all before any launch.  Slot
+ * preconditions that only device memory shows are the caller's: a slot
+ * that does not match its position gives a cache and an output that differ
+ * from the two separate calls.  Asynchronous on `stream`.
+ */
+#define PA_FUSED_WRITE_MAX_Q_LEN 16
+int pa_decode_write(const pa_tensor* q, const pa_tensor* k_new, const pa_tensor* v_new,
+                    const pa_tensor* slot_mapping, pa_tensor* k_cache, pa_tensor* v_cache,
+                    pa_tensor* k_scale, pa_tensor* v_scale, const pa_tensor* block_table,
+                    const pa_tensor* context_lens, const pa_tensor* cu_seqlens_q, int scale_mode,
+                    pa_tensor* out, const pa_decode_opts* opts, void* stream);
+
+/*
  * kv_norm_rope_write -- kv_quant_write fused with the key's RMS norm and
  * rotary position embedding, and the same transform of the query in the
  * same launch ([ATOM-2710] "Changes": query/key norm, rotary embedding and

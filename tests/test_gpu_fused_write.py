@@ -1,0 +1,194 @@
+"""GPU parity of pa_decode_write, one decode step with the cache write done
+inside the decode launch.
+
+Each case starts from a cache in which every token of every request is
+written by kv_quant_write except the step's own new tokens (the last q_len
+positions of each request), whose bytes and scales hold poison.  After
+pa_decode_write:
+  - the whole cache (codes and scale bits) equals, bit for bit, the cache
+    kv_quant_write leaves when it writes every token, and the oracle
+    writer's cache;
+  - the output matches the fp64 oracle over the fully written cache, to the
+    decode tolerance (max|err| <= 1e-2 where |ref| < 4, 2^-7|ref| above,
+    cosine >= 0.9999), and the separate writer + decode calls to 4e-3.
+The cases cover one-row and two-row workgroups, uniform, odd and ragged
+q_len, new tokens across a page boundary, requests made only of new tokens,
+the scalar and no-scale modes, two KV heads, bf16 inputs, forced and
+balanced partitions, the in-kernel merge, more new tokens than waves, and
+the calls that run unfused (q_len above the fused limit, a bf16 cache)."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_paged_kv_pa_amd as pa
+import workloads as wl
+from oracle import layout as olay
+
+from harness import GpuCase, compare, oracle_cache, oracle_out, poison_arrays
+from oracle import writer as owr
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    dict(seed=401, ctx=[300, 513], q_lens=[1, 1]),                              # one-row, two tails
+    dict(seed=402, ctx=[700, 1300, 256], q_lens=[4, 4, 4]),                     # two-row, uniform q_len 4
+    dict(seed=403, ctx=[260, 129], q_lens=[3, 3]),                              # odd q_len; new tokens cross a page
+    dict(seed=404, ctx=[800, 500, 300, 90], q_lens=[4, 1, 6, 2], ragged=True),  # ragged
+    dict(seed=405, ctx=[4, 1, 2], q_lens=[4, 1, 2], ragged=True),               # only new tokens
+    dict(seed=406, ctx=[1500, 800], q_lens=[1, 1], mode=wl.SCALAR),
+    dict(seed=407, ctx=[640, 129], q_lens=[2, 2], mode=wl.NONE),
+    dict(seed=408, ctx=[400, 131], q_lens=[2, 2], Hkv=2),
+    dict(seed=409, ctx=[600, 2000], q_lens=[16, 16]),                           # more new tokens than waves
+]
+
+
+def _new_token_poison(case, w, slots):
+    """Poison the new tokens' codes and scales in the GPU cache (they are
+    written by the call under test)."""
+    kc = case.kc.view(torch.uint8).view(-1)
+    vc = case.vc.view(torch.uint8).view(-1)
+    kidx, vidx, sidx = [], [], []
+    d = np.arange(128)
+    for s in slots:
+        page, o = divmod(int(s), 128)
+        for h in range(w.Hkv):
+            base = (page * w.Hkv + h) * 16384
+            kidx.append(base + olay.k_offset(o, d))
+            vidx.append(base + olay.v_offset(o, d))
+            sidx.append((page * w.Hkv + h) * 128 + o)
+    dev = kc.device
+    kidx = torch.from_numpy(np.concatenate(kidx).astype(np.int64)).to(dev)
+    vidx = torch.from_numpy(np.concatenate(vidx).astype(np.int64)).to(dev)
+    kc[kidx] = 0x5A
+    vc[vidx] = 0x3C
+    if w.mode == wl.PER_TOKEN:
+        sidx = torch.from_numpy(np.asarray(sidx, np.int64)).to(dev)
+        case.ks.view(-1)[sidx] = 1e3
+        case.vs.view(-1)[sidx] = 1e3
+
+
+def _oracle_cache_bf16_inputs(w):
+    """The oracle writer's cache when the K/V inputs are bf16 (each value
+    rounded to bf16 before quantization, as the GPU call receives them)."""
+    kc, vc, ks, vs = poison_arrays(w)
+    ks_in = np.array([w.k_scalar], np.float32)
+    vs_in = np.array([w.v_scalar], np.float32)
+    for b in range(w.B):
+        k, v, s = w.request_kv(b)
+        k, v = wl.bf16_round(k), wl.bf16_round(v)
+        if w.mode == wl.SCALAR:
+            owr.quant_write_ref(k, v, s, kc, vc, ks_in, vs_in, w.mode, w.Hkv)
+        else:
+            owr.quant_write_ref(k, v, s, kc, vc, ks, vs, w.mode, w.Hkv)
+    ksa, vsa = (ks_in, vs_in) if w.mode == wl.SCALAR else ((None, None) if w.mode == wl.NONE else (ks, vs))
+    return kc, vc, ks, vs, ksa, vsa
+
+
+def _snapshot(case):
+    snap = [case.kc.view(torch.uint8).clone(), case.vc.view(torch.uint8).clone()]
+    if case.ks is not None:
+        snap += [case.ks.view(torch.int32).clone(), case.vs.view(torch.int32).clone()]
+    return snap
+
+
+def _run(case, w, k, v, slots, out, **kw):
+    mq = int(w.q_lens.max()) if w.cu is not None else 0
+    pa.pa_decode_write(case.q, k, v, slots, case.kc, case.vc, case.ks_arg, case.vs_arg, case.bt, case.ctx,
+                       case.cu, case.mode, out, max_q_len=mq, **kw)
+    return out
+
+
+def _check_step(w, in_dtype=torch.float32, what="", runs=({},)):
+    case = GpuCase(w, in_dtype=in_dtype)
+    full = _snapshot(case)  # every token written by kv_quant_write
+    ref_sep = case.decode(out=torch.empty_like(case.out),
+                          max_q_len=int(w.q_lens.max()) if w.cu is not None else 0)
+    torch.cuda.synchronize()
+    ocache = _oracle_cache_bf16_inputs(w) if in_dtype == torch.bfloat16 else oracle_cache(w)
+    ref64 = oracle_out(w, cache=ocache)
+    k, v, s = w.step_tokens()
+    kt = torch.from_numpy(k).to(case.dev).to(in_dtype)
+    vt = torch.from_numpy(v).to(case.dev).to(in_dtype)
+    st = torch.from_numpy(s).to(case.dev)
+    for kw in runs:
+        tag = f"{what} {kw}"
+        print("fused write case", w.name, tag, flush=True)
+        _new_token_poison(case, w, s)
+        torch.cuda.synchronize()
+        out = _run(case, w, kt, vt, st, torch.empty_like(case.out), **kw)
+        torch.cuda.synchronize()
+        after = _snapshot(case)
+        for a, b, name in zip(after, full, ("k codes", "v codes", "k scales", "v scales")):
+            assert torch.equal(a, b), f"{tag}: {name} differ from kv_quant_write's"
+        # and from the oracle writer's (codes and scale bits)
+        assert np.array_equal(after[0].cpu().numpy().reshape(-1), ocache[0].reshape(-1)), f"{tag}: K vs oracle"
+        assert np.array_equal(after[1].cpu().numpy().reshape(-1), ocache[1].reshape(-1)), f"{tag}: V vs oracle"
+        if w.mode == wl.PER_TOKEN:
+            assert np.array_equal(after[2].cpu().numpy().reshape(-1), ocache[2].view(np.int32).reshape(-1))
+            assert np.array_equal(after[3].cpu().numpy().reshape(-1), ocache[3].view(np.int32).reshape(-1))
+        compare(out, ref64, what=f"{tag} vs oracle")
+        compare(out, ref_sep.float().cpu().numpy(), atol=4e-3, cos_min=0.99999, what=f"{tag} vs separate calls")
+
+
+@pytest.mark.parametrize("kw", CASES, ids=[str(c["seed"]) for c in CASES])
+def test_fused_write_step(kw):
+    w = wl.small_case(**kw)
+    runs = [{}, dict(force_parts=1), dict(force_parts=3), dict(force_parts=8),
+            dict(partition_mode=pa.PARTITION_BALANCED), dict(merge_mode=pa.MERGE_IN_KERNEL, force_parts=3)]
+    _check_step(w, runs=runs, what=w.name)
+
+
+def test_fused_write_bf16_inputs_and_widths():
+    w = wl.small_case(seed=410, ctx=[900, 333, 128], q_lens=[2, 2, 2])
+    _check_step(w, in_dtype=torch.bfloat16, what="bf16 inputs",
+                runs=({}, dict(workgroup_waves=4), dict(workgroup_waves=8), dict(force_parts=5)))
+
+
+def test_unfused_fallbacks():
+    # q_len above the fused limit, and a forced deeper ring: writer + decode
+    w = wl.small_case(seed=411, ctx=[700, 300], q_lens=[17, 17])
+    _check_step(w, what="q_len 17", runs=({}, dict(force_parts=2)))
+    w = wl.small_case(seed=412, ctx=[700, 300], q_lens=[1, 1])
+    _check_step(w, what="depth 3", runs=(dict(prefetch_depth=3),))
+
+
+def test_unfused_bf16_cache():
+    w = wl.bf16_kv(wl.small_case(seed=413, ctx=[500, 260], q_lens=[2, 2]))
+    case = GpuCase(w)
+    ref_sep = case.decode(out=torch.empty_like(case.out))
+    torch.cuda.synchronize()
+    full = [case.kc.view(torch.int16).clone(), case.vc.view(torch.int16).clone()]
+    k, v, s = w.step_tokens()
+    kt = torch.from_numpy(k).to(case.dev)
+    vt = torch.from_numpy(v).to(case.dev)
+    st = torch.from_numpy(s).to(case.dev)
+    # overwrite the new tokens' elements with a pattern, then write them back through the call
+    for s1 in s:
+        page, o = divmod(int(s1), 128)
+        for h in range(w.Hkv):
+            base = (page * w.Hkv + h) * 16384
+            idx = torch.from_numpy((base + olay.k_offset_bf16(o, np.arange(128))).astype(np.int64)).to(case.dev)
+            case.kc.view(torch.int16).view(-1)[idx] = 0x1234
+            idx = torch.from_numpy((base + olay.v_offset_bf16(o, np.arange(128))).astype(np.int64)).to(case.dev)
+            case.vc.view(torch.int16).view(-1)[idx] = 0x1234
+    out = _run(case, w, kt, vt, st, torch.empty_like(case.out))
+    torch.cuda.synchronize()
+    assert torch.equal(case.kc.view(torch.int16), full[0]) and torch.equal(case.vc.view(torch.int16), full[1])
+    compare(out, oracle_out(w), what="bf16 cache vs oracle")
+    compare(out, ref_sep.float().cpu().numpy(), atol=4e-3, cos_min=0.99999, what="bf16 cache vs separate")
+
+
+def test_fused_write_refuses_before_launch():
+    w = wl.small_case(seed=414, ctx=[300], q_lens=[2])
+    case = GpuCase(w)
+    k, v, s = w.step_tokens()
+    kt = torch.from_numpy(k[:1]).to(case.dev)
+    vt = torch.from_numpy(v[:1]).to(case.dev)
+    st = torch.from_numpy(s[:1]).to(case.dev)
+    before = _snapshot(case)
+    with pytest.raises(RuntimeError, match="query rows"):
+        _run(case, w, kt, vt, st, torch.empty_like(case.out))
+    torch.cuda.synchronize()
+    for a, b in zip(_snapshot(case), before):
+        assert torch.equal(a, b)

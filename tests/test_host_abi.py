@@ -402,3 +402,32 @@ def test_fused_writer_accepts_well_formed_empty_calls():
     assert _norm_rope_call(T=0) == 0, pa.pa_last_error()
     # no rotation: the tables may be absent
     assert _norm_rope_call(T=0, with_q=False, rot=0, cos=None, sin=None, kw=None) == 0, pa.pa_last_error()
+
+
+def _call_decode_write(t, T=4, kdt=torch.float32, slot_dtype=torch.int64, **opts):
+    lib = pa.load()
+    kn = _host_tensor((T, 1, 128), kdt)
+    sl = _host_tensor((T,), slot_dtype)
+    d = [_lib.desc(x) for x in (t["q"], kn, kn, sl, t["k"], t["v"], t["ks"], t["vs"], t["bt"], t["ctx"], t["cu"])]
+    do = _lib.desc(t["out"])
+    o = _lib.PaDecodeOpts()
+    for k, v in opts.items():
+        setattr(o, k, v)
+    return lib.pa_decode_write(*[_lib.ref(x) for x in d], t["mode"], _lib.ref(do), ctypes.byref(o), None)
+
+
+@pytest.mark.parametrize("over,kw,status,text", [
+    (dict(), dict(T=3), -3, "query rows"),                                   # one new token per query row
+    (dict(), dict(kdt=torch.int32), -2, "k_new"),                            # writer inputs f32 / bf16
+    (dict(), dict(slot_dtype=torch.int32), -3, "slot_mapping"),
+    (dict(bt=_host_tensor((4, 2), torch.int64)), dict(), -2, "block_table"),  # the decode's own checks
+    (dict(mode=5), dict(), -1, "scale_mode"),
+])
+def test_decode_write_refuses_bad_arguments_before_launch(over, kw, status, text):
+    assert _call_decode_write(_decode_args(**over), **kw) == status
+    assert text in pa.pa_last_error()
+
+
+def test_decode_write_accepts_a_well_formed_empty_call():
+    e = _decode_args(q=_host_tensor((0, 16, 128), torch.bfloat16), out=_host_tensor((0, 16, 128), torch.bfloat16))
+    assert _call_decode_write(e, T=0) == 0, pa.pa_last_error()

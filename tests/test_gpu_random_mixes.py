@@ -88,6 +88,36 @@ def test_random_call_over_a_bf16_cache_matches_oracle(seed):
     torch.cuda.synchronize()
     compare(out, oracle_out(w), what=f"random mix bf16 {seed} {opts}")
 
+DENSE_SEEDS = [s for s in SEEDS if draw(s)[0].sparse is None]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", DENSE_SEEDS)
+def test_random_step_with_the_write_inside_the_decode(seed):
+    """The dense draws as one decode step through pa_decode_write, from a
+    cache whose new-token slots hold poison: the cache after the call equals
+    kv_quant_write's bit for bit, and the output matches the oracle.  Draws
+    with a forced deeper ring or (ragged) no max_q_len hint run the writer
+    and the decode separately inside the call."""
+    from test_gpu_fused_write import _new_token_poison, _snapshot
+
+    w, opts = draw(seed)
+    print("random step", seed, "B", w.B, "Hkv", w.Hkv, "mode", w.mode, "q_lens", list(w.q_lens), "ctx",
+          list(w.ctx), "opts", opts, flush=True)
+    case = GpuCase(w)
+    full = _snapshot(case)
+    k, v, s = w.step_tokens()
+    _new_token_poison(case, w, s)
+    out = torch.empty_like(case.out)
+    pa.pa_decode_write(case.q, torch.from_numpy(k).to(case.dev), torch.from_numpy(v).to(case.dev),
+                       torch.from_numpy(s).to(case.dev), case.kc, case.vc, case.ks_arg, case.vs_arg, case.bt,
+                       case.ctx, case.cu, case.mode, out, **opts)
+    torch.cuda.synchronize()
+    for a, b in zip(_snapshot(case), full):
+        assert torch.equal(a, b), f"random step {seed}: cache differs from kv_quant_write's"
+    compare(out, oracle_out(w), what=f"random step {seed} {opts}")
+
+
 def test_draws_cover_every_kind_and_option():
     """The seeds above reach every call kind, scale mode and plan option."""
     kinds, modes, keys, pms = set(), set(), set(), set()

@@ -276,18 +276,30 @@ def recorded_traffic(workload):
     return None if w is None else int(w["traffic_bytes_per_launch"])
 
 
+def _events(n):
+    """n pairs of timing events, each recorded once so that the underlying
+    HIP events exist before a probe's dispatch records them."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in evs:
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    return evs
+
+
 def hbm_probe(dev, gib=4, same_bytes=None):
     """Best streaming-read rate (GB/s) of a plain 16-byte-per-lane read
     kernel over a 4 GiB buffer, for a few grid sizes; with `same_bytes`, also
     the best rate for reads of that size (rotating through the buffer so
-    they come from HBM), the floor a kernel moving that many bytes meets."""
+    they come from HBM), the floor a kernel moving that many bytes meets.
+    Every launch is timed by dispatch-recorded events, as the main kernel."""
     import ctypes
     path = os.path.join(ROOT, "fp8_paged_kv_pa_amd", "libhbmprobe.so")
     if not os.path.exists(path):
         return None
     lib = ctypes.CDLL(path)
     lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
-                                   ctypes.c_void_p]
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     nbytes = gib << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     buf.fill_(1)
@@ -296,10 +308,9 @@ def hbm_probe(dev, gib=4, same_bytes=None):
     for blocks in (256, 512, 1024, 2048, 4096):
         sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
         for rep in range(4):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            rc = lib.hbm_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream.cuda_stream)
-            e1.record()
+            e0, e1 = _events(1)[0]
+            rc = lib.hbm_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, e0.cuda_event, e1.cuda_event,
+                                    stream.cuda_stream)
             torch.cuda.synchronize()
             if rc != 0:
                 return None
@@ -312,15 +323,12 @@ def hbm_probe(dev, gib=4, same_bytes=None):
         best_small = 0.0
         for blocks in (256, 512, 1024):
             sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(24)]
-            torch.cuda.synchronize()
+            evs = _events(24)
             torch.cuda._sleep(int(5e7))
             for i, (e0, e1) in enumerate(evs):
-                e0.record()
-                lib.hbm_read_probe(buf.data_ptr() + (i % slots) * nb, nb, sink.data_ptr(), blocks,
-                                   stream.cuda_stream)
-                e1.record()
+                if lib.hbm_read_probe(buf.data_ptr() + (i % slots) * nb, nb, sink.data_ptr(), blocks,
+                                      e0.cuda_event, e1.cuda_event, stream.cuda_stream) != 0:
+                    return None
             torch.cuda.synchronize()
             ts = sorted(a.elapsed_time(b) for a, b in evs[4:])
             best_small = max(best_small, nb / (ts[len(ts) // 2] * 1e-3) / 1e9)
@@ -330,21 +338,124 @@ def hbm_probe(dev, gib=4, same_bytes=None):
     return round(best, 1), best_small
 
 
+def launch_floor(dev, grid=256, threads=256):
+    """Median dispatch-recorded duration (us) of the probe library's empty
+    kernel at the main kernel's usual grid: what any launch costs here,
+    timed the way the main kernel is."""
+    import ctypes
+    path = os.path.join(ROOT, "fp8_paged_kv_pa_amd", "libhbmprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.launch_floor_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    sink = torch.zeros(grid, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    evs = _events(72)
+    torch.cuda._sleep(int(2e7))
+    for e0, e1 in evs:
+        if lib.launch_floor_probe(flag.data_ptr(), sink.data_ptr(), grid, threads, e0.cuda_event, e1.cuda_event,
+                                  stream.cuda_stream) != 0:
+            return None
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs[8:])
+    return round(ts[len(ts) // 2], 3)
+
+
+def start_spread(dev, blocks, lds_bytes, reps=9):
+    """Median over `reps` launches of the spread (us) of the workgroups'
+    entry times (s_memrealtime, 100 MHz) in the probe library's start
+    kernel: `blocks` workgroups of 256 threads, `lds_bytes` of LDS each."""
+    import ctypes
+    path = os.path.join(ROOT, "fp8_paged_kv_pa_amd", "libhbmprobe.so")
+    lib = ctypes.CDLL(path)
+    lib.start_spread_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    ticks = torch.zeros(blocks, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    spreads = []
+    for rep in range(reps + 1):  # the first launch warms up
+        if lib.start_spread_probe(ticks.data_ptr(), blocks, 256, lds_bytes, stream.cuda_stream):
+            raise RuntimeError("start_spread_probe failed")
+        torch.cuda.synchronize()
+        t = ticks.cpu().numpy()
+        if rep:
+            spreads.append(float(t.max() - t.min()) * 0.01)
+    return round(float(np.median(spreads)), 2)
+
+
+ISSUE_KINDS = (("mfma_f32_16x16x32_bf16", 8), ("fmac_f32", 32), ("cvt_scalef32_pk_bf16_fp8", 16), ("exp_f32", 32))
+
+
+def issue_probe(dev, iters=4096):
+    """Per instruction kind the decode issues and for one and two waves per
+    SIMD: shader-clock cycles (s_memtime) per wave64 instruction and SIMD,
+    independent instructions -- the median over the waves of the probe
+    library's instruction-rate kernel, divided by the waves per SIMD -- and
+    the clock (GHz) they ran at, from the 100 MHz s_memrealtime count of the
+    same interval.  Also whether every workgroup's waves sat evenly on its
+    CU's four SIMDs."""
+    import ctypes
+    path = os.path.join(ROOT, "fp8_paged_kv_pa_amd", "libhbmprobe.so")
+    lib = ctypes.CDLL(path)
+    lib.issue_rate_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_void_p]
+    blocks = 256
+    stream = torch.cuda.current_stream()
+    res = {}
+    for wps in (1, 2):
+        waves = 4 * wps
+        rec = torch.zeros(blocks * waves * 3, dtype=torch.int64, device=dev)
+        sink = torch.zeros(blocks * 64 * waves, dtype=torch.float32, device=dev)
+        cyc, ghz, even = {}, {}, True
+        for kind, (name, per_round) in enumerate(ISSUE_KINDS):
+            for rep in range(2):  # the first run warms up
+                if lib.issue_rate_probe(kind, iters, wps, rec.data_ptr(), sink.data_ptr(), blocks,
+                                        stream.cuda_stream):
+                    raise RuntimeError("issue_rate_probe failed")
+                torch.cuda.synchronize()
+            r = rec.view(blocks, waves, 3).cpu().numpy()
+            c = np.sort(r[:, :, 0].reshape(-1))
+            f = np.sort((r[:, :, 0] / np.maximum(r[:, :, 1], 1) * 0.1).reshape(-1))
+            cyc[name] = round(float(c[len(c) // 2]) / (iters * per_round * wps), 2)
+            ghz[name] = round(float(f[len(f) // 2]), 3)
+            even = even and all(sorted(np.bincount(r[b, :, 2], minlength=4).tolist()) == [wps] * 4
+                                for b in range(blocks))
+        res[f"{wps}_wave_per_simd"] = {"cycles_per_instruction": cyc, "clock_ghz": ghz, "waves_even": bool(even)}
+    # one MFMA wave and one fma wave (four times the rounds) on each SIMD: each
+    # wave's cycles per own instruction; alone they would be the one-wave figures
+    waves = 8
+    rec = torch.zeros(blocks * waves * 3, dtype=torch.int64, device=dev)
+    sink = torch.zeros(blocks * 64 * waves, dtype=torch.float32, device=dev)
+    for rep in range(2):
+        if lib.issue_rate_probe(4, iters, 2, rec.data_ptr(), sink.data_ptr(), blocks, stream.cuda_stream):
+            raise RuntimeError("issue_rate_probe failed")
+        torch.cuda.synchronize()
+    r = rec.view(blocks, waves, 3).cpu().numpy()
+    paired = bool(np.array_equal(np.sort(r[:, :4, 2], axis=1), np.tile(np.arange(4), (blocks, 1)))
+                  and np.array_equal(np.sort(r[:, 4:, 2], axis=1), np.tile(np.arange(4), (blocks, 1))))
+    mf = float(np.median(r[:, :4, 0])) / (iters * ISSUE_KINDS[0][1])
+    fm = float(np.median(r[:, 4:, 0])) / (iters * 4 * ISSUE_KINDS[1][1])
+    res["mfma_wave_beside_fmac_wave"] = {"mfma_cycles": round(mf, 2), "fmac_cycles": round(fm, 2),
+                                         "one_of_each_per_simd": paired}
+    return res
+
+
 def block_probe(layers, w):
     """Best rate (GB/s) of the bench probe library's block-read kernel over
     exactly the (page, head) blocks one decode call reads -- every request's
     attended pages of layer l, K and V (and their scale pieces in per-token
-    mode) -- with non-temporal 16-byte loads and no arithmetic, 256
+    mode) -- with non-temporal 16-byte loads and no arithmetic, up to 256
     workgroups, rotating over the layers as the bench's steps do; and, in
-    per-token mode, the same over the K/V blocks alone.  FP8 caches only;
-    None otherwise."""
+    per-token mode, the same over the K/V blocks alone; each launch timed by
+    dispatch-recorded events, as the main kernel.  FP8 caches only; None
+    otherwise."""
     import ctypes
     path = os.path.join(ROOT, "fp8_paged_kv_pa_amd", "libhbmprobe.so")
     if not os.path.exists(path) or w.kv_dtype == "bf16":
         return None
     lib = ctypes.CDLL(path)
-    lib.hbm_block_probe.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                                             ctypes.c_void_p]
+    lib.hbm_block_probe.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 4
     ids = []
     for b in range(w.B):
         if w.sparse is None:
@@ -357,9 +468,12 @@ def block_probe(layers, w):
             ids += [P * w.Hkv + h for h in range(w.Hkv)]
     nblk = w.num_blocks * w.Hkv
     assert ids and all(0 <= i < nblk for i in ids)
-    wgs = 256
-    per_wg = (len(ids) + wgs - 1) // wgs
-    tab = np.resize(np.asarray(ids, np.int32), per_wg * wgs)
+    # at most 256 workgroups, as few entries each as that allows, and only as
+    # many workgroups as the entries fill (a small call must not be padded
+    # with repeated blocks, which would count cache hits as traffic)
+    per_wg = (len(ids) + 255) // 256
+    wgs = (len(ids) + per_wg - 1) // per_wg
+    tab = np.resize(np.asarray(ids, np.int32), per_wg * wgs)  # pads fewer than per_wg entries
     dev = layers.q[0].device
     table = torch.from_numpy(tab).to(dev)
     sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
@@ -369,18 +483,15 @@ def block_probe(layers, w):
         nbytes = len(tab) * (2 * 16384 + (2 * 512 if scales else 0))
         best = 0.0
         for rnd in range(3):
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(16)]
-            torch.cuda.synchronize()
+            evs = _events(16)
             torch.cuda._sleep(int(5e7))
             for i, (e0, e1) in enumerate(evs):
                 l = i % layers.n
-                e0.record()
                 rc = lib.hbm_block_probe(layers.kcl[l].data_ptr(), layers.vcl[l].data_ptr(),
                                          layers.ksl[l].data_ptr() if scales else None,
                                          layers.vsl[l].data_ptr() if scales else None,
-                                         table.data_ptr(), per_wg, wgs, sink.data_ptr(), stream.cuda_stream)
-                e1.record()
+                                         table.data_ptr(), per_wg, wgs, sink.data_ptr(), e0.cuda_event,
+                                         e1.cuda_event, stream.cuda_stream)
                 if rc != 0:
                     return None
             torch.cuda.synchronize()
@@ -607,6 +718,8 @@ def main():
                     help="split-K partitions: 0 the plan's, 1 fixed, 2 length-balanced")
     ap.add_argument("--separate-write", action="store_true",
                     help="write the step's new tokens with kv_quant_write, then decode (two launches)")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="print the cycles per wave64 instruction of the kinds the decode issues and the empty-launch floor, then exit")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -615,6 +728,20 @@ def main():
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the library has no "
               f"multi-GPU path; the decode kernel's per-GPU share is what one GPU shows).", file=sys.stderr)
         sys.exit(2)
+    if args.issue_probe:
+        assert torch.cuda.is_available(), "the probe needs a GPU"
+        dev = torch.device("cuda:0")
+        print(json.dumps({"issue_probe": issue_probe(dev),
+                          "launch_floor_us_by_grid": {g: launch_floor(dev, grid=g) for g in (1, 256, 1984)},
+                          "start_spread_us": {f"{g}x{lds // 1024}KiB": start_spread(dev, g, lds)
+                                              for g in (144, 1152) for lds in (0, 34 * 1024)},
+                          "note": "s_memtime cycles per wave64 instruction and SIMD with one and two waves per "
+                                  "SIMD, independent instructions, and the clock they ran at (probe library "
+                                  "issue_rate_probe); "
+                                  "median dispatch-recorded duration of an empty 256-thread kernel per grid "
+                                  "size (launch_floor_probe); spread of workgroup entry times per grid and "
+                                  "LDS size (start_spread_probe)"}))
+        return
     w = CONFIGS[args.config]()
     index_topk = INDEX_TOPK.get(args.config, 0)
     idx_bytes = index_bytes(w, index_topk) if index_topk else 0
@@ -747,6 +874,7 @@ def main():
 
     probe, probe_same = hbm_probe(dev, same_bytes=idx_bytes if index_topk else alg_bytes) or (None, None)
     probe_blocks, probe_blocks_kv = (None, None) if index_topk else (block_probe(layers, w) or (None, None))
+    floor_us = launch_floor(dev)
     try:
         cpu = None if leg is None else leg.run(layers)
     finally:
@@ -799,6 +927,7 @@ def main():
             "frac_of_probe": None if not probe else round(achieved / probe, 4),
             "hbm_read_probe_same_bytes_gbs": probe_same,
             "frac_of_same_bytes_probe": None if not probe_same else round(achieved / probe_same, 4),
+            "launch_floor_us": floor_us,
             "block_read_probe_gbs": probe_blocks,
             "block_read_probe_kv_only_gbs": probe_blocks_kv,
             "frac_of_block_probe": None if not probe_blocks else round(achieved / probe_blocks, 4),

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libfp8pa.so")
 PROBE_LIB = os.path.join(HERE, "libhbmprobe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["pa_decode.hip", "kv_write.hip", "indexer.hip", "check.hip", "api.cpp", "plan.cpp"]
+SOURCES = ["pa_decode.hip", "pa_prefill.hip", "kv_write.hip", "indexer.hip", "check.hip", "api.cpp", "plan.cpp"]
 
 # gfx950 only.  Packed-fp32 instruction selection is switched off: the
 # kernels are written in scalar fp32 and must not be fused into

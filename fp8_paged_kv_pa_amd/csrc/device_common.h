@@ -112,6 +112,37 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   return x;
 }
 
+// An empty volatile asm: a block that holds one cannot be speculated, so
+// the compiler keeps a uniform branch around the tail-chunk masks instead of
+// turning them into selects that every full chunk would execute.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
+// Maxima of a chunk's scores in 4 instructions for 8 values.  fmaxf lowers
+// to maxnum, for which the compiler first quiets each input with a v_max of
+// the value with itself; the scores are products and selects, never
+// signaling NaNs, so v_max3 / v_max take them as they are (a quiet NaN
+// yields the other operand either way).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// Word 3 of a gfx9 buffer resource: raw (untyped) 32-bit data format, no
+// swizzle, no per-lane index stride.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// A raw buffer over `bytes` bytes at `p` (0: every access is out of range,
+// which returns zeros without touching memory).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), short(0), bytes, kRsrcWord3);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }

@@ -68,6 +68,9 @@ struct DecodeArgs {
   uint8_t* v_cache_w;
   float* k_scale_w;
   float* v_scale_w;
+  // 1: the prefill kernel (long query segments): groups of
+  // kPrefillPositions positions, partitions of ppp pages, the fixed split
+  int32_t prefill;
 };
 
 // The key norm and rotary embedding the fused writer applies before the
@@ -139,6 +142,9 @@ struct IndexArgs {
 // error.
 hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool sparse, int depth, int waves,
                          hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
+// The prefill kernel alone (launch_decode calls it for a.prefill, then the merge).
+hipError_t launch_prefill_main(const DecodeArgs& a, int64_t grid, hipEvent_t ev_begin, hipEvent_t ev_end,
+                               hipStream_t stream);
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_index(const IndexArgs& a, int64_t score_grid, hipStream_t stream);
 // Workgroups of the block-score kernel for `units` (request, 16-row group) pairs.

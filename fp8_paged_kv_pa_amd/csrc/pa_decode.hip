@@ -44,27 +44,6 @@ namespace fp8pa {
 namespace {
 
 
-// An empty volatile asm: a block that holds one cannot be speculated, so
-// the compiler keeps a uniform branch around the tail-chunk masks instead of
-// turning them into selects that every full chunk would execute.
-__device__ __forceinline__ void keep_branch() { asm volatile(""); }
-
-// Maxima of a chunk's scores in 4 instructions for 8 values.  fmaxf lowers
-// to maxnum, for which the compiler first quiets each input with a v_max of
-// the value with itself; the scores are products and selects, never
-// signaling NaNs, so v_max3 / v_max take them as they are (a quiet NaN
-// yields the other operand either way).
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-__device__ __forceinline__ float max2f(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-
 constexpr float kLazyMax = 8.0f;  // log2 headroom before the running max moves
 constexpr int kAccPad = 132;      // LDS row pitch (floats) for the wave merge
 constexpr int kNoTokens = 1 << 30;  // token base of a position with nothing to read
@@ -160,16 +139,6 @@ __device__ __forceinline__ void consume_chunk(const Chunk<BF>& c) {
 #pragma unroll
   for (int i = 0; i < Chunk<BF>::kRows; ++i) asm volatile("" ::"v"(c.k[i]), "v"(c.v[i]));
   if constexpr (PER_TOKEN) asm volatile("" ::"v"(c.ks[0]), "v"(c.ks[1]), "v"(c.vs[0]), "v"(c.vs[1]));
-}
-
-// Word 3 of a gfx9 buffer resource: raw (untyped) 32-bit data format, no
-// swizzle, no per-lane index stride.
-constexpr int kRsrcWord3 = 0x00020000;
-
-// A raw buffer over `bytes` bytes at `p` (0: every access is out of range,
-// which returns zeros without touching memory).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* p, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), short(0), bytes, kRsrcWord3);
 }
 
 // Per-wave byte offsets of a lane's loads inside a block: the 16-byte
@@ -1197,7 +1166,10 @@ hipError_t launch_decode(const DecodeArgs& a, int64_t grid, bool merge, bool spa
   // the one variant-selection table: (cache element type, rows per group,
   // per-token scales, sparse, prefetch depth, waves per workgroup)
   const int d = depth, w = waves;
-  if (a.kv_bf16) {
+  if (a.prefill) {
+    hipError_t pe = launch_prefill_main(a, grid, e0, e1, stream);
+    if (pe != hipSuccess) return pe;
+  } else if (a.kv_bf16) {
     // unquantized cache: never scaled
     if (sparse) launch_shape<1, false, true, true>(a, d, w, grid, stream, e0, e1);
     else if (a.rt == 1) launch_shape<1, false, false, true>(a, d, w, grid, stream, e0, e1);

@@ -89,10 +89,16 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
     }
     lmax = std::max<int64_t>(lmax, 1);
     p.lmax = int(lmax);
+    // Long query segments whose length the host knows run the prefill
+    // kernel (FP8 caches; not with an explicitly requested balanced split or
+    // in-kernel merge, which are decode-kernel options).
+    const bool lmax_known = !c.ragged || c.max_q_len > 0;
+    p.prefill = !p.bf16kv && lmax_known && lmax >= kPrefillMinQ && c.merge_mode != PA_MERGE_IN_KERNEL &&
+                c.partition_mode != PA_PARTITION_BALANCED;
     // one or two query rows per workgroup: with two, the accumulators,
     // operands and a two-page prefetch ring fill the 256 VGPRs that let two
     // workgroups share a CU; longer q_len runs as several row groups
-    p.rt = lmax <= 1 ? 1 : 2;
+    p.rt = p.prefill ? kPrefillPositions : (lmax <= 1 ? 1 : 2);
     p.groups = int(ceil_div(lmax, p.rt));
     p.units = c.batch * hkv * p.groups;
     npages = c.max_pages;
@@ -106,7 +112,8 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
   if (c.force_parts > 0) {
     parts = c.force_parts;
   } else {
-    parts = std::max<int64_t>(1, kTargetWorkgroups / p.units_bucket);
+    // (the prefill kernel runs two workgroups per CU)
+    parts = std::max<int64_t>(1, (p.prefill ? 2 : 1) * kTargetWorkgroups / p.units_bucket);
   }
   parts = std::min<int64_t>({parts, int64_t(kMaxParts), p.pages_bucket});
   p.parts = int(std::max<int64_t>(parts, 1));
@@ -118,7 +125,7 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
   p.waves = p.rt == 2 ? 8 : 4;
   p.merge = p.parts_launched > 1;
   p.grid = p.units * p.parts_launched;
-  if (!p.sparse && p.groups > 1) {
+  if (!p.sparse && !p.prefill && p.groups > 1) {
     // workgroup id x + 8*(j*groups + gi) carries row group gi of triple
     // 8j + x: the groups of a triple run back to back on one XCD
     p.xcd_grouped = true;
@@ -145,7 +152,7 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
   // request's partials at (slot, row within the request).  At most
   // nslot - batch slots' worth of pages is spread evenly, so the split
   // always fits.
-  const bool can_balance = !p.sparse && c.batch <= kMaxBalancedBatch && c.force_parts == 0 &&
+  const bool can_balance = !p.sparse && !p.prefill && c.batch <= kMaxBalancedBatch && c.force_parts == 0 &&
                            c.merge_mode != PA_MERGE_IN_KERNEL && (!c.ragged || c.max_q_len > 0);
   if (c.partition_mode == PA_PARTITION_BALANCED && !can_balance)
     return fail(err, PA_ERR_UNSUPPORTED,

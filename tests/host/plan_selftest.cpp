@@ -77,6 +77,31 @@ static void check_xcd_layout(long long nq, long long groups, long long grid) {
   CHECK(used == (grid >= 8 ? 8 : int(grid)), "work on every XCD the grid can reach (%d)", used);
 }
 
+// The prefill grid as the kernel reads it (restated here): id / (batch * hkv
+// * parts) counts row groups down from the last, the rest is (request, KV
+// head, partition) with the partition fastest.  Every (group, request,
+// head, partition) appears once, and the last groups come first.
+static void check_prefill_layout(long long batch, long long hkv, long long groups, long long parts, long long grid) {
+  CHECK(grid == batch * hkv * groups * parts, "prefill grid %lld", grid);
+  if (grid > (1 << 20)) return;
+  std::vector<unsigned char> seen(size_t(grid), 0);
+  long long prev_gi = groups;
+  for (long long bid = 0; bid < grid; ++bid) {
+    const long long per = batch * hkv * parts;
+    const long long gi = groups - 1 - bid / per;
+    long long rem = bid % per;
+    const long long part = rem % parts;
+    rem /= parts;
+    const long long h = rem % hkv, b = rem / hkv;
+    CHECK(gi >= 0 && gi < groups && b < batch && h < hkv, "prefill ids in range");
+    CHECK(gi <= prev_gi, "heaviest groups first");
+    prev_gi = gi;
+    const long long idx = ((gi * batch + b) * hkv + h) * parts + part;
+    CHECK(!seen[size_t(idx)], "prefill workgroup twice");
+    seen[size_t(idx)] = 1;
+  }
+}
+
 static_assert(sizeof(pa_tensor) == 8 + 4 + 4 + 6 * 8 * 2, "pa_tensor");
 static_assert(sizeof(pa_decode_opts) == 48, "pa_decode_opts");
 static_assert(sizeof(pa_config) == 6 * 4 + 4 * 8 + 5 * 4 + 4, "pa_config");
@@ -142,7 +167,9 @@ int main() {
                 // largest bucket allows; it must be refused, never truncated
                 const long long pb = next_pow2(topk ? topk : W);
                 const long long parts = std::min<long long>(std::min<long long>(fp, kMaxParts), pb);
-                const long long units = topk ? c.rows * hkv : batch * hkv * ((L + 1) / 2);
+                const bool pf = !topk && L >= kPrefillMinQ && c.merge_mode != PA_MERGE_IN_KERNEL;
+                const long long per = pf ? kPrefillPositions : 2;
+                const long long units = topk ? c.rows * hkv : batch * hkv * ((L + per - 1) / per);
                 const long long counters = (next_pow2(units) * 4 + 255) / 256 * 256;
                 const long long want = counters + parts * next_pow2(c.rows) * hkv * 16 * 130 * 4;
                 CHECK(want > kMaxScratchBytes, "refused although %lld bytes fit", want);
@@ -152,7 +179,15 @@ int main() {
                     fp, (long long)c.rows, hkv, W, topk);
               if (rc) continue;
               const long long npages = topk ? topk : W;
-              CHECK(p.rt == (topk ? 1 : (L == 1 ? 1 : 2)), "rt %d", p.rt);
+              // long known q_len (uniform here) runs the prefill kernel, except
+              // with the in-kernel merge, which only the decode kernel has
+              const bool want_pf = !topk && L >= kPrefillMinQ && c.merge_mode != PA_MERGE_IN_KERNEL;
+              CHECK(p.prefill == want_pf, "prefill choice L=%d merge=%d", L, c.merge_mode);
+              CHECK(p.rt == (topk ? 1 : (want_pf ? kPrefillPositions : (L == 1 ? 1 : 2))), "rt %d", p.rt);
+              if (p.prefill) {
+                CHECK(!p.xcd_grouped && !p.balanced && p.waves == 4, "prefill layout");
+                check_prefill_layout(batch, hkv, p.groups, p.parts_launched, p.grid);
+              }
               CHECK(p.groups * p.rt >= (topk ? 1 : L), "groups");
               CHECK(p.parts_launched >= 1 && p.parts_launched <= p.parts, "parts %d/%d", p.parts_launched, p.parts);
               CHECK(p.parts <= kMaxParts, "parts cap");
@@ -233,7 +268,10 @@ int main() {
               continue;
             }
             CHECK(rc == PA_OK, "balanced plan rc %d (%s)", rc, err.c_str());
-            const bool want = batch <= kMaxBalancedBatch &&
+            // (an explicitly balanced split keeps the decode kernel; otherwise
+            // long q_len runs the prefill kernel, which takes the fixed split)
+            CHECK(p.prefill == (mode != PA_PARTITION_BALANCED && L >= kPrefillMinQ), "prefill choice");
+            const bool want = batch <= kMaxBalancedBatch && !p.prefill &&
                               (mode == PA_PARTITION_BALANCED ||
                                (mode == PA_PARTITION_PLAN && fixed.ppp >= kBalanceMinPages));
             CHECK(p.balanced == want, "balanced choice batch=%lld W=%lld mode=%d", batch, W, mode);

@@ -68,6 +68,9 @@ CONFIGS = {
 # shapes whose main kernel is bound by the matrix cores, not HBM: their
 # roofline is algorithmic flops against the dense bf16 MFMA peak
 MFMA_BOUND = {"p16k"}
+# query positions per workgroup of the prefill kernel (calls whose requests
+# hold at least 128 rows run it; pa_plan_describe reports this row count)
+PREFILL_POSITIONS = 8
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 INDEX_TOPK = {"c5i": 32}
 
@@ -246,8 +249,10 @@ def algorithmic_bytes(w):
     return kv, kv + qo + meta
 
 
-KERNEL_SOURCES = ("fp8_paged_kv_pa_amd/csrc/pa_decode.hip", "fp8_paged_kv_pa_amd/csrc/device_common.h",
-                  "fp8_paged_kv_pa_amd/csrc/launch.h", "fp8_paged_kv_pa_amd/csrc/writer_common.h")
+KERNEL_SOURCES = ("fp8_paged_kv_pa_amd/csrc/pa_decode.hip", "fp8_paged_kv_pa_amd/csrc/pa_prefill.hip",
+                  "fp8_paged_kv_pa_amd/csrc/device_common.h", "fp8_paged_kv_pa_amd/csrc/launch.h",
+                  "fp8_paged_kv_pa_amd/csrc/writer_common.h", "fp8_paged_kv_pa_amd/csrc/plan.cpp",
+                  "fp8_paged_kv_pa_amd/csrc/plan.h")
 
 
 def write_in_decode(w, separate_write, index_topk):
@@ -914,7 +919,7 @@ def main():
         "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode_main",
+            "kernel": "pa_prefill_main" if plan["rows_per_group"] == PREFILL_POSITIONS else "pa_decode_main",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -951,7 +956,6 @@ def main():
             "peak": BF16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-            "traffic": None,
             "algorithmic_flops_per_launch": int(flops),
             "dtype_note": "bf16 MFMA peak (dense); the kernel runs P.V as a bf16 hi + lo pair, "
                           "1.5x the algorithmic MFMA work",

@@ -195,7 +195,10 @@ typedef struct pa_config {
 
 /* The launch plan a config maps to (pa_plan_describe). */
 typedef struct pa_plan_info {
-  int32_t rows_per_group;  /* query rows one workgroup carries (1 or 2)      */
+  int32_t rows_per_group;  /* query positions one workgroup carries: 1 or 2,
+                              or 8 for the prefill kernel (requests of at
+                              least 128 rows, their length known: uniform
+                              q_len or max_q_len)                          */
   int32_t groups;          /* row groups per request (dense) or 1 (sparse)   */
   int32_t parts;           /* split-K partitions per unit                    */
   int32_t pages_per_part;  /* pages (dense) or list entries (sparse) per part*/

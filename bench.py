@@ -64,10 +64,11 @@ CONFIGS = {
     "c5i": lambda: wl.index_workload("c5"),
     # per-token-as-decode prefill of a 16K prompt (one q_len-16384 request)
     "p16k": lambda: wl.prefill_16k(),
+    "p16kb": lambda: wl.bf16_kv(wl.prefill_16k()),
 }
 # shapes whose main kernel is bound by the matrix cores, not HBM: their
 # roofline is algorithmic flops against the dense bf16 MFMA peak
-MFMA_BOUND = {"p16k"}
+MFMA_BOUND = {"p16k", "p16kb"}
 # query positions per workgroup of the prefill kernel (calls whose requests
 # hold at least 128 rows run it; pa_plan_describe reports this row count)
 PREFILL_POSITIONS = 8

@@ -58,16 +58,20 @@ struct PfChunk {
   f32x4 vs[8];
 };
 
-// One lane's share of a chunk as loaded: 16 bytes of K and of V (lane
-// 64i + l holds row i of the chunk, the bytes decode lane l loads as its
-// i-th piece) and, in waves 0 and 1, 16 bytes of the K or V scales.
+// One lane's share of a chunk as loaded.  FP8: 16 bytes of K and of V
+// (lane 64i + l holds row i of the chunk, the bytes decode lane l loads as
+// its i-th piece) and, in waves 0 and 1, 16 bytes of the K or V scales.
+// bf16 cache (8 rows of 1 KiB per chunk, each 16-byte piece one operand):
+// rows i and i + 4 of K and of V.
+template <bool BF>
 struct PfLoad {
-  u32x4 k, v;
+  u32x4 k[BF ? 2 : 1], v[BF ? 2 : 1];
   f32x4 s;
 };
 
-template <bool PER_TOKEN>
+template <bool PER_TOKEN, bool BF>
 __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(DecodeArgs a) {
+  static_assert(!(BF && PER_TOKEN), "a bf16 cache carries no scales");
   __shared__ PfChunk sm[2];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
@@ -143,18 +147,26 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
   }
 
   // ---- loads: lane 64i + l takes row i (1 KiB of 64 x 16 bytes) of the
-  // chunk's K and V; waves 0 and 1, lanes < 8, the chunk's K or V scales
+  // chunk's K and V (bf16: rows i and i + 4); waves 0 and 1, lanes < 8, the
+  // chunk's K or V scales
+  constexpr int kBlk = BF ? 2 * kBlockBytes : kBlockBytes;  // one (page, head) block
+  constexpr int kChunkBytes = kBlk / 4;                     // one 32-token chunk of it
   const int kv_off = 1024 * wave + 16 * lane;
   const int32_t* bt = a.block_table + int64_t(b) * a.bt_stride;
-  auto issue = [&](int c, PfLoad& d) -> bool {
+  auto issue = [&](int c, PfLoad<BF>& d) -> bool {
     const int n = c >> 2;
     const int P = (c < c1 && n < a.width) ? bt[n] : -1;
     const bool ok = P >= 0 && P < a.num_blocks;
     const int64_t blk = ok ? int64_t(P) * a.hkv + h : 0;
-    const int nrec = ok ? kBlockBytes : 0;
-    const int off = (c & 3) * 4096 + kv_off;
-    d.k = __builtin_amdgcn_raw_buffer_load_b128(block_rsrc(a.k_cache + blk * kBlockBytes, nrec), off, 0, 0);
-    d.v = __builtin_amdgcn_raw_buffer_load_b128(block_rsrc(a.v_cache + blk * kBlockBytes, nrec), off, 0, 0);
+    const int nrec = ok ? kBlk : 0;
+    const int off = (c & 3) * kChunkBytes + kv_off;
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.k_cache + blk * kBlk, nrec);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.v_cache + blk * kBlk, nrec);
+#pragma unroll
+    for (int i = 0; i < (BF ? 2 : 1); ++i) {
+      d.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 4096 * i, 0, 0);
+      d.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off + 4096 * i, 0, 0);
+    }
     if constexpr (PER_TOKEN) {
       if (wave < 2 && lane < 8) {
         const float* sp = (wave == 0 ? a.k_scale : a.v_scale) + blk * 128;
@@ -168,28 +180,61 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
   // convert a loaded chunk into LDS buffer s; V bytes of tokens the group
   // does not see are zeroed (those slots may never have been written, and a
   // NaN there would survive a zero weight)
-  auto stage = [&](const PfLoad& d, int c, PfChunk& s) {
-    u32x4 v = d.v;
+  auto stage = [&](const PfLoad<BF>& d, int c, PfChunk& s) {
+    u32x4 v[BF ? 2 : 1];
+#pragma unroll
+    for (int i = 0; i < (BF ? 2 : 1); ++i) v[i] = d.v[i];
     const int t0 = 32 * c;
     if (t0 + 32 > lim_group) {
       keep_branch();
-      uint32_t m0 = 0, m1 = 0;
+      if constexpr (BF) {
+        // bf16 V row: word w holds the lane's slots 2w and 2w+1 of one dim
+        // (slot e <-> token t0 + 16*(e/4) + 4g + e%4)
+        uint32_t m[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (t0 + 4 * g + e < lim_group) m0 |= 0xFFu << (8 * e);
-        if (t0 + 16 + 4 * g + e < lim_group) m1 |= 0xFFu << (8 * e);
+        for (int w = 0; w < 4; ++w) {
+          m[w] = 0;
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int e = 2 * w + s2;
+            if (t0 + 16 * (e >> 2) + 4 * g + (e & 3) < lim_group) m[w] |= 0xFFFFu << (16 * s2);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          v[i][0] &= m[0];
+          v[i][1] &= m[1];
+          v[i][2] &= m[2];
+          v[i][3] &= m[3];
+        }
+      } else {
+        uint32_t m0 = 0, m1 = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (t0 + 4 * g + e < lim_group) m0 |= 0xFFu << (8 * e);
+          if (t0 + 16 + 4 * g + e < lim_group) m1 |= 0xFFu << (8 * e);
+        }
+        v[0][0] &= m0;
+        v[0][1] &= m1;
+        v[0][2] &= m0;
+        v[0][3] &= m1;
       }
-      v[0] &= m0;
-      v[1] &= m1;
-      v[2] &= m0;
-      v[3] &= m1;
     }
-    // K row i: token tile i/2, k-steps 2(i%2) and 2(i%2)+1; V row i: d-tiles 2i, 2i+1
-    const int kj = 4 * (wave >> 1) + 2 * (wave & 1);
-    s.k[kj][lane] = __builtin_bit_cast(u32x4, fp8x8_to_bf16x8(d.k[0], d.k[1]));
-    s.k[kj + 1][lane] = __builtin_bit_cast(u32x4, fp8x8_to_bf16x8(d.k[2], d.k[3]));
-    s.v[2 * wave][lane] = __builtin_bit_cast(u32x4, fp8x8_to_bf16x8(v[0], v[1]));
-    s.v[2 * wave + 1][lane] = __builtin_bit_cast(u32x4, fp8x8_to_bf16x8(v[2], v[3]));
+    if constexpr (BF) {
+      // row r of a bf16 chunk is K operand r (token tile r/4, k-step r%4)
+      // and V operand (d-tile) r, as loaded
+      s.k[wave][lane] = d.k[0];
+      s.k[wave + 4][lane] = d.k[1];
+      s.v[wave][lane] = v[0];
+      s.v[wave + 4][lane] = v[1];
+    } else {
+      // K row i: token tile i/2, k-steps 2(i%2) and 2(i%2)+1; V row i: d-tiles 2i, 2i+1
+      const int kj = 4 * (wave >> 1) + 2 * (wave & 1);
+      s.k[kj][lane] = __builtin_bit_cast(u32x4, fp8x8_to_bf16x8(d.k[0][0], d.k[0][1]));
+      s.k[kj + 1][lane] = __builtin_bit_cast(u32x4, fp8x8_to_bf16x8(d.k[0][2], d.k[0][3]));
+      s.v[2 * wave][lane] = __builtin_bit_cast(u32x4, fp8x8_to_bf16x8(v[0][0], v[0][1]));
+      s.v[2 * wave + 1][lane] = __builtin_bit_cast(u32x4, fp8x8_to_bf16x8(v[0][2], v[0][3]));
+    }
     if constexpr (PER_TOKEN) {
       if (wave == 0 && lane < 8) s.ks[lane] = d.s;
       if (wave == 1 && lane < 8) s.vs[lane] = d.s;
@@ -323,7 +368,7 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
   // ---- stream the chunks: chunk c in LDS buffer (c - c0) % 2 while the
   // loads of c + 1 and c + 2 are in flight in the register ring ------------
   if (c0 < c1) {
-    PfLoad first, ring[kPfRing];
+    PfLoad<BF> first, ring[kPfRing];
     bool ok_ring[kPfRing], ok_buf[2];
     ok_buf[0] = issue(c0, first);
 #pragma unroll
@@ -381,15 +426,14 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
 }  // namespace
 
 hipError_t launch_prefill_main(const DecodeArgs& a, int64_t grid, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
-  const bool pt = a.scale_mode == PA_SCALE_PER_TOKEN;
   const dim3 block(kWave * kPfWaves);
-  if (e0 || e1) {
-    if (pt) hipExtLaunchKernelGGL(pa_prefill_main<true>, dim3(uint32_t(grid)), block, 0, s, e0, e1, 0, a);
-    else hipExtLaunchKernelGGL(pa_prefill_main<false>, dim3(uint32_t(grid)), block, 0, s, e0, e1, 0, a);
-  } else {
-    if (pt) hipLaunchKernelGGL(pa_prefill_main<true>, dim3(uint32_t(grid)), block, 0, s, a);
-    else hipLaunchKernelGGL(pa_prefill_main<false>, dim3(uint32_t(grid)), block, 0, s, a);
-  }
+  auto go = [&](auto kernel) {
+    if (e0 || e1) hipExtLaunchKernelGGL(kernel, dim3(uint32_t(grid)), block, 0, s, e0, e1, 0, a);
+    else hipLaunchKernelGGL(kernel, dim3(uint32_t(grid)), block, 0, s, a);
+  };
+  if (a.kv_bf16) go(pa_prefill_main<false, true>);
+  else if (a.scale_mode == PA_SCALE_PER_TOKEN) go(pa_prefill_main<true, false>);
+  else go(pa_prefill_main<false, false>);
   return hipGetLastError();
 }
 

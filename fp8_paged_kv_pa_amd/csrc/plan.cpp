@@ -90,10 +90,10 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
     lmax = std::max<int64_t>(lmax, 1);
     p.lmax = int(lmax);
     // Long query segments whose length the host knows run the prefill
-    // kernel (FP8 caches; not with an explicitly requested balanced split or
-    // in-kernel merge, which are decode-kernel options).
+    // kernel (not with an explicitly requested balanced split or in-kernel
+    // merge, which are decode-kernel options).
     const bool lmax_known = !c.ragged || c.max_q_len > 0;
-    p.prefill = !p.bf16kv && lmax_known && lmax >= kPrefillMinQ && c.merge_mode != PA_MERGE_IN_KERNEL &&
+    p.prefill = lmax_known && lmax >= kPrefillMinQ && c.merge_mode != PA_MERGE_IN_KERNEL &&
                 c.partition_mode != PA_PARTITION_BALANCED;
     // one or two query rows per workgroup: with two, the accumulators,
     // operands and a two-page prefetch ring fill the 256 VGPRs that let two

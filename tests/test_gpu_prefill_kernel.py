@@ -12,8 +12,9 @@ Cases: prompts whose length is not a multiple of the 8-position group (a
 last group with one position, waves with no rows), a chunked prefill over
 an earlier context, ragged segments of mixed lengths, two KV heads, the
 scalar and no-scale modes, forced partitions (partials through the merge
-kernel), uniform q_len without cu_seqlens_q, and a segment whose first
-page table entries are permuted over a poisoned pool."""
+kernel), uniform q_len without cu_seqlens_q, a segment whose page table
+entries are permuted over a poisoned pool, and the unquantized bf16 cache
+(whose poison includes NaN and infinity patterns past the context)."""
 
 import numpy as np
 import pytest
@@ -112,3 +113,28 @@ def test_prefill_16k_kernel_rows_sampled():
                       [int(x) for x in rng.integers(0, T, size=10)]))
     ref = oracle_out(w, oracle_cache(w), rows_subset=rows)
     compare(g[rows], ref, what="prefill kernel 16K")
+
+
+BF16_CASES = [
+    dict(seed=521, ctx=[300], q_lens=[300], ragged=True),
+    dict(seed=522, ctx=[700, 257], q_lens=[150, 257], ragged=True, Hkv=2),
+    dict(seed=523, ctx=[200, 333], q_lens=[130, 130]),
+]
+
+
+@pytest.mark.parametrize("kw", BF16_CASES, ids=[str(c["seed"]) for c in BF16_CASES])
+def test_prefill_kernel_bf16_cache(kw):
+    w = wl.bf16_kv(wl.small_case(**kw))
+    cfg = pa.make_config(w.Hkv, w.rows, w.B, w.W, ragged=w.cu is not None,
+                         max_q_len=int(w.q_lens.max()) if w.cu is not None else 0,
+                         scale_mode=wl.NONE, kv_dtype=3)  # bf16
+    assert pa.pa_plan_describe(cfg)["rows_per_group"] == 8
+    print("prefill kernel bf16 case", w.name, flush=True)
+    case = GpuCase(w)
+    ref = oracle_out(w)
+    out = _run(case, w)
+    compare(out, ref, what=f"{w.name} prefill kernel")
+    dec = _run(case, w, partition_mode=pa.PARTITION_BALANCED)
+    compare(out, dec.float().cpu().numpy(), atol=4e-3, cos_min=0.99999, what=f"{w.name} vs decode kernel")
+    for parts in (2, 5):
+        compare(_run(case, w, force_parts=parts), ref, what=f"{w.name} prefill kernel, {parts} partitions")

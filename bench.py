@@ -250,10 +250,24 @@ def algorithmic_bytes(w):
     return kv, kv + qo + meta
 
 
-KERNEL_SOURCES = ("fp8_paged_kv_pa_amd/csrc/pa_decode.hip", "fp8_paged_kv_pa_amd/csrc/pa_prefill.hip",
-                  "fp8_paged_kv_pa_amd/csrc/device_common.h", "fp8_paged_kv_pa_amd/csrc/launch.h",
-                  "fp8_paged_kv_pa_amd/csrc/writer_common.h", "fp8_paged_kv_pa_amd/csrc/plan.cpp",
-                  "fp8_paged_kv_pa_amd/csrc/plan.h")
+# the sources whose code a main kernel's traffic depends on (its kernel
+# file, the shared device code, the argument block and the planner)
+_SHARED_SOURCES = ("fp8_paged_kv_pa_amd/csrc/device_common.h", "fp8_paged_kv_pa_amd/csrc/launch.h",
+                   "fp8_paged_kv_pa_amd/csrc/plan.cpp", "fp8_paged_kv_pa_amd/csrc/plan.h")
+KERNEL_SOURCES = {
+    "pa_decode_main": ("fp8_paged_kv_pa_amd/csrc/pa_decode.hip",
+                       "fp8_paged_kv_pa_amd/csrc/writer_common.h") + _SHARED_SOURCES,
+    "pa_prefill_main": ("fp8_paged_kv_pa_amd/csrc/pa_prefill.hip",) + _SHARED_SOURCES,
+}
+
+
+def sources_sha256(kernel):
+    """SHA-256 over the sources of a main kernel (KERNEL_SOURCES)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
 
 
 def write_in_decode(w, separate_write, index_topk):
@@ -266,20 +280,15 @@ def write_in_decode(w, separate_write, index_topk):
 
 def recorded_traffic(workload):
     """HBM bytes per main-kernel launch from the committed counter record
-    (profiles/pa_decode_main_traffic.json), or None when the record is for
-    other kernel sources or another workload."""
-    import hashlib
+    (profiles/pa_decode_main_traffic.json), or None when the workload has no
+    record or its kernel's sources no longer hash to the recorded digest."""
     path = os.path.join(ROOT, "profiles", "pa_decode_main_traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if h.hexdigest() != rec.get("source_sha256"):
+    w = json.load(open(path)).get("workloads", {}).get(workload)
+    if w is None or w.get("kernel") not in KERNEL_SOURCES or sources_sha256(w["kernel"]) != w.get("source_sha256"):
         return None
-    w = rec.get("workloads", {}).get(workload)
-    return None if w is None else int(w["traffic_bytes_per_launch"])
+    return int(w["traffic_bytes_per_launch"])
 
 
 def _events(n):

@@ -245,11 +245,11 @@ typedef struct pa_plan_info {
  *
  * Long query segments -- the per-token-as-decode prefill [ATOM-2614]
  * "Change" runs through this contract -- take a kernel of their own when the
- * host knows every request holds at most q_len rows and that bound is at
- * least 128 (uniform calls, or pa_decode_opts.max_q_len): 16 query heads x
- * 8 positions per workgroup share each converted chunk of K/V.  Same
- * results to the decode tolerance; pa_plan_describe reports
- * rows_per_group 8 for such calls.
+ * call's bound on rows per request (its uniform q_len, or
+ * pa_decode_opts.max_q_len) is at least 128: 16 query heads x 8 positions
+ * per workgroup share each converted chunk of K/V.  Same results to the
+ * decode tolerance; pa_plan_describe reports rows_per_group 8 for such
+ * calls.
  *
  * Asynchronous on `stream`; no host synchronisation; graph-capturable once
  * the scratch is reserved (pa_reserve).  Returns PA_OK or a pa_status.

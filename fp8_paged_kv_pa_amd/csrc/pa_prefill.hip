@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
       s.v[2 * wave + 1][lane] = __builtin_bit_cast(u32x4, fp8x8_to_bf16x8(v[0][2], v[0][3]));
     }
     if constexpr (PER_TOKEN) {
-      if (wave == 0 && lane < 8) s.ks[lane] = d.s;
+      if (wave == 0 && lane < 8) s.ks[lane] = d.s * k_fold;
       if (wave == 1 && lane < 8) s.vs[lane] = d.s;
     }
   };
@@ -249,14 +249,15 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
     if (nrows == 0 || t0 >= lim_w1 || !ok) return;
     const bool full = t0 + 32 <= lim_w0;
     // per-token factors of this lane's 8 tokens (slot e <-> token
-    // t0 + 16*(e/4) + 4g + e%4): K scale folded with sm*log2(e), V scale
+    // t0 + 16*(e/4) + 4g + e%4): K scale folded with sm*log2(e) (folded when
+    // staged), V scale
     float kc[8], vsf[8];
     if constexpr (PER_TOKEN) {
       const f32x4 ka = s.ks[g], kb = s.ks[4 + g], va = s.vs[g], vb = s.vs[4 + g];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kc[e] = ka[e] * k_fold;
-        kc[4 + e] = kb[e] * k_fold;
+        kc[e] = ka[e];
+        kc[4 + e] = kb[e];
         vsf[e] = va[e];
         vsf[4 + e] = vb[e];
       }
@@ -267,7 +268,6 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
         vsf[e] = 1.0f;
       }
     }
-    __builtin_amdgcn_s_setprio(2);
     f32x4 st[2][2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) st[r][0] = st[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -281,7 +281,6 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
         st[r][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[r][j], st[r][1], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_s_setprio(0);
 
     // online softmax per row; P' = p * v_scale as a bf16 hi + lo pair (hi
     // the top 8 significant bits by truncation, lo = P' - hi exact in fp32)
@@ -351,7 +350,6 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
       for (int e = 0; e < 8; ++e) plo[r][e] = (__bf16)lo[e];
     }
 
-    __builtin_amdgcn_s_setprio(1);
     // O^T += V^T P'^T
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
@@ -362,7 +360,6 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
         acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[r], acc[r][d], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- stream the chunks: chunk c in LDS buffer (c - c0) % 2 while the

@@ -143,6 +143,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* p, int 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), short(0), bytes, kRsrcWord3);
 }
 
+// Read-only tables (block table, sparse lists) read through the constant
+// address space: uniform reads become scalar loads, counted apart from the
+// vector loads of the KV stream, so waiting for a table entry never waits
+// for KV bytes in flight.
+typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
+__device__ __forceinline__ const_i32_ptr as_const(const int32_t* p) { return (const_i32_ptr)(p); }
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }

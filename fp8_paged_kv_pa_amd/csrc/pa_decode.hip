@@ -191,12 +191,6 @@ __device__ __forceinline__ void load_chunk(Chunk<BF>& c, const DecodeArgs& a, in
   }
 }
 
-// Read-only tables (block table, sparse lists) read through the constant
-// address space: uniform reads become scalar loads, counted apart from the
-// vector loads of the KV stream, so waiting for a table entry never waits
-// for KV bytes in flight.
-typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
-__device__ __forceinline__ const_i32_ptr as_const(const int32_t* p) { return (const_i32_ptr)(p); }
 
 // Two workgroups per CU (256 registers per lane) for the four-wave,
 // two-page-ring shapes; one for the rest -- including two-row bf16, whose

@@ -152,7 +152,8 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
   constexpr int kBlk = BF ? 2 * kBlockBytes : kBlockBytes;  // one (page, head) block
   constexpr int kChunkBytes = kBlk / 4;                     // one 32-token chunk of it
   const int kv_off = 1024 * wave + 16 * lane;
-  const int32_t* bt = a.block_table + int64_t(b) * a.bt_stride;
+  // (scalar loads, off the vector-memory counter of the K/V stream)
+  const const_i32_ptr bt = as_const(a.block_table + int64_t(b) * a.bt_stride);
   auto issue = [&](int c, PfLoad<BF>& d) -> bool {
     const int n = c >> 2;
     const int P = (c < c1 && n < a.width) ? bt[n] : -1;
@@ -168,12 +169,14 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
       d.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off + 4096 * i, 0, 0);
     }
     if constexpr (PER_TOKEN) {
-      if (wave < 2 && lane < 8) {
-        const float* sp = (wave == 0 ? a.k_scale : a.v_scale) + blk * 128;
-        d.s = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(block_rsrc(sp, ok ? 512 : 0), (c & 3) * 128 + 16 * lane,
-                                                         0, 0));
-      }
+      // every lane issues it (so each step has the same loads in flight
+      // and the waits before staging count exactly); only waves 0 and 1,
+      // lanes < 8, are in range, the rest read past the 512-byte resource
+      // and get zeros without a memory access
+      const float* sp = (wave == 1 ? a.v_scale : a.k_scale) + blk * 128;
+      const int soff = (wave < 2 && lane < 8) ? (c & 3) * 128 + 16 * lane : 512;
+      d.s = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(block_rsrc(sp, ok ? 512 : 0), soff, 0, 0));
     }
     return ok;
   };
@@ -377,14 +380,15 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
       for (int k = 0; k < 2; ++k) {
         const int cc = c + k;
         const int q = k % kPfRing;  // ring slot holding chunk cc + 1
-        if (cc < c1) {
-          process(sm[k], cc, ok_buf[k]);
-          if (cc + 1 < c1) {
-            stage(ring[q], cc + 1, sm[k ^ 1]);
-            ok_buf[k ^ 1] = ok_ring[q];
-          }
-          ok_ring[q] = issue(cc + 1 + kPfRing, ring[q]);
-        }
+        if (cc < c1) process(sm[k], cc, ok_buf[k]);
+        // Staging and loads run on every step, also past the range (those
+        // loads cover 0 bytes and return zeros; that staging lands in a
+        // buffer nothing reads again), so every step has the same loads in
+        // flight and the wait before each staging counts exactly the newer
+        // step's loads instead of draining all of them.
+        stage(ring[q], cc + 1, sm[k ^ 1]);
+        ok_buf[k ^ 1] = ok_ring[q];
+        ok_ring[q] = issue(cc + 1 + kPfRing, ring[q]);
         __syncthreads();
       }
     }

@@ -25,6 +25,11 @@ stream.  One cold launch (idle GPU, caches evicted first) is reported beside
 the steady state.  The CPU oracle is then timed on the host's cores (one
 single-threaded process per core, at most 16) over requests of the same
 workload, and checks the GPU's output on them.  Prints one JSON line.
+
+Long query segments (--config p16k, and p16kb over a bf16 cache: a
+16384-token prompt as one request) run the prefill kernel, whose roofline
+is the bf16 MFMA one.  --issue-probe prints the probe library's
+instruction rates, launch floor and workgroup start spread instead.
 """
 
 import argparse

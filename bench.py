@@ -2,12 +2,13 @@
 
 A step is one pass of the hot path over one batch: the step's new tokens
 (the last q_len tokens of every request) are quantized and stored, and the
-decode attends the cache they were written to.  By default the step is one
-pa_decode_write call: the decode's main kernel writes the new tokens with
-kv_quant_write's code and attends them, plus the log-sum-exp merge kernel
-when the plan splits the context.  Block-sparse configs (their lists come
-from the indexer) and --separate-write run kv_quant_write, then
-pa_decode_ex (main kernel and merge).
+decode attends the cache they were written to.  The step is one
+pa_decode_write call (after the indexer, for the config that draws its
+block-sparse lists from it): the decode's main kernel writes the new
+tokens with kv_quant_write's code and attends them, plus the log-sum-exp
+merge kernel when the plan splits the context; calls the library cannot
+fuse (a bf16 cache, long q_len) run its writer first.  --separate-write
+runs kv_quant_write, then pa_decode_ex (main kernel and merge).
 The default workload is the long-context shape: batch 32, q_len 1, one KV
 head x 16 query heads, head_dim 128, 128-token pages, context 131072 each
 (1024 pages per request), per-token e4m3 scales, block tables drawn from a
@@ -184,28 +185,31 @@ class Layers:
 
     def step(self, l, ev=None, ev_index=None):
         mq = self.max_q_len if self.cu is not None else 0
-        if self.sp is None and not self.index_topk and not self.separate_write:
-            # one decode step through pa_decode_write: the new tokens are
-            # written inside the decode launch where the library can
-            pa.pa_decode_write(self.q[l], self.step_k, self.step_v, self.step_slots[l], self.kcl[l],
-                               self.vcl[l], self.ksl[l], self.vsl[l], self.bt[l], self.ctx, self.cu, self.mode,
-                               self.out[l], max_q_len=mq, force_parts=self.force_parts,
-                               prefetch_depth=self.prefetch_depth, workgroup_waves=self.workgroup_waves,
-                               merge_mode=self.merge_mode, partition_mode=self.partition_mode,
-                               main_begin_event=None if ev is None else ev[0],
-                               main_end_event=None if ev is None else ev[1])
-            return
-        pa.kv_quant_write(self.step_k, self.step_v, self.step_slots[l], self.kcl[l], self.vcl[l],
-                          self.ksl[l], self.vsl[l], self.mode)
+        if self.separate_write:
+            pa.kv_quant_write(self.step_k, self.step_v, self.step_slots[l], self.kcl[l], self.vcl[l],
+                              self.ksl[l], self.vsl[l], self.mode)
         sp = self.sp
         if self.index_topk:
             if ev_index is not None:
                 ev_index[0].record()
             pa.pa_index_topk(self.q_idx, self.icl[l], self.bt[l], self.ctx, self.cu, self.lists[l],
-                             self.scores[l], max_q_len=self.max_q_len if self.cu is not None else 0)
+                             self.scores[l], max_q_len=mq)
             if ev_index is not None:
                 ev_index[1].record()
             sp = self.lists[l]
+        if not self.separate_write:
+            # one decode step through pa_decode_write: the new tokens are
+            # written inside the decode launch where the library can (the
+            # indexer reads only the index cache, so it may run first)
+            pa.pa_decode_write(self.q[l], self.step_k, self.step_v, self.step_slots[l], self.kcl[l],
+                               self.vcl[l], self.ksl[l], self.vsl[l], self.bt[l], self.ctx, self.cu, self.mode,
+                               self.out[l], max_q_len=mq, force_parts=self.force_parts,
+                               prefetch_depth=self.prefetch_depth, workgroup_waves=self.workgroup_waves,
+                               merge_mode=self.merge_mode, partition_mode=self.partition_mode,
+                               sparse_page_idx=sp,
+                               main_begin_event=None if ev is None else ev[0],
+                               main_end_event=None if ev is None else ev[1])
+            return
         pa.pa_decode_ex(self.q[l], self.kcl[l], self.vcl[l], self.ksl[l], self.vsl[l], self.bt[l], self.ctx,
                         self.cu, sp, self.mode, self.out[l],
                         max_q_len=self.max_q_len if self.cu is not None else 0,
@@ -276,11 +280,13 @@ def sources_sha256(kernel):
 
 
 def write_in_decode(w, separate_write, index_topk):
-    """Whether a step's cache write runs inside the decode launch: dense FP8
-    calls through pa_decode_write with at most PA_FUSED_WRITE_MAX_Q_LEN
-    rows per request (16) and the default two-page ring."""
-    return (not separate_write and w.sparse is None and not index_topk and w.kv_dtype == "fp8"
-            and int(w.q_lens.max()) <= 16)
+    """Whether a step's cache write runs inside the decode launch: FP8 calls
+    through pa_decode_write with at most PA_FUSED_WRITE_MAX_Q_LEN rows per
+    request (16), one row per request when block-sparse, and the default
+    two-page ring."""
+    sparse = w.sparse is not None or bool(index_topk)
+    return (not separate_write and w.kv_dtype == "fp8" and int(w.q_lens.max()) <= 16
+            and (not sparse or int(w.q_lens.max()) == 1))
 
 
 def recorded_traffic(workload):

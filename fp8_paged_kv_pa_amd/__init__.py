@@ -87,16 +87,16 @@ def pa_decode_noalloc(q, k_cache, v_cache, k_scale, v_scale, block_table, contex
 def pa_decode_write(q, k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, block_table,
                     context_lens, cu_seqlens_q, scale_mode, out, sm_scale=0.0, max_q_len=0, force_parts=0,
                     main_begin_event=None, main_end_event=None, prefetch_depth=0, workgroup_waves=0,
-                    merge_mode=0, partition_mode=0, stream=None):
+                    merge_mode=0, partition_mode=0, sparse_page_idx=None, stream=None):
     """One decode step: ``kv_quant_write`` of the rows' own new tokens, then
-    ``pa_decode_ex`` over the written cache, the write done inside the
-    decode launch where it can be (see ``pa_decode_write`` in
-    include/fp8pa.h)."""
+    ``pa_decode_ex`` over the written cache (dense, or block-sparse with
+    ``sparse_page_idx``), the write done inside the decode launch where it
+    can be (see ``pa_decode_write`` in include/fp8pa.h)."""
     lib = load()
     opts = _decode_opts(sm_scale, max_q_len, force_parts, main_begin_event, main_end_event, prefetch_depth,
                         workgroup_waves, merge_mode, partition_mode)
     d = [desc(t) for t in (q, k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, block_table,
-                           context_lens, cu_seqlens_q)]
+                           context_lens, cu_seqlens_q, sparse_page_idx)]
     do = desc(out)
     check(lib.pa_decode_write(*[ref(x) for x in d], int(scale_mode), ref(do), ctypes.byref(opts),
                               stream_handle(stream)))

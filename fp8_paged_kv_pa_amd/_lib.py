@@ -136,7 +136,7 @@ def load():
     lib.pa_decode_ex.restype = ctypes.c_int
     lib.pa_decode_noalloc.argtypes = [T, T, T, T, T, T, T, T, T, ctypes.c_int, T, P(PaDecodeOpts), vp]
     lib.pa_decode_noalloc.restype = ctypes.c_int
-    lib.pa_decode_write.argtypes = [T, T, T, T, T, T, T, T, T, T, T, ctypes.c_int, T, P(PaDecodeOpts), vp]
+    lib.pa_decode_write.argtypes = [T, T, T, T, T, T, T, T, T, T, T, T, ctypes.c_int, T, P(PaDecodeOpts), vp]
     lib.pa_decode_write.restype = ctypes.c_int
     lib.pa_check_decode_inputs.argtypes = [T, T, T, T, T, T, T, T, T, ctypes.c_int, T, vp, vp]
     lib.pa_check_decode_inputs.restype = ctypes.c_int

@@ -256,9 +256,9 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   std::string perr;
   if ((rc = make_plan(cfg, &plan, &perr))) return fail(rc, perr);
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
-  // pa_decode_write: the new tokens are the query rows.  Dense FP8 calls
-  // with short requests write them inside the decode launch; the rest run
-  // the writer first.
+  // pa_decode_write: the new tokens are the query rows.  FP8 calls with
+  // short requests write them inside the decode launch (block-sparse ones
+  // when every request is a single row); the rest run the writer first.
   bool fused = false;
   if (fuse) {
     if (fuse->tokens != rows)
@@ -267,7 +267,7 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
     if (fuse->hkv != hkv) return fail(PA_ERR_SHAPE, "k_new and the cache differ in KV heads");
     const int64_t lmax = ragged ? (opts ? opts->max_q_len : 0) : (B > 0 ? rows / B : 0);
     // (the fused kernels take the two-page ring; a forced deeper ring runs unfused)
-    fused = !sparse && !bf16kv && lmax >= 1 && lmax <= PA_FUSED_WRITE_MAX_Q_LEN &&
+    fused = !bf16kv && lmax >= 1 && lmax <= PA_FUSED_WRITE_MAX_Q_LEN && (!sparse || lmax == 1) &&
             !(opts && opts->prefetch_depth > 2);
   }
   if (check_report) {
@@ -627,16 +627,16 @@ int pa_check_decode_inputs(const pa_tensor* q, const pa_tensor* k_cache, const p
 int pa_decode_write(const pa_tensor* q, const pa_tensor* k_new, const pa_tensor* v_new,
                     const pa_tensor* slot_mapping, pa_tensor* k_cache, pa_tensor* v_cache, pa_tensor* k_scale,
                     pa_tensor* v_scale, const pa_tensor* block_table, const pa_tensor* context_lens,
-                    const pa_tensor* cu_seqlens_q, int scale_mode, pa_tensor* out, const pa_decode_opts* opts,
-                    void* stream) {
+                    const pa_tensor* cu_seqlens_q, const pa_tensor* sparse_page_idx, int scale_mode,
+                    pa_tensor* out, const pa_decode_opts* opts, void* stream) {
   g_err.clear();
   WriteArgs w;
   int rc;
   if ((rc = prepare_write(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, scale_mode, nullptr,
                           nullptr, nullptr, &w)))
     return rc;
-  return decode_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, cu_seqlens_q, nullptr,
-                     scale_mode, out, opts, stream, nullptr, false, &w);
+  return decode_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, cu_seqlens_q,
+                     sparse_page_idx, scale_mode, out, opts, stream, nullptr, false, &w);
 }
 
 int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,

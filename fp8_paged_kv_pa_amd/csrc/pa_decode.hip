@@ -336,7 +336,8 @@ template <int RT, bool PER_TOKEN, bool SPARSE, int NBUF, int NW, bool BF, bool F
 __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, BF>)) void pa_decode_main(
     DecodeArgs a) {
   static_assert(!(BF && PER_TOKEN), "a bf16 cache carries no scales");
-  static_assert(!FW || (!SPARSE && !BF), "the fused write serves dense FP8 calls");
+  static_assert(!FW || !BF, "the fused write serves FP8 caches");
+  static_assert(!(FW && SPARSE) || (RT == 1 && NW == 4), "the sparse fused write: one row, four waves");
   static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
   static_assert(NW * 16 * kAccPad >= 16 * kMaxMergeParts, "merge weights reuse the wave-merge LDS");
   __shared__ float sm_ml[NW][RT][16][2];
@@ -427,7 +428,17 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       start = b * L;
     }
     nrows = 1;
-    lim0 = a.context_lens[b] - L + (row0 - start) + 1;
+    const int ctx = a.context_lens[b];
+    // the sparse fused write serves single-row requests: the row's own new
+    // token (position ctx - 1) is attended separately, when its page is on
+    // the row's list
+    lim0 = FW ? ctx - L + (row0 - start) : ctx - L + (row0 - start) + 1;
+    if constexpr (FW) {
+      fz_start = row0;
+      fz_L = 1;
+      fz_ctx = ctx;
+      fz_i0 = 0;
+    }
   } else {
     int gi;
     if (a.balanced) {
@@ -471,11 +482,16 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   bool fz_last = false;
   float fk0 = 0.f, fk1 = 0.f, fv0 = 0.f, fv1 = 0.f;
   int64_t fslot = -1;
+  // Sparse: which partition holds the new token's page is known only from
+  // the list, so wave 0 of every workgroup loads the token; partition 0
+  // stores it, and the workgroup whose stream passes its page attends it.
+  const int fz_page_base = (fz_ctx - 1) >> 7 << 7;  // token base of the new token's page (sparse)
+  bool fz_seen = false;
   if constexpr (FW) {
     const int ctx_cap = min(fz_ctx, a.width * 128);
     const int pl = (ctx_cap - 1) >> 7;
     fz_last = ctx_cap > 0 && n0 <= pl && pl < n0 + ppp;
-    if (fz_last && wave < fz_L) {
+    if ((SPARSE || fz_last) && wave < fz_L) {
       const int64_t t = fz_start + wave;
       load_pair(a.k_new, t * a.kn_tok_stride + h * a.kn_head_stride + 2 * lane, a.kn_bf16, &fk0, &fk1);
       load_pair(a.v_new, t * a.vn_tok_stride + h * a.vn_head_stride + 2 * lane, a.kn_bf16, &fv0, &fv1);
@@ -574,8 +590,12 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     if constexpr (SPARSE) return n < n1 ? (n == s0 ? first_entry : sp_c[n]) : -1;
     return n;
   };
+  // (sparse fused write: the page that starts with the row's new token is
+  // still streamed -- its bytes are all masked -- so that the stream sees
+  // it is on the list)
+  constexpr int kListSlack = (FW && SPARSE) ? 1 : 0;
   auto logical_ok = [&](int n, int ln) -> bool {
-    return n < n1 && ln >= 0 && ln < a.width && ln * 128 < lim_max;
+    return n < n1 && ln >= 0 && ln < a.width && ln * 128 < lim_max + kListSlack;
   };
   // raw physical page of logical page ln (read only if the position is usable)
   auto raw_at = [&](int n, int ln) -> int {
@@ -588,6 +608,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   };
   auto valid_page = [&](int P) -> bool { return P >= 0 && P < a.num_blocks; };
   auto process = [&](Chunk<BF>& c, int tbase) {
+    if constexpr (FW && SPARSE) fz_seen = fz_seen || tbase == fz_page_base;
     const int t0 = tbase + 32 * cw;
     if (t0 >= lim_max) {
       // nothing of this chunk is attended: still consume its registers so the
@@ -791,15 +812,16 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   // as in the page stream.  It runs after the page stream: inside its first
   // step (under that step's loads) the one-row kernel measured 11-14 us
   // slower at 128K, and the two-row kernel has no registers to spare there.
-  auto new_token = [&](int j, float k0, float k1, float v0, float v1, int64_t slot) {
+  auto new_token = [&](int j, float k0, float k1, float v0, float v1, int64_t slot, bool store, bool attend) {
     if constexpr (FW) {
       float* lds = &sm_acc[wave][0][0];  // 256 floats: the K codes' values, then V's
       float ks_t, vs_t;
       const uint32_t kcode = quantize_pair(k0, k1, a.scale_mode, a.k_scale, &ks_t);
       const uint32_t vcode = quantize_pair(v0, v1, a.scale_mode, a.v_scale, &vs_t);
-      if (fz_i0 == 0 && slot >= 0 && slot < a.num_blocks * 128)
+      if (store && slot >= 0 && slot < a.num_blocks * 128)
         store_token_fp8(a.k_cache_w, a.v_cache_w, a.k_scale_w, a.v_scale_w, a.hkv, a.scale_mode, slot, h, lane,
                         kcode, vcode, ks_t, vs_t);
+      if (!attend) return;
       const int pos = fz_ctx - fz_L + j;
       if (pos < 0 || pos >= cap) return;  // not attended (uniform)
       const bf16x2 kb = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kcode, 1.0f, false);
@@ -897,15 +919,20 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     }
   }
 
-  if constexpr (FW) {
-    if (fz_pend) new_token(wave, fk0, fk1, fv0, fv1, fslot);
+  if constexpr (FW && SPARSE) {
+    // the row's one new token: stored by partition 0, attended here if this
+    // workgroup's stream passed its page
+    if (wave == 0 && (part == 0 || fz_seen)) new_token(0, fk0, fk1, fv0, fv1, fslot, part == 0, fz_seen);
+  } else if constexpr (FW) {
+    // row group 0 of the last partition stores each new token once
+    if (fz_pend) new_token(wave, fk0, fk1, fv0, fv1, fslot, fz_i0 == 0, true);
     if (fz_last) {
       for (int j = wave + NW; j < fz_L; j += NW) {
         const int64_t t = fz_start + j;
         float k0, k1, v0, v1;
         load_pair(a.k_new, t * a.kn_tok_stride + h * a.kn_head_stride + 2 * lane, a.kn_bf16, &k0, &k1);
         load_pair(a.v_new, t * a.vn_tok_stride + h * a.vn_head_stride + 2 * lane, a.kn_bf16, &v0, &v1);
-        new_token(j, k0, k1, v0, v1, a.slots[t]);
+        new_token(j, k0, k1, v0, v1, a.slots[t], fz_i0 == 0, true);
       }
     }
   }
@@ -1131,6 +1158,10 @@ void launch_main_t(const DecodeArgs& a, int64_t grid, hipStream_t s, hipEvent_t 
 template <int RT, bool PT, bool SP, bool BF = false>
 void launch_shape(const DecodeArgs& a, int depth, int waves, int64_t grid, hipStream_t s, hipEvent_t e0,
                   hipEvent_t e1) {
+  if constexpr (SP && !BF) {
+    // the sparse fused write (single-row requests): four waves, the two-page ring
+    if (a.fused) return launch_main_t<1, PT, true, 2, 4, false, true>(a, grid, s, e0, e1);
+  }
   if constexpr (!SP && !BF) {
     // the fused write: the two-page ring at either width
     if (a.fused) {

@@ -368,8 +368,8 @@ int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new,
  * kv_quant_write; the attention is that of the decode contract over the
  * written cache ([ATOM-2614] "Change"), within the decode's tolerance.
  *
- * Arguments: those of pa_decode_ex without sparse_page_idx, plus k_new,
- * v_new, slot_mapping as in kv_quant_write, with T == rows:
+ * Arguments: those of pa_decode_ex, plus k_new, v_new, slot_mapping as in
+ * kv_quant_write, with T == rows:
  *   token t is query row t's own token; row i of request b (rows
  *   cu[b] .. cu[b+1]-1, or the uniform split) sits at position
  *   context_lens[b] - L_b + i, and slot_mapping[t] must be the cache slot
@@ -382,8 +382,12 @@ int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new,
  * in opts for a ragged call) run as one decode launch (plus the merge when
  * split): the workgroups of each request's last partition quantize its new
  * tokens, row group 0 stores them, and every row attends them from
- * registers while the page stream covers the older positions.  Every other
- * call (a bf16 cache, longer or unknown q_len) runs kv_quant_write and then
+ * registers while the page stream covers the older positions.  Block-sparse
+ * calls (sparse_page_idx as in pa_decode) whose requests are single rows
+ * run the same way: partition 0 of each row stores its token, and the row
+ * attends it only if the token's page is on its list, as the row would
+ * after a separate write.  Every other call (a bf16 cache, longer or
+ * unknown q_len, multi-row sparse calls) runs kv_quant_write and then
  * pa_decode_ex, with the same results.  Errors: everything the two calls
  * check, plus T != rows (PA_ERR_SHAPE), all before any launch.  Slot
  * preconditions that only device memory shows are the caller's: a slot
@@ -394,8 +398,9 @@ int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new,
 int pa_decode_write(const pa_tensor* q, const pa_tensor* k_new, const pa_tensor* v_new,
                     const pa_tensor* slot_mapping, pa_tensor* k_cache, pa_tensor* v_cache,
                     pa_tensor* k_scale, pa_tensor* v_scale, const pa_tensor* block_table,
-                    const pa_tensor* context_lens, const pa_tensor* cu_seqlens_q, int scale_mode,
-                    pa_tensor* out, const pa_decode_opts* opts, void* stream);
+                    const pa_tensor* context_lens, const pa_tensor* cu_seqlens_q,
+                    const pa_tensor* sparse_page_idx, int scale_mode, pa_tensor* out,
+                    const pa_decode_opts* opts, void* stream);
 
 /*
  * kv_norm_rope_write -- kv_quant_write fused with the key's RMS norm and

@@ -15,7 +15,11 @@ The cases cover one-row and two-row workgroups, uniform, odd and ragged
 q_len, new tokens across a page boundary, requests made only of new tokens,
 the scalar and no-scale modes, two KV heads, bf16 inputs, forced and
 balanced partitions, the in-kernel merge, more new tokens than waves, and
-the calls that run unfused (q_len above the fused limit, a bf16 cache)."""
+the calls that run unfused (q_len above the fused limit, a bf16 cache),
+and block-sparse single-row calls (partition 0 stores each row's token; the
+row attends it only if its page is on the row's list, as after a separate
+write), with the new token first in its page and rows whose list leaves
+that page out."""
 
 import numpy as np
 import pytest
@@ -192,3 +196,50 @@ def test_fused_write_refuses_before_launch():
     torch.cuda.synchronize()
     for a, b in zip(_snapshot(case), before):
         assert torch.equal(a, b)
+
+
+SPARSE_CASES = [
+    dict(seed=431, ctx=[700, 1300, 513], q_lens=[1, 1, 1], sparse_topk=3),             # 513: first token of page 4
+    dict(seed=432, ctx=[2000, 129], q_lens=[1, 1], sparse_topk=2, mode=wl.SCALAR),     # 129: first token of page 1
+    dict(seed=433, ctx=[1025, 400], q_lens=[1, 1], sparse_topk=4, mode=wl.NONE, Hkv=2),
+]
+
+
+@pytest.mark.parametrize("drop", [False, True], ids=["listed", "unlisted"])
+@pytest.mark.parametrize("kw", SPARSE_CASES, ids=[str(c["seed"]) for c in SPARSE_CASES])
+def test_fused_write_sparse(kw, drop):
+    w = wl.small_case(**kw)
+    case = GpuCase(w)
+    full = _snapshot(case)
+    if drop:
+        # odd rows no longer list the page that holds their new token
+        sp = w.sparse.copy()
+        for r in range(1, w.rows, 2):
+            last = (int(w.ctx[r]) - 1) // 128
+            sp[r][sp[r] == last] = -1
+        w.sparse = sp
+        case.sp = torch.from_numpy(sp).to(case.dev)
+    ocache = oracle_cache(w)
+    ref64 = oracle_out(w, cache=ocache)
+    ref_sep = case.decode(out=torch.empty_like(case.out))
+    torch.cuda.synchronize()
+    k, v, s = w.step_tokens()
+    kt = torch.from_numpy(k).to(case.dev)
+    vt = torch.from_numpy(v).to(case.dev)
+    st = torch.from_numpy(s).to(case.dev)
+    for kwr in ({}, dict(force_parts=1), dict(force_parts=2), dict(force_parts=3)):
+        tag = f"{w.name} {'unlisted' if drop else 'listed'} {kwr}"
+        print("fused write sparse case", tag, flush=True)
+        _new_token_poison(case, w, s)
+        torch.cuda.synchronize()
+        out = torch.empty_like(case.out)
+        pa.pa_decode_write(case.q, kt, vt, st, case.kc, case.vc, case.ks_arg, case.vs_arg, case.bt, case.ctx,
+                           None, case.mode, out, sparse_page_idx=case.sp, **kwr)
+        torch.cuda.synchronize()
+        after = _snapshot(case)
+        for a, b, name in zip(after, full, ("k codes", "v codes", "k scales", "v scales")):
+            assert torch.equal(a, b), f"{tag}: {name} differ from kv_quant_write's"
+        assert np.array_equal(after[0].cpu().numpy().reshape(-1), ocache[0].reshape(-1)), f"{tag}: K vs oracle"
+        assert np.array_equal(after[1].cpu().numpy().reshape(-1), ocache[1].reshape(-1)), f"{tag}: V vs oracle"
+        compare(out, ref64, what=f"{tag} vs oracle")
+        compare(out, ref_sep.float().cpu().numpy(), atol=4e-3, cos_min=0.99999, what=f"{tag} vs separate calls")

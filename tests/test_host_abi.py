@@ -408,7 +408,8 @@ def _call_decode_write(t, T=4, kdt=torch.float32, slot_dtype=torch.int64, **opts
     lib = pa.load()
     kn = _host_tensor((T, 1, 128), kdt)
     sl = _host_tensor((T,), slot_dtype)
-    d = [_lib.desc(x) for x in (t["q"], kn, kn, sl, t["k"], t["v"], t["ks"], t["vs"], t["bt"], t["ctx"], t["cu"])]
+    d = [_lib.desc(x) for x in (t["q"], kn, kn, sl, t["k"], t["v"], t["ks"], t["vs"], t["bt"], t["ctx"], t["cu"],
+                                None)]
     do = _lib.desc(t["out"])
     o = _lib.PaDecodeOpts()
     for k, v in opts.items():

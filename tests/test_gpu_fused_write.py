@@ -15,8 +15,8 @@ The cases cover one-row and two-row workgroups, uniform, odd and ragged
 q_len, new tokens across a page boundary, requests made only of new tokens,
 the scalar and no-scale modes, two KV heads, bf16 inputs, forced and
 balanced partitions, the in-kernel merge, more new tokens than waves, and
-the calls that run unfused (q_len above the fused limit, a bf16 cache),
-and block-sparse single-row calls (partition 0 stores each row's token; the
+the calls that run unfused (q_len above the fused limit, a bf16 cache,
+block-sparse calls with several rows per request), and block-sparse single-row calls (partition 0 stores each row's token; the
 row attends it only if its page is on the row's list, as after a separate
 write), with the new token first in its page and rows whose list leaves
 that page out."""
@@ -99,7 +99,7 @@ def _snapshot(case):
 def _run(case, w, k, v, slots, out, **kw):
     mq = int(w.q_lens.max()) if w.cu is not None else 0
     pa.pa_decode_write(case.q, k, v, slots, case.kc, case.vc, case.ks_arg, case.vs_arg, case.bt, case.ctx,
-                       case.cu, case.mode, out, max_q_len=mq, **kw)
+                       case.cu, case.mode, out, max_q_len=mq, sparse_page_idx=case.sp, **kw)
     return out
 
 
@@ -155,6 +155,11 @@ def test_unfused_fallbacks():
     _check_step(w, what="q_len 17", runs=({}, dict(force_parts=2)))
     w = wl.small_case(seed=412, ctx=[700, 300], q_lens=[1, 1])
     _check_step(w, what="depth 3", runs=(dict(prefetch_depth=3),))
+    # block-sparse calls with more than one row per request
+    w = wl.small_case(seed=415, ctx=[2000, 900], q_lens=[2, 2], sparse_topk=4)
+    _check_step(w, what="sparse q_len 2", runs=({}, dict(force_parts=2)))
+    w = wl.small_case(seed=416, ctx=[1500, 600, 300], q_lens=[3, 1, 2], ragged=True, sparse_topk=3)
+    _check_step(w, what="sparse ragged", runs=({},))
 
 
 def test_unfused_bf16_cache():

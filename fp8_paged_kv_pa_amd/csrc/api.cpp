@@ -360,6 +360,7 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   a.nslot = plan.nslot;
   a.lrows = plan.lrows;
   a.prefill = plan.prefill ? 1 : 0;
+  a.kv_once = plan.kv_once ? 1 : 0;
   float sm = (opts && opts->sm_scale != 0.0f) ? opts->sm_scale : 1.0f / std::sqrt(float(kDim));
   a.sm_log2 = sm * 1.4426950408889634f;
   if (fused) {

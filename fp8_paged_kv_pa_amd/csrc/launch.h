@@ -71,6 +71,9 @@ struct DecodeArgs {
   // 1: the prefill kernel (long query segments): groups of
   // kPrefillPositions positions, partitions of ppp pages, the fixed split
   int32_t prefill;
+  // 1: two-row workgroups load K/V non-temporally (at most two row groups
+  // read each page)
+  int32_t kv_once;
 };
 
 // The key norm and rotary embedding the fused writer applies before the

@@ -168,11 +168,11 @@ __device__ __forceinline__ void load_chunk(Chunk<BF>& c, const DecodeArgs& a, in
   const int nrec = valid ? kBlockBytes : 0;
   const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.k_cache + b * kBlockBytes, nrec);
   const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.v_cache + b * kBlockBytes, nrec);
-  // ONCE: these K and V bytes are read once per call (one-row workgroups),
-  // so non-temporal loads keep them from evicting what is reused (tables,
-  // the split-K partials the merge reads next, the pages the writer
-  // touches).  Two-row workgroups read each page once per row group, and
-  // the second group's read should hit the cache.
+  // ONCE: these K and V bytes are read once per call (one-row workgroups)
+  // or by at most two row groups, so non-temporal loads keep them from
+  // evicting what is reused (tables, the split-K partials the merge reads
+  // next, the pages the writer touches).  With more row groups per page the
+  // later groups' reads should hit the cache.
   constexpr int kAux = ONCE ? 2 : 0;  // cache-policy bit 1: non-temporal
 #pragma unroll
   for (int i = 0; i < Chunk<BF>::kRows; ++i)
@@ -332,13 +332,16 @@ __device__ __forceinline__ void xcd_group_of(const DecodeArgs& a, uint32_t* q, i
   }
 }
 
-template <int RT, bool PER_TOKEN, bool SPARSE, int NBUF, int NW, bool BF, bool FW>
+// ONCE2: a two-row workgroup's K/V loads are non-temporal (a.kv_once).
+template <int RT, bool PER_TOKEN, bool SPARSE, int NBUF, int NW, bool BF, bool FW, bool ONCE2>
 __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, BF>)) void pa_decode_main(
     DecodeArgs a) {
   static_assert(!(BF && PER_TOKEN), "a bf16 cache carries no scales");
   static_assert(!FW || !BF, "the fused write serves FP8 caches");
   static_assert(!(FW && SPARSE) || (RT == 1 && NW == 4), "the sparse fused write: one row, four waves");
   static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
+  static_assert(!ONCE2 || RT == 2, "one-row workgroups always load non-temporally");
+  constexpr bool kOnce = RT == 1 || ONCE2;
   static_assert(NW * 16 * kAccPad >= 16 * kMaxMergeParts, "merge weights reuse the wave-merge LDS");
   __shared__ float sm_ml[NW][RT][16][2];
   __shared__ float sm_acc[NW][16][kAccPad];
@@ -513,7 +516,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
     }
     const bool ok0 = P0 >= 0 && P0 < a.num_blocks;
     tb[0] = ok0 ? ln0 * 128 : kNoTokens;
-    load_chunk<PER_TOKEN, BF, RT == 1>(buf[0], a, int64_t(P0) * a.hkv + h, ok0, lofs);
+    load_chunk<PER_TOKEN, BF, kOnce>(buf[0], a, int64_t(P0) * a.hkv + h, ok0, lofs);
   }
   // query operands: B of S^T = K Q^T, lane = (head hr, dims 8g..8g+7 of
   // each 32-dim k-step)
@@ -889,7 +892,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       const int P = raw_at(pos, ln);
       const bool ok = valid_page(P);
       tb[k] = ok ? ln * 128 : kNoTokens;
-      load_chunk<PER_TOKEN, BF, RT == 1>(buf[k], a, int64_t(P) * a.hkv + h, ok, lofs);
+      load_chunk<PER_TOKEN, BF, kOnce>(buf[k], a, int64_t(P) * a.hkv + h, ok, lofs);
     }
     // raw entry of the next position to load (s0 + (NBUF-1)*S) and the
     // logical page of the one after it
@@ -909,7 +912,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
         const int nl = nn + (NBUF - 1) * S;
         const bool ok = valid_page(P_next);
         tb[ls] = ok ? ln_next * 128 : kNoTokens;
-        load_chunk<PER_TOKEN, BF, RT == 1>(buf[ls], a, int64_t(P_next) * a.hkv + h, ok, lofs);
+        load_chunk<PER_TOKEN, BF, kOnce>(buf[ls], a, int64_t(P_next) * a.hkv + h, ok, lofs);
         // table reads for the following steps (checked one step later)
         ln_next = ln_after;
         P_next = raw_at(nl + S, ln_next);
@@ -1141,14 +1144,24 @@ __global__ __launch_bounds__(4 * kWave) void pa_merge(DecodeArgs a) {
 
 // With events, the dispatch itself records them (start and end of this
 // kernel), so the measured time is the kernel's own, without marker packets.
+template <int RT, bool PT, bool SP, int NB, int NW, bool BF, bool FW, bool O2>
+void launch_main_k(const DecodeArgs& a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (e0 || e1)
+    hipExtLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB, NW, BF, FW, O2>), dim3(uint32_t(grid)),
+                          dim3(kWave * NW), 0, s, e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB, NW, BF, FW, O2>), dim3(uint32_t(grid)), dim3(kWave * NW),
+                       0, s, a);
+}
+
+// two-row shapes: the non-temporal instance where at most two row groups
+// read each page
 template <int RT, bool PT, bool SP, int NB, int NW, bool BF, bool FW = false>
 void launch_main_t(const DecodeArgs& a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (e0 || e1)
-    hipExtLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB, NW, BF, FW>), dim3(uint32_t(grid)), dim3(kWave * NW),
-                          0, s, e0, e1, 0, a);
-  else
-    hipLaunchKernelGGL((pa_decode_main<RT, PT, SP, NB, NW, BF, FW>), dim3(uint32_t(grid)), dim3(kWave * NW), 0,
-                       s, a);
+  if constexpr (RT == 2) {
+    if (a.kv_once) return launch_main_k<RT, PT, SP, NB, NW, BF, FW, true>(a, grid, s, e0, e1);
+  }
+  launch_main_k<RT, PT, SP, NB, NW, BF, FW, false>(a, grid, s, e0, e1);
 }
 
 // prefetch depth and workgroup width: eight waves (two pages side by side)

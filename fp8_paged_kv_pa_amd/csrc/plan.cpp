@@ -100,6 +100,12 @@ int make_plan(const pa_config& c, Plan* out, std::string* err) {
     // workgroups share a CU; longer q_len runs as several row groups
     p.rt = p.prefill ? kPrefillPositions : (lmax <= 1 ? 1 : 2);
     p.groups = int(ceil_div(lmax, p.rt));
+    // Two-row workgroups read each page once per row group.  With at most
+    // two groups the K/V loads are non-temporal, as one-row workgroups' are
+    // (measured: q_len 2 and 4, FP8 and bf16, faster steps although the
+    // second group's reads then miss the cache more often); with more groups
+    // the later groups' cache hits are worth more (q_len 8: slower).
+    p.kv_once = !p.prefill && p.rt == 2 && p.groups <= 2;
     p.units = c.batch * hkv * p.groups;
     npages = c.max_pages;
   }

@@ -60,6 +60,7 @@ struct Plan {
   int rt = 1;              // query positions per workgroup (1 or 2; prefill: kPrefillPositions)
   bool prefill = false;    // the prefill kernel (long query segments)
   int groups = 1;          // row groups per request (dense)
+  bool kv_once = false;    // two-row calls of at most two row groups: non-temporal K/V loads
   int parts = 1;           // split-K partitions per unit (scratch is sized for this)
   int parts_launched = 1;  // partitions that can hold work given the real width
   int ppp = 1;             // pages (dense) or list entries (sparse) per partition

@@ -189,6 +189,8 @@ int main() {
                 check_prefill_layout(batch, hkv, p.groups, p.parts_launched, p.grid);
               }
               CHECK(p.groups * p.rt >= (topk ? 1 : L), "groups");
+              // non-temporal two-row loads: at most two row groups per page
+              CHECK(p.kv_once == (!topk && !want_pf && L >= 2 && L <= 4), "kv_once L=%d", L);
               CHECK(p.parts_launched >= 1 && p.parts_launched <= p.parts, "parts %d/%d", p.parts_launched, p.parts);
               CHECK(p.parts <= kMaxParts, "parts cap");
               // every page position covered once: [k*ppp, (k+1)*ppp) for k < parts_launched

@@ -280,12 +280,12 @@ def sources_sha256(kernel):
 
 
 def write_in_decode(w, separate_write, index_topk):
-    """Whether a step's cache write runs inside the decode launch: FP8 calls
+    """Whether a step's cache write runs inside the decode launch: calls
     through pa_decode_write with at most PA_FUSED_WRITE_MAX_Q_LEN rows per
     request (16), one row per request when block-sparse, and the default
     two-page ring."""
     sparse = w.sparse is not None or bool(index_topk)
-    return (not separate_write and w.kv_dtype == "fp8" and int(w.q_lens.max()) <= 16
+    return (not separate_write and int(w.q_lens.max()) <= 16
             and (not sparse or int(w.q_lens.max()) == 1))
 
 

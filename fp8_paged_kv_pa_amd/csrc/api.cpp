@@ -256,9 +256,9 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
   std::string perr;
   if ((rc = make_plan(cfg, &plan, &perr))) return fail(rc, perr);
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
-  // pa_decode_write: the new tokens are the query rows.  FP8 calls with
-  // short requests write them inside the decode launch (block-sparse ones
-  // when every request is a single row); the rest run the writer first.
+  // pa_decode_write: the new tokens are the query rows.  Calls with short
+  // requests write them inside the decode launch (block-sparse ones when
+  // every request is a single row); the rest run the writer first.
   bool fused = false;
   if (fuse) {
     if (fuse->tokens != rows)
@@ -267,7 +267,7 @@ int decode_impl(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, co
     if (fuse->hkv != hkv) return fail(PA_ERR_SHAPE, "k_new and the cache differ in KV heads");
     const int64_t lmax = ragged ? (opts ? opts->max_q_len : 0) : (B > 0 ? rows / B : 0);
     // (the fused kernels take the two-page ring; a forced deeper ring runs unfused)
-    fused = !bf16kv && lmax >= 1 && lmax <= PA_FUSED_WRITE_MAX_Q_LEN && (!sparse || lmax == 1) &&
+    fused = lmax >= 1 && lmax <= PA_FUSED_WRITE_MAX_Q_LEN && (!sparse || lmax == 1) &&
             !(opts && opts->prefetch_depth > 2);
   }
   if (check_report) {

@@ -10,8 +10,9 @@
 // Fix").  It is the only cache writer of the library (ROCm/ATOM pull request
 // 2710 review, "Smaller": one shared writer so the FP8 and non-FP8 branches
 // cannot drift), so the unquantized bf16 cache is written here too.  Its
-// per-token load, quantization and FP8 store live in writer_common.h, which
-// the decode kernel's fused write (pa_decode_write) calls as well.
+// per-token load, quantization and FP8 and bf16 stores live in
+// writer_common.h, which the decode kernel's fused write (pa_decode_write)
+// calls as well.
 //
 // The fused variant (kv_norm_rope_write) applies the key's RMS norm and
 // rotary embedding to K in registers before the same quantize-and-store
@@ -31,43 +32,6 @@ namespace fp8pa {
 namespace {
 
 constexpr int kWriteWaves = 4;
-
-// fp32 -> bf16 bits: round to nearest, ties to even, on the 16 dropped
-// bits; NaN stays NaN (quiet bit set, sign kept).  Integer work, so the
-// stored bits do not depend on a conversion instruction's NaN handling.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// The unquantized cache: bf16 elements in the bf16 page layout (same
-// chunking as the FP8 pages, 8 elements per 16-byte lane operand).
-__device__ __forceinline__ void store_bf16(const WriteArgs& a, int64_t page, int h, int o, int lane,
-                                           float k0, float k1, float v0, float v1) {
-  const int64_t blk = (page * a.hkv + h) * int64_t(16384);
-  uint16_t* kc = reinterpret_cast<uint16_t*>(a.k_cache) + blk;
-  uint16_t* vc = reinterpret_cast<uint16_t*>(a.v_cache) + blk;
-  const int c = o >> 5, tau = (o >> 4) & 1;
-  // K: dims 2*lane and 2*lane+1 are adjacent elements (u even, u+1)
-  {
-    const int d = 2 * lane;
-    const int j = d >> 5, g = (d >> 3) & 3, u = d & 7, r = o & 15;
-    const int off = 4096 * c + 512 * (4 * tau + j) + 8 * (16 * g + r) + u;
-    *reinterpret_cast<uint32_t*>(kc + off) = f32_to_bf16_bits(k0) | (f32_to_bf16_bits(k1) << 16);
-  }
-  // V: the two dims sit in pieces 8 elements apart
-  {
-    const int w = o & 15, g = w >> 2, e = 4 * tau + (w & 3);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int d = 2 * lane + s;
-      const int delta = d >> 4, r = d & 15;
-      const int off = 4096 * c + 512 * delta + 8 * (16 * g + r) + e;
-      vc[off] = uint16_t(f32_to_bf16_bits(s ? v1 : v0));
-    }
-  }
-}
 
 // Sum over the wave of one value per lane as a balanced binary tree in lane
 // order: at step k every lane adds the lane k apart (xor), so each partial is
@@ -176,10 +140,9 @@ __global__ __launch_bounds__(kWave * kWriteWaves) void kv_write_kernel(WriteArgs
     const int64_t pos = min(max(a.nr.positions[t], int64_t(0)), a.nr.max_pos - 1);
     transform_pair(k0, k1, a.nr.k_weight, a.nr, pos, lane);
   }
-  const int64_t page = slot >> 7;
-  const int o = int(slot & 127);
   if (a.out_bf16) {
-    store_bf16(a, page, h, o, lane, k0, k1, v0, v1);
+    store_token_bf16(a.k_cache, a.v_cache, a.hkv, slot, h, lane, f32_to_bf16_bits(k0) | (f32_to_bf16_bits(k1) << 16),
+                     f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16));
     return;
   }
 

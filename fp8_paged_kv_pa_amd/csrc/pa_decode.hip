@@ -337,7 +337,6 @@ template <int RT, bool PER_TOKEN, bool SPARSE, int NBUF, int NW, bool BF, bool F
 __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, BF>)) void pa_decode_main(
     DecodeArgs a) {
   static_assert(!(BF && PER_TOKEN), "a bf16 cache carries no scales");
-  static_assert(!FW || !BF, "the fused write serves FP8 caches");
   static_assert(!(FW && SPARSE) || (RT == 1 && NW == 4), "the sparse fused write: one row, four waves");
   static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
   static_assert(!ONCE2 || RT == 2, "one-row workgroups always load non-temporally");
@@ -818,17 +817,29 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   auto new_token = [&](int j, float k0, float k1, float v0, float v1, int64_t slot, bool store, bool attend) {
     if constexpr (FW) {
       float* lds = &sm_acc[wave][0][0];  // 256 floats: the K codes' values, then V's
-      float ks_t, vs_t;
-      const uint32_t kcode = quantize_pair(k0, k1, a.scale_mode, a.k_scale, &ks_t);
-      const uint32_t vcode = quantize_pair(v0, v1, a.scale_mode, a.v_scale, &vs_t);
-      if (store && slot >= 0 && slot < a.num_blocks * 128)
-        store_token_fp8(a.k_cache_w, a.v_cache_w, a.k_scale_w, a.v_scale_w, a.hkv, a.scale_mode, slot, h, lane,
-                        kcode, vcode, ks_t, vs_t);
-      if (!attend) return;
+      float ks_t = 1.0f, vs_t = 1.0f;
+      bf16x2 kb, vb;  // the stored values: the dequantized codes, or the bf16 elements
+      if constexpr (BF) {
+        // the unquantized cache: the elements rounded to bf16, no scale
+        const uint32_t kw = f32_to_bf16_bits(k0) | (f32_to_bf16_bits(k1) << 16);
+        const uint32_t vw = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+        if (store && slot >= 0 && slot < a.num_blocks * 128)
+          store_token_bf16(a.k_cache_w, a.v_cache_w, a.hkv, slot, h, lane, kw, vw);
+        if (!attend) return;
+        kb = __builtin_bit_cast(bf16x2, kw);
+        vb = __builtin_bit_cast(bf16x2, vw);
+      } else {
+        const uint32_t kcode = quantize_pair(k0, k1, a.scale_mode, a.k_scale, &ks_t);
+        const uint32_t vcode = quantize_pair(v0, v1, a.scale_mode, a.v_scale, &vs_t);
+        if (store && slot >= 0 && slot < a.num_blocks * 128)
+          store_token_fp8(a.k_cache_w, a.v_cache_w, a.k_scale_w, a.v_scale_w, a.hkv, a.scale_mode, slot, h, lane,
+                          kcode, vcode, ks_t, vs_t);
+        if (!attend) return;
+        kb = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kcode, 1.0f, false);
+        vb = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vcode, 1.0f, false);
+      }
       const int pos = fz_ctx - fz_L + j;
       if (pos < 0 || pos >= cap) return;  // not attended (uniform)
-      const bf16x2 kb = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kcode, 1.0f, false);
-      const bf16x2 vb = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vcode, 1.0f, false);
       // the previous token's reads of these rows are done before they change
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -1171,14 +1182,15 @@ void launch_main_t(const DecodeArgs& a, int64_t grid, hipStream_t s, hipEvent_t 
 template <int RT, bool PT, bool SP, bool BF = false>
 void launch_shape(const DecodeArgs& a, int depth, int waves, int64_t grid, hipStream_t s, hipEvent_t e0,
                   hipEvent_t e1) {
-  if constexpr (SP && !BF) {
+  if constexpr (SP) {
     // the sparse fused write (single-row requests): four waves, the two-page ring
-    if (a.fused) return launch_main_t<1, PT, true, 2, 4, false, true>(a, grid, s, e0, e1);
-  }
-  if constexpr (!SP && !BF) {
-    // the fused write: the two-page ring at either width
+    if (a.fused) return launch_main_t<1, PT, true, 2, 4, BF, true>(a, grid, s, e0, e1);
+  } else {
+    // the fused write: the two-page ring at either width (two-row bf16: four waves)
     if (a.fused) {
-      if (waves == 8) return launch_main_t<RT, PT, SP, 2, 8, BF, true>(a, grid, s, e0, e1);
+      if constexpr (!(BF && RT == 2)) {
+        if (waves == 8) return launch_main_t<RT, PT, SP, 2, 8, BF, true>(a, grid, s, e0, e1);
+      }
       return launch_main_t<RT, PT, SP, 2, 4, BF, true>(a, grid, s, e0, e1);
     }
   }

@@ -86,4 +86,44 @@ __device__ __forceinline__ void store_token_fp8(uint8_t* k_cache, uint8_t* v_cac
   }
 }
 
+// fp32 -> bf16 bits: round to nearest, ties to even, on the 16 dropped
+// bits; NaN stays NaN (quiet bit set, sign kept).  Integer work, so the
+// stored bits do not depend on a conversion instruction's NaN handling.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// The unquantized cache: stores this lane's two K and two V elements
+// (kb, vb: bf16 bits, low half = even dim) of token slot `slot` for KV
+// head h in the bf16 page layout (the FP8 pages' chunking, 8 elements per
+// 16-byte operand piece).  K: the two dims are adjacent elements; V: they
+// sit in pieces 8 elements apart.
+__device__ __forceinline__ void store_token_bf16(uint8_t* k_cache, uint8_t* v_cache, int hkv, int64_t slot, int h,
+                                                 int lane, uint32_t kb, uint32_t vb) {
+  const int64_t page = slot >> 7;
+  const int o = int(slot & 127);
+  const int64_t blk = (page * hkv + h) * int64_t(16384);
+  uint16_t* kc = reinterpret_cast<uint16_t*>(k_cache) + blk;
+  uint16_t* vc = reinterpret_cast<uint16_t*>(v_cache) + blk;
+  const int c = o >> 5, tau = (o >> 4) & 1;
+  {
+    const int d = 2 * lane;
+    const int j = d >> 5, g = (d >> 3) & 3, u = d & 7, r = o & 15;
+    const int off = 4096 * c + 512 * (4 * tau + j) + 8 * (16 * g + r) + u;
+    *reinterpret_cast<uint32_t*>(kc + off) = kb;
+  }
+  {
+    const int w = o & 15, g = w >> 2, e = 4 * tau + (w & 3);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int d = 2 * lane + s;
+      const int delta = d >> 4, r = d & 15;
+      const int off = 4096 * c + 512 * delta + 8 * (16 * g + r) + e;
+      vc[off] = uint16_t(vb >> (16 * s));
+    }
+  }
+}
+
 }  // namespace fp8pa

@@ -377,18 +377,19 @@ int kv_quant_write(const pa_tensor* k_new, const pa_tensor* v_new,
  *   pos%128, >= 0).  context_lens counts the new tokens.
  *   k_cache, v_cache, k_scale, v_scale are written (as kv_quant_write) and
  *   read (as pa_decode).
- * Behaviour: dense FP8 calls (PER_TOKEN, SCALAR or NONE) whose requests hold
- * at most PA_FUSED_WRITE_MAX_Q_LEN rows (uniform split, or max_q_len given
- * in opts for a ragged call) run as one decode launch (plus the merge when
- * split): the workgroups of each request's last partition quantize its new
- * tokens, row group 0 stores them, and every row attends them from
- * registers while the page stream covers the older positions.  Block-sparse
- * calls (sparse_page_idx as in pa_decode) whose requests are single rows
- * run the same way: partition 0 of each row stores its token, and the row
- * attends it only if the token's page is on its list, as the row would
- * after a separate write.  Every other call (a bf16 cache, longer or
- * unknown q_len, multi-row sparse calls) runs kv_quant_write and then
- * pa_decode_ex, with the same results.  Errors: everything the two calls
+ * Behaviour: dense calls (FP8 with PER_TOKEN, SCALAR or NONE scales, or a
+ * bf16 cache) whose requests hold at most PA_FUSED_WRITE_MAX_Q_LEN rows
+ * (uniform split, or max_q_len given in opts for a ragged call) run as one
+ * decode launch (plus the merge when split): the workgroups of each
+ * request's last partition quantize (bf16 cache: round) its new tokens,
+ * row group 0 stores them, and every row attends them from registers while
+ * the page stream covers the older positions.  Block-sparse calls
+ * (sparse_page_idx as in pa_decode) whose requests are single rows run the
+ * same way: partition 0 of each row stores its token, and the row attends
+ * it only if the token's page is on its list, as the row would after a
+ * separate write.  Every other call (longer or unknown q_len, multi-row
+ * sparse calls, a forced prefetch depth above 2) runs kv_quant_write and
+ * then pa_decode_ex, with the same results.  Errors: everything the two calls
  * check, plus T != rows (PA_ERR_SHAPE), all before any launch.  Slot
  * preconditions that only device memory shows are the caller's: a slot
  * that does not match its position gives a cache and an output that differ

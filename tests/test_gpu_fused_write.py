@@ -15,8 +15,9 @@ The cases cover one-row and two-row workgroups, uniform, odd and ragged
 q_len, new tokens across a page boundary, requests made only of new tokens,
 the scalar and no-scale modes, two KV heads, bf16 inputs, forced and
 balanced partitions, the in-kernel merge, more new tokens than waves, and
-the calls that run unfused (q_len above the fused limit, a bf16 cache,
-block-sparse calls with several rows per request), and block-sparse single-row calls (partition 0 stores each row's token; the
+the calls that run unfused (q_len above the fused limit, block-sparse
+calls with several rows per request), the bf16 cache (the new tokens
+rounded to bf16 and stored in the same launch), and block-sparse single-row calls (partition 0 stores each row's token; the
 row attends it only if its page is on the row's list, as after a separate
 write), with the new token first in its page and rows whose list leaves
 that page out."""
@@ -162,30 +163,71 @@ def test_unfused_fallbacks():
     _check_step(w, what="sparse ragged", runs=({},))
 
 
-def test_unfused_bf16_cache():
-    w = wl.bf16_kv(wl.small_case(seed=413, ctx=[500, 260], q_lens=[2, 2]))
-    case = GpuCase(w)
-    ref_sep = case.decode(out=torch.empty_like(case.out))
-    torch.cuda.synchronize()
-    full = [case.kc.view(torch.int16).clone(), case.vc.view(torch.int16).clone()]
-    k, v, s = w.step_tokens()
-    kt = torch.from_numpy(k).to(case.dev)
-    vt = torch.from_numpy(v).to(case.dev)
-    st = torch.from_numpy(s).to(case.dev)
-    # overwrite the new tokens' elements with a pattern, then write them back through the call
-    for s1 in s:
+BF16_CASES = [
+    dict(seed=413, ctx=[500, 260], q_lens=[2, 2]),                              # two-row (four waves)
+    dict(seed=417, ctx=[300, 513], q_lens=[1, 1]),                              # one-row, two tails
+    dict(seed=418, ctx=[800, 500, 300, 90], q_lens=[4, 1, 6, 2], ragged=True),  # ragged
+    dict(seed=419, ctx=[600, 2000], q_lens=[16, 16]),                           # more new tokens than waves
+    dict(seed=420, ctx=[400, 131], q_lens=[3, 3], Hkv=2),                       # new tokens cross a page
+    dict(seed=421, ctx=[700, 1300, 513], q_lens=[1, 1, 1], sparse_topk=3),      # block-sparse
+]
+
+
+def _bf16_slots_elements(kc16, vc16, w, slots):
+    """The K and V elements of the new tokens' slots (every head, every dim)."""
+    d = np.arange(128)
+    ki, vi = [], []
+    for s1 in slots:
         page, o = divmod(int(s1), 128)
         for h in range(w.Hkv):
             base = (page * w.Hkv + h) * 16384
-            idx = torch.from_numpy((base + olay.k_offset_bf16(o, np.arange(128))).astype(np.int64)).to(case.dev)
-            case.kc.view(torch.int16).view(-1)[idx] = 0x1234
-            idx = torch.from_numpy((base + olay.v_offset_bf16(o, np.arange(128))).astype(np.int64)).to(case.dev)
-            case.vc.view(torch.int16).view(-1)[idx] = 0x1234
-    out = _run(case, w, kt, vt, st, torch.empty_like(case.out))
+            ki.append(base + olay.k_offset_bf16(o, d))
+            vi.append(base + olay.v_offset_bf16(o, d))
+    ki, vi = np.concatenate(ki), np.concatenate(vi)
+    return kc16[ki], vc16[vi], ki, vi
+
+
+@pytest.mark.parametrize("in_dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("kw", BF16_CASES, ids=[str(c["seed"]) for c in BF16_CASES])
+def test_fused_write_bf16_cache(kw, in_dtype):
+    """The unquantized cache: the new tokens are rounded to bf16 and stored
+    inside the decode launch, bit-equal to kv_quant_write's and the oracle
+    writer's elements."""
+    w = wl.bf16_kv(wl.small_case(**kw))
+    case = GpuCase(w, in_dtype=in_dtype)
+    mq = int(w.q_lens.max()) if w.cu is not None else 0
+    ref_sep = case.decode(out=torch.empty_like(case.out), max_q_len=mq)
     torch.cuda.synchronize()
-    assert torch.equal(case.kc.view(torch.int16), full[0]) and torch.equal(case.vc.view(torch.int16), full[1])
-    compare(out, oracle_out(w), what="bf16 cache vs oracle")
-    compare(out, ref_sep.float().cpu().numpy(), atol=4e-3, cos_min=0.99999, what="bf16 cache vs separate")
+    full = [case.kc.view(torch.int16).clone(), case.vc.view(torch.int16).clone()]
+    okc, ovc = oracle_cache(w)[:2]
+    ref64 = oracle_out(w)
+    k, v, s = w.step_tokens()
+    kt = torch.from_numpy(k).to(case.dev).to(in_dtype)
+    vt = torch.from_numpy(v).to(case.dev).to(in_dtype)
+    st = torch.from_numpy(s).to(case.dev)
+    ok_new, ov_new, ki, vi = _bf16_slots_elements(okc, ovc, w, s)
+    kit = torch.from_numpy(ki.astype(np.int64)).to(case.dev)
+    vit = torch.from_numpy(vi.astype(np.int64)).to(case.dev)
+    runs = [{}, dict(force_parts=1), dict(force_parts=3)]
+    if int(w.q_lens.max()) == 1 and w.sparse is None:
+        runs.append(dict(workgroup_waves=8))
+    for kwr in runs:
+        tag = f"{w.name} bf16 cache, {in_dtype} inputs, {kwr}"
+        print("fused write case", tag, flush=True)
+        # overwrite the new tokens' elements with a pattern; the call writes them back
+        case.kc.view(torch.int16).view(-1)[kit] = 0x1234
+        case.vc.view(torch.int16).view(-1)[vit] = 0x1234
+        torch.cuda.synchronize()
+        out = _run(case, w, kt, vt, st, torch.empty_like(case.out), **kwr)
+        torch.cuda.synchronize()
+        assert torch.equal(case.kc.view(torch.int16), full[0]), f"{tag}: K differs from kv_quant_write's"
+        assert torch.equal(case.vc.view(torch.int16), full[1]), f"{tag}: V differs from kv_quant_write's"
+        g = case.kc.view(torch.int16).view(-1)[kit].cpu().numpy().view(np.uint16)
+        assert np.array_equal(g, ok_new), f"{tag}: new K elements vs the oracle writer"
+        g = case.vc.view(torch.int16).view(-1)[vit].cpu().numpy().view(np.uint16)
+        assert np.array_equal(g, ov_new), f"{tag}: new V elements vs the oracle writer"
+        compare(out, ref64, what=f"{tag} vs oracle")
+        compare(out, ref_sep.float().cpu().numpy(), atol=4e-3, cos_min=0.99999, what=f"{tag} vs separate calls")
 
 
 def test_fused_write_refuses_before_launch():

@@ -479,28 +479,35 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   }
   // Fused write: the partition holding the request's last attended position
   // takes the new tokens.  Each wave's first new token is loaded ahead of
-  // the page stream, so it has arrived by the time the wave handles it,
-  // under the first pages' latency.
+  // the page stream, quantized and stored while the first pages load, and
+  // attended after the stream.  The loads are issued by every wave (a wave
+  // past the request's tokens reloads its last one), so the compiler counts
+  // them exactly and waits for them alone.
   bool fz_last = false;
   float fk0 = 0.f, fk1 = 0.f, fv0 = 0.f, fv1 = 0.f;
   int64_t fslot = -1;
   // Sparse: which partition holds the new token's page is known only from
-  // the list, so wave 0 of every workgroup loads the token; partition 0
+  // the list, so wave 0 of every workgroup takes the token; partition 0
   // stores it, and the workgroup whose stream passes its page attends it.
   const int fz_page_base = (fz_ctx - 1) >> 7 << 7;  // token base of the new token's page (sparse)
   bool fz_seen = false;
+  float fz_ksc = 1.0f, fz_vsc = 1.0f;  // SCALAR mode: the caller's scales (scalar loads)
   if constexpr (FW) {
     const int ctx_cap = min(fz_ctx, a.width * 128);
     const int pl = (ctx_cap - 1) >> 7;
     fz_last = ctx_cap > 0 && n0 <= pl && pl < n0 + ppp;
-    if ((SPARSE || fz_last) && wave < fz_L) {
-      const int64_t t = fz_start + wave;
-      load_pair(a.k_new, t * a.kn_tok_stride + h * a.kn_head_stride + 2 * lane, a.kn_bf16, &fk0, &fk1);
-      load_pair(a.v_new, t * a.vn_tok_stride + h * a.vn_head_stride + 2 * lane, a.kn_bf16, &fv0, &fv1);
-      fslot = a.slots[t];
+    const int64_t t = fz_start + min(wave, max(fz_L, 1) - 1);
+    load_pair(a.k_new, t * a.kn_tok_stride + h * a.kn_head_stride + 2 * lane, a.kn_bf16, &fk0, &fk1);
+    load_pair(a.v_new, t * a.vn_tok_stride + h * a.vn_head_stride + 2 * lane, a.kn_bf16, &fv0, &fv1);
+    fslot = a.slots[t];
+    if (!BF && a.scale_mode == PA_SCALE_SCALAR) {
+      fz_ksc = __int_as_float(as_const(reinterpret_cast<const int32_t*>(a.k_scale))[0]);
+      fz_vsc = __int_as_float(as_const(reinterpret_cast<const int32_t*>(a.v_scale))[0]);
     }
   }
   const bool fz_pend = fz_last && wave < fz_L;  // this wave has a first new token
+  // the wave that quantizes and stores its first token before the stream
+  const bool fz_mine = SPARSE ? wave == 0 : fz_pend;
 
   // The partition's first chunk and the query operands do not depend on the
   // context length: issue their loads now, so they travel together with the
@@ -811,32 +818,44 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   // (two dims per lane) to the score layout (the query operand's dims) and
   // the accumulator layout, a few values at a time.  Scores and weights are
   // fp32: the token's K scale multiplies its score, its V scale its weight,
-  // as in the page stream.  It runs after the page stream: inside its first
-  // step (under that step's loads) the one-row kernel measured 11-14 us
-  // slower at 128K, and the two-row kernel has no registers to spare there.
-  auto new_token = [&](int j, float k0, float k1, float v0, float v1, int64_t slot, bool store, bool attend) {
+  // as in the page stream.  A wave's first token is quantized and stored
+  // before the page stream (under the first pages' loads) and folded in
+  // after it; folding it inside the stream's first step measured slower
+  // (more registers live through the loop).
+  // Quantize (bf16 cache: round) this lane's two K and two V values of a
+  // new token and store them if asked; returns the stored values: FP8 codes
+  // (low 16 bits) or bf16 pairs, and the scales through ks_t, vs_t.
+  auto write_token = [&](float k0, float k1, float v0, float v1, int64_t slot, bool store, uint32_t* kw,
+                         uint32_t* vw, float* ks_t, float* vs_t) __attribute__((always_inline)) {
     if constexpr (FW) {
-      float* lds = &sm_acc[wave][0][0];  // 256 floats: the K codes' values, then V's
-      float ks_t = 1.0f, vs_t = 1.0f;
-      bf16x2 kb, vb;  // the stored values: the dequantized codes, or the bf16 elements
       if constexpr (BF) {
         // the unquantized cache: the elements rounded to bf16, no scale
-        const uint32_t kw = f32_to_bf16_bits(k0) | (f32_to_bf16_bits(k1) << 16);
-        const uint32_t vw = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+        *kw = f32_to_bf16_bits(k0) | (f32_to_bf16_bits(k1) << 16);
+        *vw = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+        *ks_t = *vs_t = 1.0f;
         if (store && slot >= 0 && slot < a.num_blocks * 128)
-          store_token_bf16(a.k_cache_w, a.v_cache_w, a.hkv, slot, h, lane, kw, vw);
-        if (!attend) return;
+          store_token_bf16(a.k_cache_w, a.v_cache_w, a.hkv, slot, h, lane, *kw, *vw);
+      } else {
+        *kw = quantize_pair_v(k0, k1, a.scale_mode, fz_ksc, ks_t);
+        *vw = quantize_pair_v(v0, v1, a.scale_mode, fz_vsc, vs_t);
+        if (store && slot >= 0 && slot < a.num_blocks * 128)
+          store_token_fp8(a.k_cache_w, a.v_cache_w, a.k_scale_w, a.v_scale_w, a.hkv, a.scale_mode, slot, h, lane,
+                          *kw, *vw, *ks_t, *vs_t);
+      }
+    }
+  };
+  // Fold new token j (values as write_token returned them) into the rows
+  // that see it.
+  auto fold_token = [&](int j, uint32_t kw, uint32_t vw, float ks_t, float vs_t) __attribute__((always_inline)) {
+    if constexpr (FW) {
+      float* lds = &sm_acc[wave][0][0];  // 256 floats: the K codes' values, then V's
+      bf16x2 kb, vb;  // the stored values: the dequantized codes, or the bf16 elements
+      if constexpr (BF) {
         kb = __builtin_bit_cast(bf16x2, kw);
         vb = __builtin_bit_cast(bf16x2, vw);
       } else {
-        const uint32_t kcode = quantize_pair(k0, k1, a.scale_mode, a.k_scale, &ks_t);
-        const uint32_t vcode = quantize_pair(v0, v1, a.scale_mode, a.v_scale, &vs_t);
-        if (store && slot >= 0 && slot < a.num_blocks * 128)
-          store_token_fp8(a.k_cache_w, a.v_cache_w, a.k_scale_w, a.v_scale_w, a.hkv, a.scale_mode, slot, h, lane,
-                          kcode, vcode, ks_t, vs_t);
-        if (!attend) return;
-        kb = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kcode, 1.0f, false);
-        vb = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vcode, 1.0f, false);
+        kb = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw, 1.0f, false);
+        vb = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vw, 1.0f, false);
       }
       const int pos = fz_ctx - fz_L + j;
       if (pos < 0 || pos >= cap) return;  // not attended (uniform)
@@ -891,6 +910,26 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       }
     }
   };
+  auto new_token = [&](int j, float k0, float k1, float v0, float v1, int64_t slot, bool store)
+                       __attribute__((always_inline)) {
+    uint32_t kw, vw;
+    float ks_t, vs_t;
+    write_token(k0, k1, v0, v1, slot, store, &kw, &vw, &ks_t, &vs_t);
+    fold_token(j, kw, vw, ks_t, vs_t);
+  };
+
+  // One-row workgroups: the wave's first new token is quantized and stored
+  // now, while the first pages load (its loads were issued first, so the
+  // wait is for them alone), and attended after the stream.  Two-row
+  // workgroups (two waves per SIMD, registers full) do both after the
+  // stream: measured, their step was 0.7 us longer this way.
+  constexpr bool kEarlyWrite = RT == 1;
+  uint32_t fz_kw = 0, fz_vw = 0;
+  float fz_ks = 1.0f, fz_vs = 1.0f;
+  if constexpr (FW && kEarlyWrite) {
+    if (fz_mine)
+      write_token(fk0, fk1, fv0, fv1, fslot, SPARSE ? part == 0 : fz_i0 == 0, &fz_kw, &fz_vw, &fz_ks, &fz_vs);
+  }
 
   // ---- stream the partition's pages: a ring of NBUF chunk buffers, the
   // loads of the next NBUF-1 pages in flight while one is processed.  Table
@@ -934,19 +973,23 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   }
 
   if constexpr (FW && SPARSE) {
-    // the row's one new token: stored by partition 0, attended here if this
-    // workgroup's stream passed its page
-    if (wave == 0 && (part == 0 || fz_seen)) new_token(0, fk0, fk1, fv0, fv1, fslot, part == 0, fz_seen);
+    // the row's one new token (stored by partition 0 before the stream),
+    // attended here if this workgroup's stream passed its page
+    if (wave == 0 && fz_seen) fold_token(0, fz_kw, fz_vw, fz_ks, fz_vs);
   } else if constexpr (FW) {
     // row group 0 of the last partition stores each new token once
-    if (fz_pend) new_token(wave, fk0, fk1, fv0, fv1, fslot, fz_i0 == 0, true);
+    if constexpr (kEarlyWrite) {
+      if (fz_pend) fold_token(wave, fz_kw, fz_vw, fz_ks, fz_vs);
+    } else {
+      if (fz_pend) new_token(wave, fk0, fk1, fv0, fv1, fslot, fz_i0 == 0);
+    }
     if (fz_last) {
       for (int j = wave + NW; j < fz_L; j += NW) {
         const int64_t t = fz_start + j;
         float k0, k1, v0, v1;
         load_pair(a.k_new, t * a.kn_tok_stride + h * a.kn_head_stride + 2 * lane, a.kn_bf16, &k0, &k1);
         load_pair(a.v_new, t * a.vn_tok_stride + h * a.vn_head_stride + 2 * lane, a.kn_bf16, &v0, &v1);
-        new_token(j, k0, k1, v0, v1, a.slots[t], fz_i0 == 0, true);
+        new_token(j, k0, k1, v0, v1, a.slots[t], fz_i0 == 0);
       }
     }
   }

@@ -31,8 +31,8 @@ __device__ __forceinline__ void load_pair(const void* base, int64_t off, int bf1
 
 // Quantize this lane's two values of one 128-wide row.  Returns the two
 // codes (low byte = even dim) and, through *scale_out, the stored scale.
-__device__ __forceinline__ uint32_t quantize_pair(float x0, float x1, int mode, const float* scalar,
-                                                  float* scale_out) {
+// `scalar` is the caller's scale in SCALAR mode (unused otherwise).
+__device__ __forceinline__ uint32_t quantize_pair_v(float x0, float x1, int mode, float scalar, float* scale_out) {
   float s = 1.0f;
   bool divide = false;
   if (mode == PA_SCALE_PER_TOKEN) {
@@ -40,7 +40,7 @@ __device__ __forceinline__ uint32_t quantize_pair(float x0, float x1, int mode, 
     s = amax / 448.0f;  // IEEE fp32 division
     divide = s != 0.0f;
   } else if (mode == PA_SCALE_SCALAR) {
-    s = *scalar;
+    s = scalar;
     divide = true;
   }
   float y0 = x0, y1 = x1;
@@ -50,6 +50,12 @@ __device__ __forceinline__ uint32_t quantize_pair(float x0, float x1, int mode, 
   }
   *scale_out = s;
   return f32_to_e4m3(y0) | (f32_to_e4m3(y1) << 8);
+}
+
+// The same, reading the SCALAR-mode scale from `scalar`.
+__device__ __forceinline__ uint32_t quantize_pair(float x0, float x1, int mode, const float* scalar,
+                                                  float* scale_out) {
+  return quantize_pair_v(x0, x1, mode, mode == PA_SCALE_SCALAR ? *scalar : 1.0f, scale_out);
 }
 
 // Stores this lane's two codes of token slot `slot` (page slot >> 7, offset

@@ -12,7 +12,7 @@ pa_decode_write:
     decode tolerance (max|err| <= 1e-2 where |ref| < 4, 2^-7|ref| above,
     cosine >= 0.9999), and the separate writer + decode calls to 4e-3.
 The cases cover one-row and two-row workgroups, uniform, odd and ragged
-q_len, new tokens across a page boundary, requests made only of new tokens,
+q_len (also with an empty request), new tokens across a page boundary, requests made only of new tokens,
 the scalar and no-scale modes, two KV heads, bf16 inputs, forced and
 balanced partitions, the in-kernel merge, more new tokens than waves, and
 the calls that run unfused (q_len above the fused limit, block-sparse
@@ -45,6 +45,8 @@ CASES = [
     dict(seed=407, ctx=[640, 129], q_lens=[2, 2], mode=wl.NONE),
     dict(seed=408, ctx=[400, 131], q_lens=[2, 2], Hkv=2),
     dict(seed=409, ctx=[600, 2000], q_lens=[16, 16]),                           # more new tokens than waves
+    dict(seed=440, ctx=[300, 50, 513], q_lens=[1, 0, 1], ragged=True),          # one-row, an empty request
+    dict(seed=441, ctx=[700, 90, 260], q_lens=[2, 0, 3], ragged=True),          # two-row, an empty request
 ]
 
 

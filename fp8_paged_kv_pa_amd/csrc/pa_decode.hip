@@ -342,8 +342,9 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   static_assert(!ONCE2 || RT == 2, "one-row workgroups always load non-temporally");
   constexpr bool kOnce = RT == 1 || ONCE2;
   static_assert(NW * 16 * kAccPad >= 16 * kMaxMergeParts, "merge weights reuse the wave-merge LDS");
+  static_assert((kWave * NW) % 256 == 0, "the combine takes 256 threads per row");
   __shared__ float sm_ml[NW][RT][16][2];
-  __shared__ float sm_acc[NW][16][kAccPad];
+  __shared__ float sm_acc[RT][NW][16][kAccPad];  // per row, per wave
   constexpr int S = NW / 4;  // pages streamed side by side (one per group of four waves)
   const int lane = threadIdx.x & (kWave - 1);
   // wave index as a provably uniform (scalar) value: table reads indexed by
@@ -567,7 +568,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       if (a.unit_count) store_coherent(a.part_ml + 2 * pi, -INFINITY, 0.0f);
       else *reinterpret_cast<float2*>(a.part_ml + 2 * pi) = float2{-INFINITY, 0.0f};
     }
-    if (a.unit_count) merge_if_last(a, unit, row0, nrows, h, &sm_acc[0][0][0]);
+    if (a.unit_count) merge_if_last(a, unit, row0, nrows, h, &sm_acc[0][0][0][0]);
     return;
   }
 
@@ -848,7 +849,7 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   // that see it.
   auto fold_token = [&](int j, uint32_t kw, uint32_t vw, float ks_t, float vs_t) __attribute__((always_inline)) {
     if constexpr (FW) {
-      float* lds = &sm_acc[wave][0][0];  // 256 floats: the K codes' values, then V's
+      float* lds = &sm_acc[0][wave][0][0];  // 256 floats: the K codes' values, then V's
       bf16x2 kb, vb;  // the stored values: the dequantized codes, or the bf16 elements
       if constexpr (BF) {
         kb = __builtin_bit_cast(bf16x2, kw);
@@ -995,12 +996,11 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   }
 
   // ---- merge the waves, then write output or the partition partial --------
-  // Per row, every wave leaves its (max, sum) and its unscaled accumulators
-  // in LDS; after one barrier each thread of the first 256 weights the
-  // waves' accumulators of its (head, 8 dims) by 2^(m_w - max) and sums them.
+  // Every wave leaves each row's (max, sum) and unscaled accumulators in
+  // LDS; after one barrier, 256 threads per row (a workgroup of 256 takes
+  // the rows in turn) weight the waves' accumulators of their (head, 8
+  // dims) by 2^(m_w - max) and sum them.
   const int t = threadIdx.x;
-  const int oh = (t >> 4) & 15;  // output head handled by this thread (threads < 256)
-  const int od = (t & 15) * 8;   // first of its 8 dims
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     if (r >= nrows) break;
@@ -1012,9 +1012,13 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
       sm_ml[wave][r][hr][1] = lh;
     }
 #pragma unroll
-    for (int d = 0; d < 8; ++d) *reinterpret_cast<f32x4*>(&sm_acc[wave][hr][16 * d + 4 * g]) = acc[r][d];
-    __syncthreads();
-    if (t < 256) {
+    for (int d = 0; d < 8; ++d) *reinterpret_cast<f32x4*>(&sm_acc[r][wave][hr][16 * d + 4 * g]) = acc[r][d];
+  }
+  __syncthreads();
+  const int oh = (t >> 4) & 15;  // output head handled by this thread
+  const int od = (t & 15) * 8;   // first of its 8 dims
+  for (int r = t >> 8; r < nrows; r += (kWave * NW) >> 8) {
+    {
       float mw[NW];
       float Mo = -INFINITY;
 #pragma unroll
@@ -1029,8 +1033,8 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
         // a wave that saw no token has m = -inf: weight 0
         const float fw = (Mo == -INFINITY || mw[w] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - Mo);
         Ls += fw * sm_ml[w][r][oh][1];
-        s0v += fw * *reinterpret_cast<const f32x4*>(&sm_acc[w][oh][od]);
-        s1v += fw * *reinterpret_cast<const f32x4*>(&sm_acc[w][oh][od + 4]);
+        s0v += fw * *reinterpret_cast<const f32x4*>(&sm_acc[r][w][oh][od]);
+        s1v += fw * *reinterpret_cast<const f32x4*>(&sm_acc[r][w][oh][od + 4]);
       }
       const int row = row0 + r;
       const int qh = 16 * h + oh;
@@ -1066,9 +1070,9 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
         }
       }
     }
-    __syncthreads();
   }
-  if (a.parts > 1 && a.unit_count) merge_if_last(a, unit, row0, nrows, h, &sm_acc[0][0][0]);
+  // (merge_if_last starts with a barrier before it reuses the LDS)
+  if (a.parts > 1 && a.unit_count) merge_if_last(a, unit, row0, nrows, h, &sm_acc[0][0][0][0]);
 }
 
 // One wavefront per (row, query head): combine the partitions' (m, l, acc)

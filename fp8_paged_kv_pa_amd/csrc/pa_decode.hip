@@ -1018,55 +1018,53 @@ __global__ __launch_bounds__(kWave * NW, (kMinBlocks<RT, NW == 4 && NBUF <= 2, B
   const int oh = (t >> 4) & 15;  // output head handled by this thread
   const int od = (t & 15) * 8;   // first of its 8 dims
   for (int r = t >> 8; r < nrows; r += (kWave * NW) >> 8) {
-    {
-      float mw[NW];
-      float Mo = -INFINITY;
+    float mw[NW];
+    float Mo = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        mw[w] = sm_ml[w][r][oh][0];
-        Mo = fmaxf(Mo, mw[w]);
+    for (int w = 0; w < NW; ++w) {
+      mw[w] = sm_ml[w][r][oh][0];
+      Mo = fmaxf(Mo, mw[w]);
+    }
+    float Ls = 0.0f;
+    f32x4 s0v = {0.f, 0.f, 0.f, 0.f}, s1v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      // a wave that saw no token has m = -inf: weight 0
+      const float fw = (Mo == -INFINITY || mw[w] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - Mo);
+      Ls += fw * sm_ml[w][r][oh][1];
+      s0v += fw * *reinterpret_cast<const f32x4*>(&sm_acc[r][w][oh][od]);
+      s1v += fw * *reinterpret_cast<const f32x4*>(&sm_acc[r][w][oh][od + 4]);
+    }
+    const int row = row0 + r;
+    const int qh = 16 * h + oh;
+    if (!to_partial) {
+      const float inv = Ls > 0.0f ? v_fold / Ls : 0.0f;
+      uint32_t packed[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        packed[e] = uint32_t(f32_to_bf16_rne(s0v[2 * e] * inv)) |
+                    (uint32_t(f32_to_bf16_rne(s0v[2 * e + 1] * inv)) << 16);
+        packed[2 + e] = uint32_t(f32_to_bf16_rne(s1v[2 * e] * inv)) |
+                        (uint32_t(f32_to_bf16_rne(s1v[2 * e + 1] * inv)) << 16);
       }
-      float Ls = 0.0f;
-      f32x4 s0v = {0.f, 0.f, 0.f, 0.f}, s1v = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        // a wave that saw no token has m = -inf: weight 0
-        const float fw = (Mo == -INFINITY || mw[w] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - Mo);
-        Ls += fw * sm_ml[w][r][oh][1];
-        s0v += fw * *reinterpret_cast<const f32x4*>(&sm_acc[r][w][oh][od]);
-        s1v += fw * *reinterpret_cast<const f32x4*>(&sm_acc[r][w][oh][od + 4]);
-      }
-      const int row = row0 + r;
-      const int qh = 16 * h + oh;
-      if (!to_partial) {
-        const float inv = Ls > 0.0f ? v_fold / Ls : 0.0f;
-        uint32_t packed[4];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          packed[e] = uint32_t(f32_to_bf16_rne(s0v[2 * e] * inv)) |
-                      (uint32_t(f32_to_bf16_rne(s0v[2 * e + 1] * inv)) << 16);
-          packed[2 + e] = uint32_t(f32_to_bf16_rne(s1v[2 * e] * inv)) |
-                          (uint32_t(f32_to_bf16_rne(s1v[2 * e + 1] * inv)) << 16);
-        }
-        uint16_t* op = a.out + int64_t(row) * a.out_row_stride + int64_t(qh) * a.out_head_stride + od;
-        *reinterpret_cast<u32x4*>(op) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+      uint16_t* op = a.out + int64_t(row) * a.out_row_stride + int64_t(qh) * a.out_head_stride + od;
+      *reinterpret_cast<u32x4*>(op) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    } else {
+      const int64_t pi = (prow0 + r) * Hq + qh;
+      if (a.unit_count) {
+        float* ap = a.part_acc + pi * 128 + od;
+        store_coherent(ap, s0v[0], s0v[1]);
+        store_coherent(ap + 2, s0v[2], s0v[3]);
+        store_coherent(ap + 4, s1v[0], s1v[1]);
+        store_coherent(ap + 6, s1v[2], s1v[3]);
+        if ((t & 15) == 0) store_coherent(a.part_ml + 2 * pi, Mo, Ls);
       } else {
-        const int64_t pi = (prow0 + r) * Hq + qh;
-        if (a.unit_count) {
-          float* ap = a.part_acc + pi * 128 + od;
-          store_coherent(ap, s0v[0], s0v[1]);
-          store_coherent(ap + 2, s0v[2], s0v[3]);
-          store_coherent(ap + 4, s1v[0], s1v[1]);
-          store_coherent(ap + 6, s1v[2], s1v[3]);
-          if ((t & 15) == 0) store_coherent(a.part_ml + 2 * pi, Mo, Ls);
-        } else {
-          f32x4* ap = reinterpret_cast<f32x4*>(a.part_acc + pi * 128 + od);
-          ap[0] = s0v;
-          ap[1] = s1v;
-          if ((t & 15) == 0) {
-            a.part_ml[2 * pi] = Mo;
-            a.part_ml[2 * pi + 1] = Ls;
-          }
+        f32x4* ap = reinterpret_cast<f32x4*>(a.part_acc + pi * 128 + od);
+        ap[0] = s0v;
+        ap[1] = s1v;
+        if ((t & 15) == 0) {
+          a.part_ml[2 * pi] = Mo;
+          a.part_ml[2 * pi + 1] = Ls;
         }
       }
     }

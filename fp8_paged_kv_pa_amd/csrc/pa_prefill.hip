@@ -46,6 +46,8 @@ constexpr int kPfPos = kPrefillPositions;  // query positions per workgroup
 constexpr int kPfWaves = 4;
 constexpr int kPfRing = 2;  // chunks in flight per lane beyond the one being staged
 constexpr int kPfOcc = 2;   // workgroups per CU (two waves per SIMD)
+constexpr int kPfRows = kPfPos / kPfWaves;  // query positions (16-head row tiles) per wave
+static_assert(kPfRows * kPfWaves == kPfPos, "every wave owns the same number of positions");
 constexpr float kPfLazy = 8.0f;  // log2 headroom before the running max moves
 
 // One chunk (32 tokens of a (page, KV head) block) in LDS, as bf16 operands:
@@ -105,8 +107,8 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
   const int cap = a.width * 128;
   // row i of the request sees tokens t < ctx - L + i + 1
   const int lim_group = max(0, min(ctx - L + i0 + npos, cap));  // the group's last row
-  const int wp = 2 * wave;                                       // the wave's first position in the group
-  const int nrows = max(0, min(2, npos - wp));
+  const int wp = kPfRows * wave;                                 // the wave's first position in the group
+  const int nrows = max(0, min(kPfRows, npos - wp));
   const int lim0 = ctx - L + i0 + wp + 1;                        // the wave's first row
   const int lim_w0 = max(0, min(lim0, cap));
   const int lim_w1 = max(0, min(lim0 + max(nrows, 1) - 1, cap));
@@ -125,9 +127,9 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
 
   // query operands: B of S^T = K Q^T, lane = (head hr, dims 8g..8g+7 of
   // each 32-dim k-step); a wave with one row computes a copy in its second
-  bf16x8 qop[2][4];
+  bf16x8 qop[kPfRows][4];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
+  for (int r = 0; r < kPfRows; ++r) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint16_t* qp = a.q + int64_t(row0 + min(r, max(nrows, 1) - 1)) * a.q_row_stride +
@@ -136,10 +138,10 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
     }
   }
 
-  f32x4 acc[2][8];
-  float m_run[2], l_run[2];
+  f32x4 acc[kPfRows][8];
+  float m_run[kPfRows], l_run[kPfRows];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
+  for (int r = 0; r < kPfRows; ++r) {
     m_run[r] = -INFINITY;
     l_run[r] = 0.0f;
 #pragma unroll
@@ -271,15 +273,15 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
         vsf[e] = 1.0f;
       }
     }
-    f32x4 st[2][2];
+    f32x4 st[kPfRows][2];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) st[r][0] = st[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < kPfRows; ++r) st[r][0] = st[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bf16x8 k0 = __builtin_bit_cast(bf16x8, s.k[j][lane]);
       const bf16x8 k1 = __builtin_bit_cast(bf16x8, s.k[4 + j][lane]);
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
+      for (int r = 0; r < kPfRows; ++r) {
         st[r][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[r][j], st[r][0], 0, 0, 0);
         st[r][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[r][j], st[r][1], 0, 0, 0);
       }
@@ -287,9 +289,9 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
 
     // online softmax per row; P' = p * v_scale as a bf16 hi + lo pair (hi
     // the top 8 significant bits by truncation, lo = P' - hi exact in fp32)
-    bf16x8 phi[2], plo[2];
+    bf16x8 phi[kPfRows], plo[kPfRows];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < kPfRows; ++r) {
       const float mu = (m_run[r] == -INFINITY) ? 0.0f : m_run[r];
       float x[8];
 #pragma unroll
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
     for (int d = 0; d < 8; ++d) {
       const bf16x8 vop = __builtin_bit_cast(bf16x8, s.v[d][lane]);
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
+      for (int r = 0; r < kPfRows; ++r) {
         acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi[r], acc[r][d], 0, 0, 0);
         acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[r], acc[r][d], 0, 0, 0);
       }
@@ -396,7 +398,7 @@ __global__ __launch_bounds__(kWave * kPfWaves, kPfOcc) void pa_prefill_main(Deco
 
   // ---- this wave's rows: bf16 output, or the partition's partial ---------
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
+  for (int r = 0; r < kPfRows; ++r) {
     if (r >= nrows) break;
     float lh = l_run[r];
     lh += __shfl_xor(lh, 16, kWave);  // the head's four lane groups hold its tokens' sums

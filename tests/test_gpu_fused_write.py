@@ -20,7 +20,8 @@ calls with several rows per request), the bf16 cache (the new tokens
 rounded to bf16 and stored in the same launch), and block-sparse single-row calls (partition 0 stores each row's token; the
 row attends it only if its page is on the row's list, as after a separate
 write), with the new token first in its page and rows whose list leaves
-that page out."""
+that page out; and the call captured in a graph and replayed over re-poisoned
+new-token slots."""
 
 import numpy as np
 import pytest
@@ -292,3 +293,79 @@ def test_fused_write_sparse(kw, drop):
         assert np.array_equal(after[1].cpu().numpy().reshape(-1), ocache[1].reshape(-1)), f"{tag}: V vs oracle"
         compare(out, ref64, what=f"{tag} vs oracle")
         compare(out, ref_sep.float().cpu().numpy(), atol=4e-3, cos_min=0.99999, what=f"{tag} vs separate calls")
+
+
+GRAPH_CASES = [
+    dict(seed=450, ctx=[1300, 700, 513], q_lens=[1, 1, 1]),                      # one-row: write before the stream
+    dict(seed=451, ctx=[900, 260], q_lens=[4, 4]),                               # two-row: write after the stream
+    dict(seed=452, ctx=[2000, 1300], q_lens=[1, 1], sparse_topk=4),              # block-sparse
+    dict(seed=453, ctx=[800, 333], q_lens=[1, 1], bf16=True),                    # bf16 cache
+]
+
+
+@pytest.mark.parametrize("kw", GRAPH_CASES, ids=[str(c["seed"]) for c in GRAPH_CASES])
+def test_fused_write_graph_replay(kw):
+    """pa_decode_write captured in a graph (scratch reserved first) and
+    replayed several times over a cache whose new-token slots are poisoned
+    again before each replay, with eager calls between the replays: every
+    replay leaves the cache kv_quant_write leaves and the eager output, bit
+    for bit."""
+    kw = dict(kw)
+    bf = kw.pop("bf16", False)
+    w = wl.small_case(**kw)
+    if bf:
+        w = wl.bf16_kv(w)
+    case = GpuCase(w)
+    k, v, s = w.step_tokens()
+    kt = torch.from_numpy(k).to(case.dev)
+    vt = torch.from_numpy(v).to(case.dev)
+    st = torch.from_numpy(s).to(case.dev)
+    if bf:
+        full = [case.kc.view(torch.int16).clone(), case.vc.view(torch.int16).clone()]
+        _, _, ki, vi = _bf16_slots_elements(np.zeros(case.kc.numel(), np.uint16),
+                                            np.zeros(case.vc.numel(), np.uint16), w, s)
+        kit = torch.from_numpy(ki.astype(np.int64)).to(case.dev)
+        vit = torch.from_numpy(vi.astype(np.int64)).to(case.dev)
+
+        def poison():
+            case.kc.view(torch.int16).view(-1)[kit] = 0x1234
+            case.vc.view(torch.int16).view(-1)[vit] = 0x1234
+
+        def cache_ok():
+            return torch.equal(case.kc.view(torch.int16), full[0]) and torch.equal(case.vc.view(torch.int16), full[1])
+    else:
+        full = _snapshot(case)
+
+        def poison():
+            _new_token_poison(case, w, s)
+
+        def cache_ok():
+            return all(torch.equal(a, b) for a, b in zip(_snapshot(case), full))
+    stream = torch.cuda.Stream()
+    cfg = pa.make_config(w.Hkv, w.rows, w.B, w.W, topk=0 if w.sparse is None else w.sparse.shape[1],
+                         scale_mode=w.mode, kv_dtype=3 if bf else 1)
+    pa.pa_reserve(cfg, stream)
+    print("fused write graph case", w.name, pa.pa_plan_describe(cfg)["rows_per_group"], flush=True)
+    poison()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        eager = _run(case, w, kt, vt, st, torch.empty_like(case.out)).clone()
+    torch.cuda.synchronize()
+    assert cache_ok(), "eager call: cache differs from kv_quant_write's"
+    compare(eager, oracle_out(w), what=f"{w.name} eager")
+    out = torch.empty_like(case.out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        _run(case, w, kt, vt, st, out)
+    for rep in range(3):
+        poison()
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert cache_ok(), f"replay {rep}: cache differs from kv_quant_write's"
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}: output"
+        with torch.cuda.stream(stream):
+            other = case.decode(out=torch.empty_like(case.out))
+        torch.cuda.synchronize()
+        compare(other, oracle_out(w), what=f"{w.name} eager decode between replays {rep}")

@@ -4,7 +4,10 @@ rows, context lengths drawn around page edges, and the plan options
 (partition mode, forced partition counts, workgroup width, prefetch depth,
 merge placement, the max_q_len hint), each drawn only where the option is
 served.  Every output element is held to max|err| <= 1e-2 and cosine >=
-0.9999, the tolerance stated for this path."""
+0.9999, the tolerance stated for this path.  Every draw (and every fourth
+over a bf16 cache) also runs as one pa_decode_write step from a cache whose
+new-token slots hold poison: the cache afterwards equals kv_quant_write's
+bit for bit."""
 
 import numpy as np
 import pytest
@@ -88,34 +91,61 @@ def test_random_call_over_a_bf16_cache_matches_oracle(seed):
     torch.cuda.synchronize()
     compare(out, oracle_out(w), what=f"random mix bf16 {seed} {opts}")
 
-DENSE_SEEDS = [s for s in SEEDS if draw(s)[0].sparse is None]
+def _write_step(w, opts, seed):
+    """One decode step through pa_decode_write from a cache whose new-token
+    slots hold poison: the cache after the call equals kv_quant_write's bit
+    for bit, and the output matches the oracle."""
+    from test_gpu_fused_write import _bf16_slots_elements, _new_token_poison, _snapshot
+
+    case = GpuCase(w)
+    k, v, s = w.step_tokens()
+    kt, vt, st = (torch.from_numpy(x).to(case.dev) for x in (k, v, s))
+    # the reference cache: every step token written by kv_quant_write too (a
+    # block-sparse workload writes only the pages its lists name, and a
+    # request's earlier new tokens can sit on a page before the listed last one)
+    pa.kv_quant_write(kt, vt, st, case.kc, case.vc, case.ks_arg, case.vs_arg, case.mode)
+    torch.cuda.synchronize()
+    if w.kv_dtype == "bf16":
+        full = [case.kc.view(torch.int16).clone(), case.vc.view(torch.int16).clone()]
+        _, _, ki, vi = _bf16_slots_elements(np.zeros(case.kc.numel(), np.uint16),
+                                            np.zeros(case.vc.numel(), np.uint16), w, s)
+        case.kc.view(torch.int16).view(-1)[torch.from_numpy(ki.astype(np.int64)).to(case.dev)] = 0x1234
+        case.vc.view(torch.int16).view(-1)[torch.from_numpy(vi.astype(np.int64)).to(case.dev)] = 0x1234
+        snap = lambda: [case.kc.view(torch.int16), case.vc.view(torch.int16)]
+    else:
+        full = _snapshot(case)
+        _new_token_poison(case, w, s)
+        snap = lambda: _snapshot(case)
+    out = torch.empty_like(case.out)
+    pa.pa_decode_write(case.q, kt, vt, st, case.kc, case.vc, case.ks_arg, case.vs_arg, case.bt,
+                       case.ctx, case.cu, case.mode, out, sparse_page_idx=case.sp, **opts)
+    torch.cuda.synchronize()
+    for a, b in zip(snap(), full):
+        assert torch.equal(a, b), f"random step {seed}: cache differs from kv_quant_write's"
+    compare(out, oracle_out(w), what=f"random step {seed} {opts}")
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("seed", DENSE_SEEDS)
+@pytest.mark.parametrize("seed", SEEDS)
 def test_random_step_with_the_write_inside_the_decode(seed):
-    """The dense draws as one decode step through pa_decode_write, from a
-    cache whose new-token slots hold poison: the cache after the call equals
-    kv_quant_write's bit for bit, and the output matches the oracle.  Draws
-    with a forced deeper ring or (ragged) no max_q_len hint run the writer
-    and the decode separately inside the call."""
-    from test_gpu_fused_write import _new_token_poison, _snapshot
-
+    """Every draw as one decode step through pa_decode_write.  Draws with a
+    forced deeper ring, (ragged) no max_q_len hint, more than 16 rows per
+    request or several rows per block-sparse request run the writer and the
+    decode separately inside the call; the rest write inside the decode."""
     w, opts = draw(seed)
     print("random step", seed, "B", w.B, "Hkv", w.Hkv, "mode", w.mode, "q_lens", list(w.q_lens), "ctx",
-          list(w.ctx), "opts", opts, flush=True)
-    case = GpuCase(w)
-    full = _snapshot(case)
-    k, v, s = w.step_tokens()
-    _new_token_poison(case, w, s)
-    out = torch.empty_like(case.out)
-    pa.pa_decode_write(case.q, torch.from_numpy(k).to(case.dev), torch.from_numpy(v).to(case.dev),
-                       torch.from_numpy(s).to(case.dev), case.kc, case.vc, case.ks_arg, case.vs_arg, case.bt,
-                       case.ctx, case.cu, case.mode, out, **opts)
-    torch.cuda.synchronize()
-    for a, b in zip(_snapshot(case), full):
-        assert torch.equal(a, b), f"random step {seed}: cache differs from kv_quant_write's"
-    compare(out, oracle_out(w), what=f"random step {seed} {opts}")
+          list(w.ctx), "sparse", w.sparse is not None, "opts", opts, flush=True)
+    _write_step(w, opts, seed)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", SEEDS[::4])
+def test_random_step_over_a_bf16_cache(seed):
+    w, opts = draw(seed)
+    w = wl.bf16_kv(w)
+    print("random bf16 step", seed, "q_lens", list(w.q_lens), "sparse", w.sparse is not None, "opts", opts,
+          flush=True)
+    _write_step(w, opts, seed)
 
 
 def test_draws_cover_every_kind_and_option():
